@@ -1,0 +1,124 @@
+/*
+ * kq.h -- C ABI of the K-quant weight x Q8_K activation matmul ("kq v2")
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (K-quant kernel arc page, daScript PR "dasLLAMA: K-quant
+ * kernel arc -- kq v2 integer folds, kq v3 panel-scratch tiles, chain
+ * regrain, parity gates"; section "The pieces", kq v2 item, and the k4 v2
+ * and k5/k6 v2 commit messages):
+ *
+ *   y[t][n] = sum over superblocks s of ONE float fold of integer partials
+ *     Q4_K, Q5_K:  d*d8*P - dmin*d8*M
+ *                  P = sum_j sc_j * (sum over sub-block j of q_i * a_i)
+ *                  M = sum_j m_j * (bsum_{2j} + bsum_{2j+1})
+ *     Q6_K:        d*d8*(iacc - 32*bacc)
+ *                  iacc = sum_j sc_j * (sum over 16-wide sub-block j of q_i * a_i)
+ *                  bacc = sum_j sc_j * bsum_j
+ *
+ * where the weight row n is a sequence of 256-weight ggml superblocks
+ * (Q4_K 144 B, Q5_K 176 B, Q6_K 210 B records) and the activation row t is
+ * in Q8_K form: a[k] int8, one float scale d8 per 256 and an int16 sum per
+ * 16 (bsum).  Q5_K shares Q4_K's 6-bit scale/min block and adds a fifth
+ * quant bit; Q6_K carries signed 8-bit scales per 16 weights.  The
+ * activation is always quantised to Q8_K before the dot (the k5/k6 v2
+ * commit message: the matmuls always quantize Q8_K), and K must cover
+ * whole superblocks (the chain-regrain commit message: dim % 256 for any
+ * kq weight).
+ *
+ * Conventions shared by every entry point:
+ *  - Buffers.  Every pointer argument except the host side of a copy is a
+ *    DEVICE pointer on the current HIP device, owned by the caller.  The
+ *    library allocates nothing and keeps no mutable global state; calls are
+ *    reentrant.
+ *  - Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Every call only enqueues work and returns; nothing
+ *    synchronises.  Outputs are fully overwritten.
+ *  - Layouts.  Row-major and dense: x[t][k], xq[t][k], xs[t][k/256],
+ *    xbs[t][k/16], y[t][n], partials[t][n][k/256].
+ *  - Alignment.  w_ggml, w_planes, x, xq and xbs must be 16-byte aligned;
+ *    xs, y and the partials 4-byte aligned.
+ *  - Errors.  All arguments are checked on the host before any HIP call, so
+ *    a bad call returns its code without touching the device.  A failed
+ *    kernel launch returns KQ_ELAUNCH.  No exceptions cross the ABI.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats (the ggml K-quant records). */
+typedef enum { KQ_Q4_K = 4, KQ_Q5_K = 5, KQ_Q6_K = 6 } kq_format;
+
+/* Status codes. */
+enum {
+    KQ_OK = 0,
+    KQ_EINVAL = -1,  /* a size is out of range, or a pointer is NULL */
+    KQ_EFORMAT = -2, /* unknown weight format */
+    KQ_EALIGN = -3,  /* a pointer is not aligned as required */
+    KQ_ELAUNCH = -4  /* the HIP launch failed */
+};
+
+/* Bytes of one ggml superblock record of `fmt` (144, 176, 210), or 0. */
+size_t kq_record_bytes(int fmt);
+
+/* Bytes of the device planes that kq_pack writes for an n x k matrix of
+ * `fmt`, or 0 on bad arguments (n < 1, k < 256, k % 256 != 0, bad fmt).
+ * It is the ggml byte count plus at most 255 bytes of alignment padding
+ * per plane. */
+size_t kq_packed_bytes(int fmt, int64_t n, int64_t k);
+
+/* Re-lay ggml superblock records w_ggml[n][k/256] (record bytes as on
+ * disk) into the device planes w_planes (kq_packed_bytes bytes).  The
+ * planes hold every byte of the records, split by field (K-quant kernel
+ * arc page, "The pieces", kq v3 item: the DRAM planes keep the packed
+ * 144/176/210 B per superblock), so the matmul's loads are 16-byte
+ * aligned and coalesced.  One-time, at load. */
+int kq_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, void *stream);
+
+/* Inverse of kq_pack: planes back to ggml records (for round-trip tests). */
+int kq_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, void *stream);
+
+/* Q8_K quantisation of float activations x[t][k]: per 256 values
+ * amax = max|x|, d8 = amax/127 (IEEE binary32 division), a = rint(x/d8)
+ * (binary32 division, round half to even), clamped to [-127, 127]; an
+ * all-zero chunk gives d8 = 0 and a = 0; xbs holds the sum of each 16
+ * codes (K-quant kernel arc page, "The pieces", kq v2 item; the k4 v2
+ * commit message).  Outputs xq[t][k] int8, xs[t][k/256] float,
+ * xbs[t][k/16] int16.  t >= 1.  x must be finite. */
+int kq_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
+                    void *stream);
+
+/* Decode GEMV, batch t in 1..8: y[t][n] = W . a_t by the folds above,
+ * streaming the packed planes once. */
+int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+            const int16_t *xbs, int64_t t, float *y, void *stream);
+
+/* Prefill GEMM, m >= 1 tokens: y[m][n], same contract as kq_gemv. */
+int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+            const int16_t *xbs, int64_t m, float *y, void *stream);
+
+/* kq_gemv that also stores each superblock's int32 partials:
+ * P[t][n][k/256] and M[t][n][k/256] (Q6_K: P = iacc - 32*bacc and M = 0;
+ * M may be NULL for Q6_K).  The same kernel body as kq_gemv. */
+int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq,
+                     const float *xs, const int16_t *xbs, int64_t t, float *y, int32_t *P,
+                     int32_t *M, void *stream);
+
+/* kq_gemm that also stores the int32 partials, as kq_gemv_partials. */
+int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq,
+                     const float *xs, const int16_t *xbs, int64_t m, float *y, int32_t *P,
+                     int32_t *M, void *stream);
+
+/* Static text for a status code. */
+const char *kq_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

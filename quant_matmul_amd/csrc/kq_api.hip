@@ -1,0 +1,130 @@
+// kq_api.hip -- the C ABI declared in include/kq.h: argument checks on the
+// host (before any HIP call, so a bad call never touches the device), then
+// the launch on the caller's stream.
+#include <limits.h>
+
+#include "kq_common.h"
+
+namespace kq {
+int launch_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
+                        hipStream_t stream);
+int launch_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, hipStream_t stream);
+int launch_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, hipStream_t stream);
+int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st);
+int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st);
+}  // namespace kq
+
+namespace {
+
+bool known(int fmt) { return fmt == KQ_Q4_K || fmt == KQ_Q5_K || fmt == KQ_Q6_K; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// n x k weight matrix: n >= 1, k a positive multiple of 256, both < 2^31
+int check_nk(int64_t n, int64_t k)
+{
+    if (n < 1 || n > INT_MAX || k < kq::QK || k > INT_MAX || k % kq::QK) return KQ_EINVAL;
+    return KQ_OK;
+}
+
+// operands of one matmul call
+int check_matmul(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                 const int16_t *xbs, int64_t t, int64_t tmax, const float *y, const int32_t *P,
+                 const int32_t *M, bool partials)
+{
+    if (!known(fmt)) return KQ_EFORMAT;
+    if (check_nk(n, k)) return KQ_EINVAL;
+    if (t < 1 || t > tmax) return KQ_EINVAL;
+    // the grid and every row-major offset stay inside int64 / uint32
+    if (n * t > ((int64_t)1 << 40)) return KQ_EINVAL;
+    if (!w || !xq || !xs || !xbs || !y) return KQ_EINVAL;
+    if (partials && (!P || (fmt != KQ_Q6_K && !M))) return KQ_EINVAL;
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xbs, 16) || !aligned(xs, 4) || !aligned(y, 4))
+        return KQ_EALIGN;
+    if (partials && (!aligned(P, 4) || (M && !aligned(M, 4)))) return KQ_EALIGN;
+    return KQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kq_record_bytes(int fmt) { return known(fmt) ? (size_t)kq::record_bytes(fmt) : 0; }
+
+size_t kq_packed_bytes(int fmt, int64_t n, int64_t k)
+{
+    if (!known(fmt) || check_nk(n, k)) return 0;
+    return (size_t)kq::planes_of(fmt, n, k / kq::QK).total;
+}
+
+int kq_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, void *stream)
+{
+    if (!known(fmt)) return KQ_EFORMAT;
+    if (check_nk(n, k) || !w_ggml || !w_planes) return KQ_EINVAL;
+    if (!aligned(w_ggml, 16) || !aligned(w_planes, 16)) return KQ_EALIGN;
+    return kq::launch_pack(fmt, w_ggml, n, k, w_planes, (hipStream_t)stream);
+}
+
+int kq_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, void *stream)
+{
+    if (!known(fmt)) return KQ_EFORMAT;
+    if (check_nk(n, k) || !w_ggml || !w_planes) return KQ_EINVAL;
+    if (!aligned(w_ggml, 16) || !aligned(w_planes, 16)) return KQ_EALIGN;
+    return kq::launch_unpack(fmt, w_planes, n, k, w_ggml, (hipStream_t)stream);
+}
+
+int kq_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs, void *stream)
+{
+    if (t < 1 || t > INT_MAX || check_nk(1, k) || !x || !xq || !xs || !xbs) return KQ_EINVAL;
+    if (t * (k / kq::QK) > ((int64_t)1 << 36)) return KQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xbs, 16) || !aligned(xs, 4)) return KQ_EALIGN;
+    return kq::launch_quantize_q8k(x, t, k, xq, xs, xbs, (hipStream_t)stream);
+}
+
+int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+            const int16_t *xbs, int64_t t, float *y, void *stream)
+{
+    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, t, 8, y, nullptr, nullptr, false);
+    if (rc) return rc;
+    return kq::launch_gemv(fmt, w_planes, n, k, xq, xs, xbs, t, y, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                     const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, void *stream)
+{
+    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, t, 8, y, P, M, true);
+    if (rc) return rc;
+    return kq::launch_gemv(fmt, w_planes, n, k, xq, xs, xbs, t, y, P, M, (hipStream_t)stream);
+}
+
+int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+            const int16_t *xbs, int64_t m, float *y, void *stream)
+{
+    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, m, INT_MAX, y, nullptr, nullptr, false);
+    if (rc) return rc;
+    return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                     const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *stream)
+{
+    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, m, INT_MAX, y, P, M, true);
+    if (rc) return rc;
+    return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, (hipStream_t)stream);
+}
+
+const char *kq_strerror(int code)
+{
+    switch (code) {
+    case KQ_OK: return "ok";
+    case KQ_EINVAL: return "invalid argument (size out of range or NULL pointer)";
+    case KQ_EFORMAT: return "unknown weight format";
+    case KQ_EALIGN: return "misaligned pointer";
+    case KQ_ELAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status code";
+    }
+}
+
+}  // extern "C"

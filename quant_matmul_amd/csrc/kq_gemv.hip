@@ -1,0 +1,249 @@
+// kq_gemv.hip -- decode GEMV, batch 1..8 (gfx950).
+//
+// y[t][n] = sum_s fold(P, M) over superblocks s (K-quant kernel arc page,
+// "The pieces", kq v2 item; k4 v2 and k5/k6 v2 commit messages): the
+// sub-scale x int32 dot and min x bsum terms are accumulated in int32 per
+// superblock and closed by ONE float fold per (token, row, superblock).
+//
+// Work mapping.  A quad of lanes owns one superblock of one row; lane c of
+// the quad owns 64 consecutive-in-record weights (two sub-blocks for Q4_K /
+// Q5_K, four 16-wide sub-blocks for Q6_K), loads its 32 bytes of 4-bit
+// quants (plus its high bits) with 16-byte loads, unpacks them in registers
+// and dots them with sdot4 against the Q8_K codes.  The quad's four int32
+// partials are summed with two DPP steps, so every lane of the quad holds
+// the superblock's exact P (and M); the float fold follows.  A wave covers
+// 16 rows at one superblock per step; the waves of a workgroup share the
+// same 16 rows and split the superblocks between them, and their float sums
+// meet in LDS.  Decode streams the weight planes exactly once (the page's
+// "decode reads the whole blob per token", kq v3 commit message).
+#include "kq_common.h"
+
+namespace kq {
+
+namespace {
+
+struct Lane {
+    int p, m;  // this lane's share of P and M for one token
+};
+
+// Q4_K / Q5_K: lane c covers sub-blocks 2c (low nibbles of quant bytes
+// 32c..32c+31) and 2c+1 (their high nibbles).
+template <int FMT, int T>
+__device__ inline void lane_q45(const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c,
+                                const int8_t *__restrict__ a, int64_t K, const int16_t *__restrict__ bs,
+                                int64_t KB, Lane (&out)[T], float &d, float &dmin)
+{
+    const uint4 h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
+    const int64_t qs_off = FMT == KQ_Q4_K ? pl.off[1] : pl.off[2];
+    const uint4 *qs = reinterpret_cast<const uint4 *>(w + qs_off + sb * 128 + 32 * c);
+    const uint4 q0 = qs[0], q1 = qs[1];
+    uint32_t lo[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        hi[i] = (lo[i] >> 4) & 0x0F0F0F0Fu;
+        lo[i] &= 0x0F0F0F0Fu;
+    }
+    if (FMT == KQ_Q5_K) {
+        // fifth bit of weight 32j + l is bit j of high-bit byte l
+        const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 32);
+        const uint4 h0 = qh[0], h1 = qh[1];
+        const uint32_t hb[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            lo[i] |= ((hb[i] >> (2 * c)) & 0x01010101u) << 4;
+            hi[i] |= ((hb[i] >> (2 * c + 1)) & 0x01010101u) << 4;
+        }
+    }
+    d = f16_bits_to_float(h.x & 0xFFFFu);
+    dmin = f16_bits_to_float(h.x >> 16);
+    int sc0, m0, sc1, m1;
+    scale_min_6bit(h.y, h.z, h.w, 2 * c, sc0, m0);
+    scale_min_6bit(h.y, h.z, h.w, 2 * c + 1, sc1, m1);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const uint4 *ap = reinterpret_cast<const uint4 *>(a + t * K + 64 * c);
+        const uint4 A0 = ap[0], A1 = ap[1], A2 = ap[2], A3 = ap[3];
+        int dl = 0, dh = 0;
+        dl = sdot4(lo[0], A0.x, dl); dl = sdot4(lo[1], A0.y, dl);
+        dl = sdot4(lo[2], A0.z, dl); dl = sdot4(lo[3], A0.w, dl);
+        dl = sdot4(lo[4], A1.x, dl); dl = sdot4(lo[5], A1.y, dl);
+        dl = sdot4(lo[6], A1.z, dl); dl = sdot4(lo[7], A1.w, dl);
+        dh = sdot4(hi[0], A2.x, dh); dh = sdot4(hi[1], A2.y, dh);
+        dh = sdot4(hi[2], A2.z, dh); dh = sdot4(hi[3], A2.w, dh);
+        dh = sdot4(hi[4], A3.x, dh); dh = sdot4(hi[5], A3.y, dh);
+        dh = sdot4(hi[6], A3.z, dh); dh = sdot4(hi[7], A3.w, dh);
+        // bsums 4c..4c+3: the first two cover sub-block 2c, the last two 2c+1
+        const uint2 b = *reinterpret_cast<const uint2 *>(bs + t * KB + 4 * c);
+        const int b0 = (int16_t)(b.x & 0xFFFF), b1 = (int16_t)(b.x >> 16);
+        const int b2 = (int16_t)(b.y & 0xFFFF), b3 = (int16_t)(b.y >> 16);
+        out[t].p = sc0 * dl + sc1 * dh;
+        out[t].m = m0 * (b0 + b1) + m1 * (b2 + b3);
+    }
+}
+
+// Q6_K: lane c = 2h + u covers the low-array bytes 64h + 32u .. +31: their
+// low nibbles are weights 128h + 32u + l (16-wide sub-blocks 8h+2u, 8h+2u+1)
+// and their high nibbles weights 128h + 32u + 64 + l (sub-blocks 8h+2u+4,
+// 8h+2u+5); the high two bits come from bits 2u.. (resp. 2u+4..) of high
+// byte 32h + l.  Signed scales; P = iacc - 32*bacc, exact in int32.
+template <int T>
+__device__ inline void lane_q6(const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c,
+                               const int8_t *__restrict__ a, int64_t K, const int16_t *__restrict__ bs,
+                               int64_t KB, Lane (&out)[T], float &d)
+{
+    const int h = c >> 1, u = c & 1;
+    const uint4 *ql = reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 128 + 64 * h + 32 * u);
+    const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 64 + 32 * h);
+    const uint2 s8 = *reinterpret_cast<const uint2 *>(w + pl.off[2] + sb * 16 + 8 * h);
+    const uint16_t dbits = *reinterpret_cast<const uint16_t *>(w + pl.off[3] + sb * 2);
+    const uint4 L0 = ql[0], L1 = ql[1], H0 = qh[0], H1 = qh[1];
+    const uint32_t lw[8] = {L0.x, L0.y, L0.z, L0.w, L1.x, L1.y, L1.z, L1.w};
+    const uint32_t hw[8] = {H0.x, H0.y, H0.z, H0.w, H1.x, H1.y, H1.z, H1.w};
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        lo[i] = (lw[i] & 0x0F0F0F0Fu) | (((hw[i] >> (2 * u)) & 0x03030303u) << 4);
+        hi[i] = ((lw[i] >> 4) & 0x0F0F0F0Fu) | (((hw[i] >> (2 * u + 4)) & 0x03030303u) << 4);
+    }
+    d = f16_bits_to_float(dbits);
+    const int sa = (int8_t)byte_of(s8.x, 2 * u), sb_ = (int8_t)byte_of(s8.x, 2 * u + 1);
+    const int sc_ = (int8_t)byte_of(s8.y, 2 * u), sd = (int8_t)byte_of(s8.y, 2 * u + 1);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int8_t *at = a + t * K + 128 * h + 32 * u;
+        const uint4 A0 = reinterpret_cast<const uint4 *>(at)[0];
+        const uint4 A1 = reinterpret_cast<const uint4 *>(at)[1];
+        const uint4 A2 = reinterpret_cast<const uint4 *>(at + 64)[0];
+        const uint4 A3 = reinterpret_cast<const uint4 *>(at + 64)[1];
+        int d0 = 0, d1 = 0, d2 = 0, d3 = 0;
+        d0 = sdot4(lo[0], A0.x, d0); d0 = sdot4(lo[1], A0.y, d0);
+        d0 = sdot4(lo[2], A0.z, d0); d0 = sdot4(lo[3], A0.w, d0);
+        d1 = sdot4(lo[4], A1.x, d1); d1 = sdot4(lo[5], A1.y, d1);
+        d1 = sdot4(lo[6], A1.z, d1); d1 = sdot4(lo[7], A1.w, d1);
+        d2 = sdot4(hi[0], A2.x, d2); d2 = sdot4(hi[1], A2.y, d2);
+        d2 = sdot4(hi[2], A2.z, d2); d2 = sdot4(hi[3], A2.w, d2);
+        d3 = sdot4(hi[4], A3.x, d3); d3 = sdot4(hi[5], A3.y, d3);
+        d3 = sdot4(hi[6], A3.z, d3); d3 = sdot4(hi[7], A3.w, d3);
+        // bsums 8h..8h+7: 2u, 2u+1 pair with the low half, 2u+4, 2u+5 the high
+        const uint4 b = *reinterpret_cast<const uint4 *>(bs + t * KB + 8 * h);
+        const uint32_t blo = u ? b.y : b.x, bhi = u ? b.w : b.z;
+        const int ba = (int16_t)(blo & 0xFFFF), bb = (int16_t)(blo >> 16);
+        const int bc = (int16_t)(bhi & 0xFFFF), bd = (int16_t)(bhi >> 16);
+        const int iacc = sa * d0 + sb_ * d1 + sc_ * d2 + sd * d3;
+        const int bacc = sa * ba + sb_ * bb + sc_ * bc + sd * bd;
+        out[t].p = iacc - 32 * bacc;
+        out[t].m = 0;
+    }
+}
+
+}  // namespace
+
+template <int FMT, int T, bool PART>
+__global__ __launch_bounds__(512) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
+                                                   const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                                                   const int16_t *__restrict__ xbs, float *__restrict__ y,
+                                                   int32_t *__restrict__ Pout, int32_t *__restrict__ Mout)
+{
+    __shared__ float red[8][T][16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int c = lane & 3, rho = lane >> 2;
+    const int64_t row = (int64_t)blockIdx.x * 16 + rho;
+    const bool valid = row < n;
+    const int64_t K = (int64_t)nsb * QK, KB = K / 16;
+    const Planes pl = planes_of(FMT, n, nsb);
+
+    float acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+
+    for (int s = wave; s < nsb; s += nw) {
+        // rows past n read superblock 0 (in bounds) and are never stored
+        const int64_t sb = valid ? row * nsb + s : 0;
+        Lane part[T];
+        float d, dmin = 0.0f;
+        if (FMT == KQ_Q6_K)
+            lane_q6<T>(w, pl, sb, c, xq + (int64_t)s * QK, K, xbs + (int64_t)s * 16, KB, part, d);
+        else
+            lane_q45<FMT, T>(w, pl, sb, c, xq + (int64_t)s * QK, K, xbs + (int64_t)s * 16, KB, part, d,
+                             dmin);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            // DPP sums run with every lane of the wave active
+            const int P = quad_sum(part[t].p);
+            const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
+            const float d8 = xs[t * nsb + s];
+            if (PART && c == 0 && valid) {
+                const int64_t o = ((int64_t)t * n + row) * nsb + s;
+                Pout[o] = P;
+                if (Mout) Mout[o] = M;
+            }
+            acc[t] = fmaf(d * d8, (float)P, acc[t]);
+            if (FMT != KQ_Q6_K) acc[t] = fmaf(-(dmin * d8), (float)M, acc[t]);
+        }
+    }
+
+    if (c == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) red[wave][t][rho] = acc[t];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 16 * T; i += blockDim.x) {
+        const int t = i >> 4, r = i & 15;
+        const int64_t rr = (int64_t)blockIdx.x * 16 + r;
+        if (rr < n) {
+            float v = 0.0f;
+            for (int wv = 0; wv < nw; ++wv) v += red[wv][t][r];
+            y[t * n + rr] = v;
+        }
+    }
+}
+
+template <int FMT, bool PART>
+static void launch_t(int t, dim3 g, dim3 b, hipStream_t st, const uint8_t *w, int64_t n, int nsb,
+                     const int8_t *xq, const float *xs, const int16_t *xbs, float *y, int32_t *P, int32_t *M)
+{
+#define KQ_GEMV_CASE(TT) \
+    case TT: hipLaunchKernelGGL((gemv_kernel<FMT, TT, PART>), g, b, 0, st, w, n, nsb, xq, xs, xbs, y, P, M); break;
+    switch (t) {
+        KQ_GEMV_CASE(1) KQ_GEMV_CASE(2) KQ_GEMV_CASE(3) KQ_GEMV_CASE(4)
+        KQ_GEMV_CASE(5) KQ_GEMV_CASE(6) KQ_GEMV_CASE(7) KQ_GEMV_CASE(8)
+    }
+#undef KQ_GEMV_CASE
+}
+
+// Waves per workgroup: enough waves in flight to cover HBM latency, at most
+// one wave per superblock of the row group and at most 8.
+static int gemv_waves(int64_t groups, int64_t nsb)
+{
+    int64_t nw = (2048 + groups - 1) / groups;
+    if (nw > nsb) nw = nsb;
+    if (nw > 8) nw = 8;
+    if (nw < 1) nw = 1;
+    return (int)nw;
+}
+
+int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st)
+{
+    const int64_t nsb = k / QK;
+    const int64_t groups = (n + 15) / 16;
+    const dim3 g((unsigned)groups), b(64 * gemv_waves(groups, nsb));
+    const uint8_t *wb = (const uint8_t *)w;
+    const bool part = P != nullptr;
+    if (fmt == KQ_Q4_K) {
+        if (part) launch_t<KQ_Q4_K, true>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
+        else launch_t<KQ_Q4_K, false>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
+    } else if (fmt == KQ_Q5_K) {
+        if (part) launch_t<KQ_Q5_K, true>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
+        else launch_t<KQ_Q5_K, false>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
+    } else {
+        if (part) launch_t<KQ_Q6_K, true>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
+        else launch_t<KQ_Q6_K, false>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
+    }
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
+}
+
+}  // namespace kq

@@ -1,0 +1,73 @@
+"""Allocation helpers around the kq C ABI for torch callers.
+
+These only allocate device tensors of the right shapes and call the
+same-named entry points of the binding; all arithmetic runs in libkq.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (kq_gemm, kq_gemm_partials, kq_gemv, kq_gemv_partials, kq_pack, kq_packed_bytes,
+               kq_quantize_q8k, kq_record_bytes, kq_unpack)
+
+QK = 256
+
+
+def upload_records(recs: np.ndarray, device="cuda") -> torch.Tensor:
+    """ggml records (n, k/256, bytes) uint8 -> a flat device tensor."""
+    return torch.from_numpy(np.ascontiguousarray(recs).reshape(-1)).to(device)
+
+
+def pack(fmt, recs_dev: torch.Tensor, n: int, k: int, stream=None) -> torch.Tensor:
+    planes = torch.empty(kq_packed_bytes(fmt, n, k), dtype=torch.uint8, device=recs_dev.device)
+    kq_pack(fmt, recs_dev, n, k, planes, stream)
+    return planes
+
+
+def unpack(fmt, planes: torch.Tensor, n: int, k: int, stream=None) -> torch.Tensor:
+    out = torch.empty(n * (k // QK) * kq_record_bytes(fmt), dtype=torch.uint8, device=planes.device)
+    kq_unpack(fmt, planes, n, k, out, stream)
+    return out
+
+
+def q8k_buffers(t: int, k: int, device="cuda"):
+    return (torch.empty((t, k), dtype=torch.int8, device=device),
+            torch.empty((t, k // QK), dtype=torch.float32, device=device),
+            torch.empty((t, k // 16), dtype=torch.int16, device=device))
+
+
+def quantize_q8k(x: torch.Tensor, stream=None):
+    t, k = x.shape
+    xq, xs, xbs = q8k_buffers(t, k, x.device)
+    kq_quantize_q8k(x, t, k, xq, xs, xbs, stream)
+    return xq, xs, xbs
+
+
+def gemv(fmt, planes, n: int, k: int, q8, stream=None) -> torch.Tensor:
+    xq, xs, xbs = q8
+    t = xq.shape[0]
+    y = torch.empty((t, n), dtype=torch.float32, device=xq.device)
+    kq_gemv(fmt, planes, n, k, xq, xs, xbs, t, y, stream)
+    return y
+
+
+def gemm(fmt, planes, n: int, k: int, q8, stream=None) -> torch.Tensor:
+    xq, xs, xbs = q8
+    m = xq.shape[0]
+    y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    kq_gemm(fmt, planes, n, k, xq, xs, xbs, m, y, stream)
+    return y
+
+
+def matmul_partials(kind: str, fmt, planes, n: int, k: int, q8, stream=None):
+    """(y, P, M) from kq_gemv_partials (kind 'gemv') or kq_gemm_partials."""
+    xq, xs, xbs = q8
+    t = xq.shape[0]
+    dev = xq.device
+    y = torch.empty((t, n), dtype=torch.float32, device=dev)
+    P = torch.empty((t, n, k // QK), dtype=torch.int32, device=dev)
+    M = torch.empty((t, n, k // QK), dtype=torch.int32, device=dev)
+    f = kq_gemv_partials if kind == "gemv" else kq_gemm_partials
+    f(fmt, planes, n, k, xq, xs, xbs, t, y, P, M, stream)
+    return y, P, M

@@ -29,3 +29,12 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # name the case on stderr before a GPU test runs, so a run that ends
+    # abruptly still says which case it was in
+    if "gpu" in request.keywords:
+        print(f"\n[gpu case] {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield

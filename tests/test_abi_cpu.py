@@ -1,0 +1,106 @@
+"""CPU tier: libkq.so loads, exports every entry point include/kq.h
+declares, and rejects bad arguments with the documented status code before
+any HIP call (so these run on a host without a GPU; no call here reaches a
+kernel launch)."""
+import os
+import re
+
+import pytest
+
+import quant_matmul_amd as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+GOOD16 = 0x10000   # fake but 16-byte aligned "device pointers": never dereferenced,
+GOOD16B = 0x20000  # every call below fails validation first
+ODD = 0x10001
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_symbols()
+    assert set(names) == set(kq.SYMBOLS)
+    for name in names:
+        assert hasattr(kq.lib, name), name
+
+
+def test_record_and_packed_bytes():
+    assert [kq.kq_record_bytes(f) for f in (4, 5, 6)] == [144, 176, 210]
+    assert kq.kq_record_bytes(7) == 0
+    for fmt, rb in ((4, 144), (5, 176), (6, 210)):
+        for n, k in ((1, 256), (17, 2560), (9728, 2560), (2560, 9728)):
+            b = kq.kq_packed_bytes(fmt, n, k)
+            base = n * (k // 256) * rb
+            assert base <= b <= base + 4 * 255
+            assert b % 256 == 0
+    assert kq.kq_packed_bytes(4, 0, 256) == 0
+    assert kq.kq_packed_bytes(4, 4, 300) == 0
+    assert kq.kq_packed_bytes(4, 4, 0) == 0
+    assert kq.kq_packed_bytes(9, 4, 256) == 0
+
+
+def _gemv(fmt=4, w=GOOD16, n=16, k=256, xq=GOOD16, xs=GOOD16, xbs=GOOD16, t=1, y=GOOD16):
+    return kq.lib.kq_gemv(fmt, w, n, k, xq, xs, xbs, t, y, None)
+
+
+def test_gemv_argument_checks():
+    assert _gemv(fmt=3) == kq.KQ_EFORMAT
+    assert _gemv(fmt=7) == kq.KQ_EFORMAT
+    assert _gemv(k=300) == kq.KQ_EINVAL
+    assert _gemv(k=0) == kq.KQ_EINVAL
+    assert _gemv(n=0) == kq.KQ_EINVAL
+    assert _gemv(n=-5) == kq.KQ_EINVAL
+    assert _gemv(t=0) == kq.KQ_EINVAL
+    assert _gemv(t=9) == kq.KQ_EINVAL
+    for name in ("w", "xq", "xs", "xbs", "y"):
+        assert _gemv(**{name: None}) == kq.KQ_EINVAL, name
+    for name in ("w", "xq", "xbs"):
+        assert _gemv(**{name: GOOD16 + 4}) == kq.KQ_EALIGN, name
+    for name in ("xs", "y"):
+        assert _gemv(**{name: ODD}) == kq.KQ_EALIGN, name
+
+
+def test_gemm_argument_checks():
+    f = kq.lib.kq_gemm
+    assert f(8, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EFORMAT
+    assert f(4, GOOD16, 16, 512 + 16, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EINVAL
+    assert f(4, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 0, GOOD16, None) == kq.KQ_EINVAL
+    assert f(4, GOOD16, 16, 256, None, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EINVAL
+    assert f(4, GOOD16 + 8, 16, 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EALIGN
+
+
+def test_partials_argument_checks():
+    for f in (kq.lib.kq_gemv_partials, kq.lib.kq_gemm_partials):
+        # P missing
+        assert f(4, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 1, GOOD16, None, GOOD16, None) == kq.KQ_EINVAL
+        # M missing is an error for Q4_K / Q5_K ...
+        assert f(5, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 1, GOOD16, GOOD16, None, None) == kq.KQ_EINVAL
+        # ... and misaligned partials are rejected
+        assert f(6, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 1, GOOD16, ODD, None, None) == kq.KQ_EALIGN
+
+
+def test_quantize_and_pack_argument_checks():
+    q = kq.lib.kq_quantize_q8k
+    assert q(GOOD16, 0, 256, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert q(GOOD16, 1, 100, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert q(None, 1, 256, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert q(GOOD16 + 4, 1, 256, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EALIGN
+    for f in (kq.lib.kq_pack, kq.lib.kq_unpack):
+        assert f(1, GOOD16, 4, 256, GOOD16B, None) == kq.KQ_EFORMAT
+        assert f(4, GOOD16, 4, 255, GOOD16B, None) == kq.KQ_EINVAL
+        assert f(4, None, 4, 256, GOOD16B, None) == kq.KQ_EINVAL
+        assert f(6, GOOD16 + 2, 4, 256, GOOD16B, None) == kq.KQ_EALIGN
+
+
+def test_strerror_and_python_error():
+    assert kq.kq_strerror(0) == "ok"
+    assert "format" in kq.kq_strerror(kq.KQ_EFORMAT)
+    assert "unknown" in kq.kq_strerror(12345)
+    with pytest.raises(kq.KqError) as e:
+        kq.kq_gemv(9, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 1, GOOD16, stream=0)
+    assert e.value.code == kq.KQ_EFORMAT

@@ -1,0 +1,204 @@
+"""GPU tier: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (K-quant kernel arc page, "Testing" and the per-format-tune commit
+message's tolerance rule): the Q8_K activation image and the per-superblock
+int32 partials are bit-exact; float outputs agree within 1e-5 * R per
+output, R = sum_i |w_i * xhat_i| -- a row-magnitude tolerance, because the
+signed Q6_K sub-scales cancel inside a row and an element-relative bound
+would trip on fold-order noise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from quant_matmul_amd import torch_ops as ops
+import quant_matmul_amd as kq
+
+pytestmark = pytest.mark.gpu
+FMTS = ["q4_k", "q5_k", "q6_k"]
+TOL = 1e-5
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+class Case:
+    """Seeded weights and activations, the oracle's view and the device's."""
+
+    def __init__(self, fmt, n, k, t, seed=1, x=None):
+        self.fmt, self.n, self.k, self.t = fmt, n, k, t
+        self.recs = synth.weights(fmt, n, k, seed)
+        self.x = synth.activations(t, k, seed + 1000) if x is None else x
+        self.q8_host = oracle.quantize_q8k(self.x)
+        self.planes = ops.pack(fmt, ops.upload_records(self.recs), n, k)
+        self.q8 = tuple(dev(a) for a in self.q8_host)
+
+    def oracle_rows(self, rows=None):
+        recs = self.recs if rows is None else self.recs[rows]
+        xq, xs, xbs = self.q8_host
+        P, M = oracle.partials(self.fmt, recs, xq, xbs)
+        y = oracle.matmul(self.fmt, recs, xq, xs, xbs)
+        R = oracle.rowmag(self.fmt, recs, xq, xs)
+        return y, P, M, R
+
+
+def check(case, y, P, M, rows=None):
+    y_o, P_o, M_o, R = case.oracle_rows(rows)
+    y, P, M = host(y), host(P), host(M)
+    if rows is not None:
+        y, P, M = y[:, rows], P[:, rows], M[:, rows]
+    assert np.array_equal(P, P_o), f"P mismatch at {np.argwhere(P != P_o)[:5]}"
+    if case.fmt != "q6_k":
+        assert np.array_equal(M, M_o), f"M mismatch at {np.argwhere(M != M_o)[:5]}"
+    err = np.abs(y.astype(np.float64) - y_o)
+    assert np.all(np.isfinite(y))
+    bad = err > TOL * R
+    assert not bad.any(), f"{bad.sum()} outputs beyond tolerance, worst ratio {np.max(err / R):.3g}"
+
+
+# ------------------------------------------------------------ Q8_K ------
+@pytest.mark.parametrize("t,k", [(1, 256), (3, 2560), (8, 9728), (512, 2560), (129, 768)])
+def test_quantize_bit_exact(t, k):
+    x = synth.activations(t, k, 40 + t)
+    # edge chunks: all zero, a single value, exact .5 ties, tiny magnitudes
+    x[0, :256] = 0.0
+    if k >= 768:
+        x[0, 256:512] = 0.0
+        x[0, 300] = -0.3
+        x[0, 512:768] = np.round(x[0, 512:768] * 20) / 2
+        x[0, 512] = 127.0
+    if t > 1:
+        x[1, :256] *= np.float32(1e-30)
+    xq, xs, xbs = ops.quantize_q8k(dev(x))
+    rq, rs, rbs = oracle.quantize_q8k(x)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(xbs), rbs)
+
+
+# ------------------------------------------------------------ pack ------
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(1, 256), (17, 2560), (300, 768)])
+def test_pack_round_trip_and_planes(fmt, n, k):
+    recs = synth.weights(fmt, n, k, 7)
+    planes = ops.pack(fmt, ops.upload_records(recs), n, k)
+    back = host(ops.unpack(fmt, planes, n, k))
+    assert np.array_equal(back, recs.reshape(-1))
+    # the planes are the record fields regrouped, each plane 256-B aligned
+    fields = {"q4_k": [(0, 16), (16, 144)], "q5_k": [(0, 16), (16, 48), (48, 176)],
+              "q6_k": [(0, 128), (128, 192), (192, 208), (208, 210)]}[fmt]
+    p = host(planes)
+    off = 0
+    flat = recs.reshape(n * (k // 256), -1)
+    for a, b in fields:
+        size = flat.shape[0] * (b - a)
+        assert np.array_equal(p[off:off + size], flat[:, a:b].reshape(-1))
+        off += (size + 255) // 256 * 256
+    assert off == len(p)
+
+
+# ------------------------------------------------------------ GEMV ------
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("n,k", [(256, 2560), (37, 256), (1, 512), (17, 9728)])
+def test_gemv_parity(fmt, t, n, k):
+    c = Case(fmt, n, k, t, seed=10 * t + n)
+    y, P, M = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
+    check(c, y, P, M)
+    # the production entry point runs the same body without the stores
+    y2 = ops.gemv(fmt, c.planes, n, k, c.q8)
+    assert torch.equal(y, y2)
+
+
+# ------------------------------------------------------------ GEMM ------
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,n,k", [(128, 256, 2560), (129, 100, 768), (1, 64, 256), (300, 65, 512),
+                                   (256, 300, 1024)])
+def test_gemm_parity(fmt, m, n, k):
+    c = Case(fmt, n, k, m, seed=m + n)
+    y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8)
+    check(c, y, P, M)
+    y2 = ops.gemm(fmt, c.planes, n, k, c.q8)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_and_gemm_partials_agree(fmt):
+    # the page's tile-vs-gemv bit-exactness gate (kq v3 commit message)
+    n, k, t = 200, 2560, 8
+    c = Case(fmt, n, k, t, seed=5)
+    _, P1, M1 = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
+    _, P2, M2 = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8)
+    assert torch.equal(P1, P2)
+    if fmt != "q6_k":
+        assert torch.equal(M1, M2)
+
+
+# --------------------------------------------- full-size, sampled rows --
+def sample_rows(n):
+    return sorted(set([0, 1, n // 2, n - 2, n - 1] + list(range(7, n, 613))))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
+@pytest.mark.parametrize("t", [1, 4])
+def test_gemv_full_size_sampled(fmt, n, k, t):
+    c = Case(fmt, n, k, t, seed=3)
+    y, P, M = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
+    check(c, y, P, M, rows=sample_rows(n))
+    y2 = ops.gemv(fmt, c.planes, n, k, c.q8)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
+def test_gemm_pp512_full_size_sampled(fmt, n, k):
+    m = 512
+    x = synth.activations(m, k, 77)
+    xd = dev(x)
+    q8 = ops.quantize_q8k(xd)  # quantised on device, as in the prefill path
+    c = Case(fmt, n, k, m, seed=4, x=x)
+    for a, b in zip(q8, c.q8):
+        assert torch.equal(a, b)
+    y = ops.gemm(fmt, c.planes, n, k, q8)
+    rows = sample_rows(n)[:24]
+    y_o, _, _, R = c.oracle_rows(rows)
+    err = np.abs(host(y)[:, rows].astype(np.float64) - y_o)
+    assert np.all(err <= TOL * R)
+
+
+# ------------------------------------------ poison, guards, determinism --
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_outputs_fully_written_and_guards_intact(kind, fmt):
+    n, k, t = 70, 768, (3 if kind == "gemv" else 70)
+    c = Case(fmt, n, k, t, seed=9)
+    g = 4096
+    buf = torch.full((g + t * n + g,), float("nan"), dtype=torch.float32, device="cuda")
+    canary = torch.tensor([1234.5], device="cuda")
+    buf[:g] = canary
+    buf[-g:] = canary
+    y = buf[g:g + t * n]
+    xq, xs, xbs = c.q8
+    f = kq.kq_gemv if kind == "gemv" else kq.kq_gemm
+    f(fmt, c.planes, n, k, xq, xs, xbs, t, y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:g] == 1234.5) and torch.all(buf[-g:] == 1234.5)
+    assert not torch.isnan(y).any()
+
+
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+def test_repeat_runs_are_bitwise_identical(kind):
+    n, k = 2560, 9728
+    t = 4 if kind == "gemv" else 256
+    c = Case("q6_k", n, k, t, seed=12)
+    f = ops.gemv if kind == "gemv" else ops.gemm
+    ys = [f("q6_k", c.planes, n, k, c.q8) for _ in range(3)]
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
