@@ -22,44 +22,88 @@ namespace kq {
 
 namespace {
 
-struct Lane {
-    int p, m;  // this lane's share of P and M for one token
+// Raw bytes one lane needs from one superblock, loaded before any compute
+// so a wave has every superblock of its share in flight at once.
+template <int FMT>
+struct Raw;
+template <>
+struct Raw<KQ_Q4_K> {
+    uint4 h, q0, q1;
+};
+template <>
+struct Raw<KQ_Q5_K> {
+    uint4 h, q0, q1, qh0, qh1;
+};
+template <>
+struct Raw<KQ_Q6_K> {
+    uint4 l0, l1, h0, h1;
+    uint2 s8;
+    uint32_t d;
 };
 
 // Q4_K / Q5_K: lane c covers sub-blocks 2c (low nibbles of quant bytes
 // 32c..32c+31) and 2c+1 (their high nibbles).
-template <int FMT, int T>
-__device__ inline void lane_q45(const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c,
-                                const int8_t *__restrict__ a, int64_t K, const int16_t *__restrict__ bs,
-                                int64_t KB, Lane (&out)[T], float &d, float &dmin)
+__device__ inline void load_raw(Raw<KQ_Q4_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
 {
-    const uint4 h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
-    const int64_t qs_off = FMT == KQ_Q4_K ? pl.off[1] : pl.off[2];
-    const uint4 *qs = reinterpret_cast<const uint4 *>(w + qs_off + sb * 128 + 32 * c);
-    const uint4 q0 = qs[0], q1 = qs[1];
-    uint32_t lo[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
+    const uint4 *qs = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 128 + 32 * c);
+    r.q0 = qs[0];
+    r.q1 = qs[1];
+}
+__device__ inline void load_raw(Raw<KQ_Q5_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
+{
+    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
+    const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 32);
+    r.qh0 = qh[0];
+    r.qh1 = qh[1];
+    const uint4 *qs = reinterpret_cast<const uint4 *>(w + pl.off[2] + sb * 128 + 32 * c);
+    r.q0 = qs[0];
+    r.q1 = qs[1];
+}
+// Q6_K: lane c = 2h + u covers the low-array bytes 64h + 32u .. +31.
+__device__ inline void load_raw(Raw<KQ_Q6_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
+{
+    const int h = c >> 1, u = c & 1;
+    const uint4 *ql = reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 128 + 64 * h + 32 * u);
+    const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 64 + 32 * h);
+    r.l0 = ql[0];
+    r.l1 = ql[1];
+    r.h0 = qh[0];
+    r.h1 = qh[1];
+    r.s8 = *reinterpret_cast<const uint2 *>(w + pl.off[2] + sb * 16 + 8 * h);
+    r.d = *reinterpret_cast<const uint16_t *>(w + pl.off[3] + sb * 2);
+}
+
+struct Lane {
+    int p, m;  // this lane's share of P and M for one token
+};
+
+template <int FMT, int T>
+__device__ inline void compute_q45(const Raw<FMT> &r, int c, const int8_t *__restrict__ a, int64_t K,
+                                   const int16_t *__restrict__ bs, int64_t KB, Lane (&out)[T], float &d,
+                                   float &dmin)
+{
+    uint32_t lo[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
     uint32_t hi[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         hi[i] = (lo[i] >> 4) & 0x0F0F0F0Fu;
         lo[i] &= 0x0F0F0F0Fu;
     }
-    if (FMT == KQ_Q5_K) {
+    if constexpr (FMT == KQ_Q5_K) {
         // fifth bit of weight 32j + l is bit j of high-bit byte l
-        const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 32);
-        const uint4 h0 = qh[0], h1 = qh[1];
-        const uint32_t hb[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const uint32_t hb[8] = {r.qh0.x, r.qh0.y, r.qh0.z, r.qh0.w, r.qh1.x, r.qh1.y, r.qh1.z, r.qh1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             lo[i] |= ((hb[i] >> (2 * c)) & 0x01010101u) << 4;
             hi[i] |= ((hb[i] >> (2 * c + 1)) & 0x01010101u) << 4;
         }
     }
-    d = f16_bits_to_float(h.x & 0xFFFFu);
-    dmin = f16_bits_to_float(h.x >> 16);
+    d = f16_bits_to_float(r.h.x & 0xFFFFu);
+    dmin = f16_bits_to_float(r.h.x >> 16);
     int sc0, m0, sc1, m1;
-    scale_min_6bit(h.y, h.z, h.w, 2 * c, sc0, m0);
-    scale_min_6bit(h.y, h.z, h.w, 2 * c + 1, sc1, m1);
+    scale_min_6bit(r.h.y, r.h.z, r.h.w, 2 * c, sc0, m0);
+    scale_min_6bit(r.h.y, r.h.z, r.h.w, 2 * c + 1, sc1, m1);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const uint4 *ap = reinterpret_cast<const uint4 *>(a + t * K + 64 * c);
@@ -82,33 +126,27 @@ __device__ inline void lane_q45(const uint8_t *__restrict__ w, const Planes &pl,
     }
 }
 
-// Q6_K: lane c = 2h + u covers the low-array bytes 64h + 32u .. +31: their
-// low nibbles are weights 128h + 32u + l (16-wide sub-blocks 8h+2u, 8h+2u+1)
-// and their high nibbles weights 128h + 32u + 64 + l (sub-blocks 8h+2u+4,
-// 8h+2u+5); the high two bits come from bits 2u.. (resp. 2u+4..) of high
-// byte 32h + l.  Signed scales; P = iacc - 32*bacc, exact in int32.
+// Q6_K lane c = 2h + u: the low nibbles of its 32 low-array bytes are
+// weights 128h + 32u + l (16-wide sub-blocks 8h+2u, 8h+2u+1), the high
+// nibbles weights 128h + 32u + 64 + l (sub-blocks 8h+2u+4, 8h+2u+5); the
+// high two bits come from bits 2u.. (resp. 2u+4..) of high byte 32h + l.
+// Signed scales; P = iacc - 32*bacc, exact in int32.
 template <int T>
-__device__ inline void lane_q6(const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c,
-                               const int8_t *__restrict__ a, int64_t K, const int16_t *__restrict__ bs,
-                               int64_t KB, Lane (&out)[T], float &d)
+__device__ inline void compute_q6(const Raw<KQ_Q6_K> &r, int c, const int8_t *__restrict__ a, int64_t K,
+                                  const int16_t *__restrict__ bs, int64_t KB, Lane (&out)[T], float &d)
 {
     const int h = c >> 1, u = c & 1;
-    const uint4 *ql = reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 128 + 64 * h + 32 * u);
-    const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 64 + 32 * h);
-    const uint2 s8 = *reinterpret_cast<const uint2 *>(w + pl.off[2] + sb * 16 + 8 * h);
-    const uint16_t dbits = *reinterpret_cast<const uint16_t *>(w + pl.off[3] + sb * 2);
-    const uint4 L0 = ql[0], L1 = ql[1], H0 = qh[0], H1 = qh[1];
-    const uint32_t lw[8] = {L0.x, L0.y, L0.z, L0.w, L1.x, L1.y, L1.z, L1.w};
-    const uint32_t hw[8] = {H0.x, H0.y, H0.z, H0.w, H1.x, H1.y, H1.z, H1.w};
+    const uint32_t lw[8] = {r.l0.x, r.l0.y, r.l0.z, r.l0.w, r.l1.x, r.l1.y, r.l1.z, r.l1.w};
+    const uint32_t hw[8] = {r.h0.x, r.h0.y, r.h0.z, r.h0.w, r.h1.x, r.h1.y, r.h1.z, r.h1.w};
     uint32_t lo[8], hi[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         lo[i] = (lw[i] & 0x0F0F0F0Fu) | (((hw[i] >> (2 * u)) & 0x03030303u) << 4);
         hi[i] = ((lw[i] >> 4) & 0x0F0F0F0Fu) | (((hw[i] >> (2 * u + 4)) & 0x03030303u) << 4);
     }
-    d = f16_bits_to_float(dbits);
-    const int sa = (int8_t)byte_of(s8.x, 2 * u), sb_ = (int8_t)byte_of(s8.x, 2 * u + 1);
-    const int sc_ = (int8_t)byte_of(s8.y, 2 * u), sd = (int8_t)byte_of(s8.y, 2 * u + 1);
+    d = f16_bits_to_float(r.d);
+    const int sa = (int8_t)byte_of(r.s8.x, 2 * u), sb_ = (int8_t)byte_of(r.s8.x, 2 * u + 1);
+    const int sc_ = (int8_t)byte_of(r.s8.y, 2 * u), sd = (int8_t)byte_of(r.s8.y, 2 * u + 1);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int8_t *at = a + t * K + 128 * h + 32 * u;
@@ -139,13 +177,17 @@ __device__ inline void lane_q6(const uint8_t *__restrict__ w, const Planes &pl, 
 
 }  // namespace
 
-template <int FMT, int T, bool PART>
-__global__ __launch_bounds__(512) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
-                                                   const int8_t *__restrict__ xq, const float *__restrict__ xs,
-                                                   const int16_t *__restrict__ xbs, float *__restrict__ y,
-                                                   int32_t *__restrict__ Pout, int32_t *__restrict__ Mout)
+// One workgroup = 16 rows x all superblocks; its waves take contiguous runs
+// of `per_wave` superblocks, U at a time with every load of the U issued
+// before the first is consumed.
+template <int FMT, int T, int U, bool PART>
+__global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
+                                                    const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                                                    const int16_t *__restrict__ xbs, float *__restrict__ y,
+                                                    int32_t *__restrict__ Pout, int32_t *__restrict__ Mout,
+                                                    int per_wave)
 {
-    __shared__ float red[8][T][16];
+    __shared__ float red[16][T][16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
@@ -154,34 +196,45 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t *__restrict__ w
     const bool valid = row < n;
     const int64_t K = (int64_t)nsb * QK, KB = K / 16;
     const Planes pl = planes_of(FMT, n, nsb);
+    // rows past n read row 0 (in bounds) and are never stored
+    const int64_t rbase = (valid ? row : 0) * nsb;
 
     float acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = 0.0f;
 
-    for (int s = wave; s < nsb; s += nw) {
-        // rows past n read superblock 0 (in bounds) and are never stored
-        const int64_t sb = valid ? row * nsb + s : 0;
-        Lane part[T];
-        float d, dmin = 0.0f;
-        if (FMT == KQ_Q6_K)
-            lane_q6<T>(w, pl, sb, c, xq + (int64_t)s * QK, K, xbs + (int64_t)s * 16, KB, part, d);
-        else
-            lane_q45<FMT, T>(w, pl, sb, c, xq + (int64_t)s * QK, K, xbs + (int64_t)s * 16, KB, part, d,
-                             dmin);
+    const int s_begin = wave * per_wave;
+    const int s_end = min(nsb, s_begin + per_wave);
+    for (int s0 = s_begin; s0 < s_end; s0 += U) {
+        Raw<FMT> raw[U];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            // DPP sums run with every lane of the wave active
-            const int P = quad_sum(part[t].p);
-            const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
-            const float d8 = xs[t * nsb + s];
-            if (PART && c == 0 && valid) {
-                const int64_t o = ((int64_t)t * n + row) * nsb + s;
-                Pout[o] = P;
-                if (Mout) Mout[o] = M;
+        for (int u = 0; u < U; ++u)
+            if (s0 + u < s_end) load_raw(raw[u], w, pl, rbase + s0 + u, c);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u;
+            if (s >= s_end) break;
+            Lane part[T];
+            float d, dmin = 0.0f;
+            if constexpr (FMT == KQ_Q6_K)
+                compute_q6<T>(raw[u], c, xq + (int64_t)s * QK, K, xbs + (int64_t)s * 16, KB, part, d);
+            else
+                compute_q45<FMT, T>(raw[u], c, xq + (int64_t)s * QK, K, xbs + (int64_t)s * 16, KB, part, d,
+                                    dmin);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                // DPP sums run with every lane of the wave active
+                const int P = quad_sum(part[t].p);
+                const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
+                const float d8 = xs[t * nsb + s];
+                if (PART && c == 0 && valid) {
+                    const int64_t o = ((int64_t)t * n + row) * nsb + s;
+                    Pout[o] = P;
+                    if (Mout) Mout[o] = M;
+                }
+                acc[t] = fmaf(d * d8, (float)P, acc[t]);
+                if (FMT != KQ_Q6_K) acc[t] = fmaf(-(dmin * d8), (float)M, acc[t]);
             }
-            acc[t] = fmaf(d * d8, (float)P, acc[t]);
-            if (FMT != KQ_Q6_K) acc[t] = fmaf(-(dmin * d8), (float)M, acc[t]);
         }
     }
 
@@ -201,28 +254,50 @@ __global__ __launch_bounds__(512) void gemv_kernel(const uint8_t *__restrict__ w
     }
 }
 
-template <int FMT, bool PART>
-static void launch_t(int t, dim3 g, dim3 b, hipStream_t st, const uint8_t *w, int64_t n, int nsb,
-                     const int8_t *xq, const float *xs, const int16_t *xbs, float *y, int32_t *P, int32_t *M)
+struct GemvArgs {
+    const uint8_t *w;
+    int64_t n;
+    int nsb;
+    const int8_t *xq;
+    const float *xs;
+    const int16_t *xbs;
+    float *y;
+    int32_t *P, *M;
+    int per_wave;
+};
+
+template <int FMT, int T, int U, bool PART>
+static void launch_one(dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
-#define KQ_GEMV_CASE(TT) \
-    case TT: hipLaunchKernelGGL((gemv_kernel<FMT, TT, PART>), g, b, 0, st, w, n, nsb, xq, xs, xbs, y, P, M); break;
-    switch (t) {
-        KQ_GEMV_CASE(1) KQ_GEMV_CASE(2) KQ_GEMV_CASE(3) KQ_GEMV_CASE(4)
-        KQ_GEMV_CASE(5) KQ_GEMV_CASE(6) KQ_GEMV_CASE(7) KQ_GEMV_CASE(8)
-    }
-#undef KQ_GEMV_CASE
+    hipLaunchKernelGGL((gemv_kernel<FMT, T, U, PART>), g, b, 0, st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs, a.y,
+                       a.P, a.M, a.per_wave);
 }
 
-// Waves per workgroup: enough waves in flight to cover HBM latency, at most
-// one wave per superblock of the row group and at most 8.
-static int gemv_waves(int64_t groups, int64_t nsb)
+template <int FMT, int T>
+static void launch_u(int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
-    int64_t nw = (2048 + groups - 1) / groups;
-    if (nw > nsb) nw = nsb;
-    if (nw > 8) nw = 8;
-    if (nw < 1) nw = 1;
-    return (int)nw;
+    if (part) return launch_one<FMT, T, 4, true>(g, b, st, a);
+    switch (u) {
+    case 1: return launch_one<FMT, T, 1, false>(g, b, st, a);
+    case 2: return launch_one<FMT, T, 2, false>(g, b, st, a);
+    case 3: return launch_one<FMT, T, 3, false>(g, b, st, a);
+    default: return launch_one<FMT, T, 4, false>(g, b, st, a);
+    }
+}
+
+template <int FMT>
+static void launch_t(int t, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+{
+    switch (t) {
+    case 1: return launch_u<FMT, 1>(u, part, g, b, st, a);
+    case 2: return launch_u<FMT, 2>(u, part, g, b, st, a);
+    case 3: return launch_u<FMT, 3>(u, part, g, b, st, a);
+    case 4: return launch_u<FMT, 4>(u, part, g, b, st, a);
+    case 5: return launch_u<FMT, 5>(u, part, g, b, st, a);
+    case 6: return launch_u<FMT, 6>(u, part, g, b, st, a);
+    case 7: return launch_u<FMT, 7>(u, part, g, b, st, a);
+    default: return launch_u<FMT, 8>(u, part, g, b, st, a);
+    }
 }
 
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -230,19 +305,20 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
 {
     const int64_t nsb = k / QK;
     const int64_t groups = (n + 15) / 16;
-    const dim3 g((unsigned)groups), b(64 * gemv_waves(groups, nsb));
-    const uint8_t *wb = (const uint8_t *)w;
+    // about 16 waves per CU in flight, at most 16 waves per workgroup, and
+    // every wave of a workgroup with the same share of superblocks
+    int64_t nw = (4096 + groups - 1) / groups;
+    nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
+    nw = nw > nsb ? nsb : nw;
+    const int64_t per_wave = (nsb + nw - 1) / nw;
+    nw = (nsb + per_wave - 1) / per_wave;
+    const int u = per_wave >= 4 ? 4 : (int)per_wave;
+    GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave};
+    const dim3 g((unsigned)groups), b((unsigned)(64 * nw));
     const bool part = P != nullptr;
-    if (fmt == KQ_Q4_K) {
-        if (part) launch_t<KQ_Q4_K, true>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
-        else launch_t<KQ_Q4_K, false>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
-    } else if (fmt == KQ_Q5_K) {
-        if (part) launch_t<KQ_Q5_K, true>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
-        else launch_t<KQ_Q5_K, false>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
-    } else {
-        if (part) launch_t<KQ_Q6_K, true>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
-        else launch_t<KQ_Q6_K, false>((int)t, g, b, st, wb, n, (int)nsb, xq, xs, xbs, y, P, M);
-    }
+    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, u, part, g, b, st, a);
+    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, u, part, g, b, st, a);
+    else launch_t<KQ_Q6_K>((int)t, u, part, g, b, st, a);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 

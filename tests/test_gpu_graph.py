@@ -1,0 +1,51 @@
+"""The kq entry points under HIP graph capture: a captured quantise + GEMV +
+GEMM sequence, replayed several times with eager work and synchronisation in
+between, matches the eager results bitwise on every replay (the entry points
+record no memset and allocate nothing)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import quant_matmul_amd as kq
+from quant_matmul_amd import torch_ops as ops
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k"])
+def test_graph_replays_match_eager(fmt):
+    n, k, t, m = 300, 2560, 2, 130
+    planes = ops.pack(fmt, ops.upload_records(synth.weights(fmt, n, k, 21)), n, k)
+    x1 = torch.from_numpy(synth.activations(t, k, 22)).cuda()
+    xm = torch.from_numpy(synth.activations(m, k, 23)).cuda()
+    q1, qm = ops.q8k_buffers(t, k), ops.q8k_buffers(m, k)
+    y1 = torch.empty((t, n), device="cuda")
+    ym = torch.empty((m, n), device="cuda")
+
+    def seq():
+        kq.kq_quantize_q8k(x1, t, k, *q1)
+        kq.kq_gemv(fmt, planes, n, k, *q1, t, y1)
+        kq.kq_quantize_q8k(xm, m, k, *qm)
+        kq.kq_gemm(fmt, planes, n, k, *qm, m, ym)
+
+    seq()
+    torch.cuda.synchronize()
+    ref = [a.clone() for a in (*q1, *qm, y1, ym)]
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        seq()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        seq()
+    for rep in range(4):
+        for a in (*q1, *qm, y1, ym):
+            a.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((*q1, *qm, y1, ym), ref):
+            assert torch.equal(a, b), f"replay {rep} differs from eager"
