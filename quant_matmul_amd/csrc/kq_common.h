@@ -98,7 +98,60 @@ __device__ inline int quad_sum(int v)
     return v;
 }
 
-template <typename T>
-__device__ inline T ldg(const T *p) { return __builtin_nontemporal_load(p); }
+// Raw bytes of one 64-weight share of a superblock, as loaded from the
+// planes by one lane (GEMV) or one unpack task (GEMM), before any compute.
+// Share c of a Q4_K/Q5_K superblock is sub-blocks 2c and 2c+1 (the low and
+// high nibbles of quant bytes 32c..32c+31); share c = 2h + u of a Q6_K
+// superblock is the low-array bytes 64h + 32u .. +31 (weights 128h + 32u +
+// 0..31 and + 64 + 0..31), their high-bit bytes and their four scales.
+template <int FMT>
+struct Raw;
+template <>
+struct Raw<KQ_Q4_K> {
+    uint4 h, q0, q1;
+};
+template <>
+struct Raw<KQ_Q5_K> {
+    uint4 h, q0, q1, qh0, qh1;
+};
+template <>
+struct Raw<KQ_Q6_K> {
+    uint4 l0, l1, h0, h1;
+    uint2 s8;
+    uint32_t d;
+};
+
+// Q4_K / Q5_K: lane c covers sub-blocks 2c (low nibbles of quant bytes
+// 32c..32c+31) and 2c+1 (their high nibbles).
+__device__ inline void load_raw(Raw<KQ_Q4_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
+{
+    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
+    const uint4 *qs = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 128 + 32 * c);
+    r.q0 = qs[0];
+    r.q1 = qs[1];
+}
+__device__ inline void load_raw(Raw<KQ_Q5_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
+{
+    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
+    const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 32);
+    r.qh0 = qh[0];
+    r.qh1 = qh[1];
+    const uint4 *qs = reinterpret_cast<const uint4 *>(w + pl.off[2] + sb * 128 + 32 * c);
+    r.q0 = qs[0];
+    r.q1 = qs[1];
+}
+// Q6_K: lane c = 2h + u covers the low-array bytes 64h + 32u .. +31.
+__device__ inline void load_raw(Raw<KQ_Q6_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
+{
+    const int h = c >> 1, u = c & 1;
+    const uint4 *ql = reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 128 + 64 * h + 32 * u);
+    const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 64 + 32 * h);
+    r.l0 = ql[0];
+    r.l1 = ql[1];
+    r.h0 = qh[0];
+    r.h1 = qh[1];
+    r.s8 = *reinterpret_cast<const uint2 *>(w + pl.off[2] + sb * 16 + 8 * h);
+    r.d = *reinterpret_cast<const uint16_t *>(w + pl.off[3] + sb * 2);
+}
 
 }  // namespace kq

@@ -22,7 +22,13 @@
 //    m <= 63 are exact in f16, and |M| < 2^24 keeps the f32 sum exact).
 //  * Epilogue per superblock: acc += d8 * (d*P - dmin*M).
 //
-// Wave tile 64 tokens x 32*TN rows (2 x TN MFMA tiles); WM x WN waves.
+// Pipeline.  A workgroup is 4 waves over a 256-token x 32*TN-row tile; each
+// wave owns 64 tokens x 32*TN rows (2 x TN MFMA tiles).  Per superblock s
+// the Q8_K codes of the wave's tokens sit in registers (prefetched one
+// superblock ahead), the digit panel in one of two LDS buffers; while the
+// high-digit MFMAs of s run, the wave unpacks its share of superblock s+1
+// (whose packed bytes were prefetched) into the other buffer, so the VALU
+// unpack overlaps the matrix pipe.  One barrier per superblock.
 #include "kq_common.h"
 
 namespace kq {
@@ -49,8 +55,9 @@ __device__ inline void split_digits(uint32_t e, uint32_t o, uint32_t &hi, uint32
 // (0..63): the digits of sc*q.
 __device__ inline void digits_q45(uint32_t q, int sc, uint32_t &hi, uint32_t &lo)
 {
-    const uint32_t e = (q & 0x00FF00FFu) * (uint32_t)sc;
-    const uint32_t o = ((q >> 8) & 0x00FF00FFu) * (uint32_t)sc;
+    // each 16-bit lane <= 31*63, and both factors fit 24 bits
+    const uint32_t e = (uint32_t)__umul24(q & 0x00FF00FFu, (uint32_t)sc);
+    const uint32_t o = (uint32_t)__umul24((q >> 8) & 0x00FF00FFu, (uint32_t)sc);
     split_digits(e, o, hi, lo);
 }
 
@@ -63,115 +70,122 @@ __device__ inline void digits_q45(uint32_t q, int sc, uint32_t &hi, uint32_t &lo
 __device__ inline void digits_q6(uint32_t q, int sc, uint32_t &hi, uint32_t &lo)
 {
     const int bias = (4096 - 32 * sc) * 0x00010001;
-    const uint32_t e = (uint32_t)((int)(q & 0x00FF00FFu) * sc + bias);
-    const uint32_t o = (uint32_t)((int)((q >> 8) & 0x00FF00FFu) * sc + bias);
+    const uint32_t e = (uint32_t)(__mul24((int)(q & 0x00FF00FFu), sc) + bias);
+    const uint32_t o = (uint32_t)(__mul24((int)((q >> 8) & 0x00FF00FFu), sc) + bias);
     uint32_t hu;
     split_digits(e, o, hu, lo);
     hi = ((hu | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
 }
 
+// Half share: 32 weights of a superblock row, one unpack task.  Task
+// h = 2c + half of a Q4_K/Q5_K row covers quant bytes 32c + 16*half .. +15:
+// their low nibbles are weights 64c + 16*half + 0..15 (sub-block 2c), their
+// high nibbles weights 64c + 32 + 16*half + 0..15 (sub-block 2c+1).  Task
+// h = 2c + half of a Q6_K row (c = 2hh + u) covers low-array bytes
+// 64hh + 32u + 16*half .. +15: weights 128hh + 32u + 16*half + 0..15
+// (sub-block 8hh + 2u + half) and the same + 64 (sub-block 8hh + 2u + 4 + half).
 template <int FMT>
-__device__ inline void store_digits(int8_t *wh, int8_t *wl, int r, int k0, const uint32_t (&h)[8],
-                                    const uint32_t (&l)[8])
+struct Half;
+template <>
+struct Half<KQ_Q4_K> {
+    uint4 h, q;
+};
+template <>
+struct Half<KQ_Q5_K> {
+    uint4 h, q, qh;
+};
+template <>
+struct Half<KQ_Q6_K> {
+    uint4 l, hq;
+    uint2 s8;
+    uint32_t d;
+};
+
+__device__ inline void load_half(Half<KQ_Q4_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int h)
 {
-    uint4 *ph = reinterpret_cast<uint4 *>(wh + r * LDS_STRIDE + k0);
-    uint4 *pl = reinterpret_cast<uint4 *>(wl + r * LDS_STRIDE + k0);
-    ph[0] = make_uint4(h[0], h[1], h[2], h[3]);
-    ph[1] = make_uint4(h[4], h[5], h[6], h[7]);
-    pl[0] = make_uint4(l[0], l[1], l[2], l[3]);
-    pl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
+    r.q = *reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 128 + 16 * h);
+}
+__device__ inline void load_half(Half<KQ_Q5_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int h)
+{
+    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
+    r.qh = *reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 32 + 16 * (h & 1));
+    r.q = *reinterpret_cast<const uint4 *>(w + pl.off[2] + sb * 128 + 16 * h);
+}
+__device__ inline void load_half(Half<KQ_Q6_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int h)
+{
+    const int c = h >> 1, half = h & 1, hh = c >> 1;
+    r.l = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 128 + 16 * h);
+    r.hq = *reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 64 + 32 * hh + 16 * half);
+    r.s8 = *reinterpret_cast<const uint2 *>(w + pl.off[2] + sb * 16 + 8 * hh);
+    r.d = *reinterpret_cast<const uint16_t *>(w + pl.off[3] + sb * 2);
 }
 
-// Unpack 64 weights of row r (task c of 4) of superblock sb into the digit
-// panel.  Q4_K/Q5_K task c covers sub-blocks 2c and 2c+1 (k = 64c..64c+63);
-// Q6_K task c = 2h + u covers k = 128h + 32u + 0..31 and + 64 + 0..31.
-template <int FMT>
-__device__ inline void unpack_task(const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, bool valid,
-                                   int r, int c, int8_t *wh, int8_t *wl, _Float16 *mexp, float *dn, float *dmn)
+__device__ inline void store_half(int8_t *wh, int8_t *wl, int r, int k0, const uint32_t (&h)[4], const uint32_t (&l)[4])
 {
-    uint32_t h0[8], l0[8], h1[8], l1[8];
-    if (FMT == KQ_Q6_K) {
-        const int hh = c >> 1, u = c & 1;
-        uint32_t lo[8], hi[8];
-        uint2 s8 = make_uint2(0, 0);
-        uint16_t dbits = 0;
-        if (valid) {
-            const uint4 *ql = reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 128 + 64 * hh + 32 * u);
-            const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 64 + 32 * hh);
-            const uint4 L0 = ql[0], L1 = ql[1], H0 = qh[0], H1 = qh[1];
-            const uint32_t lw[8] = {L0.x, L0.y, L0.z, L0.w, L1.x, L1.y, L1.z, L1.w};
-            const uint32_t hw[8] = {H0.x, H0.y, H0.z, H0.w, H1.x, H1.y, H1.z, H1.w};
+    *reinterpret_cast<uint4 *>(wh + r * LDS_STRIDE + k0) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4 *>(wl + r * LDS_STRIDE + k0) = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ inline void unpack_half(const Half<KQ_Q6_K> &rw, bool valid, int r, int h, int8_t *wh, int8_t *wl,
+                                   _Float16 *, float *dn, float *dmn)
+{
+    const int c = h >> 1, half = h & 1, hh = c >> 1, u = c & 1;
+    const uint32_t lw[4] = {rw.l.x, rw.l.y, rw.l.z, rw.l.w};
+    const uint32_t hw[4] = {rw.hq.x, rw.hq.y, rw.hq.z, rw.hq.w};
+    const uint2 s8 = valid ? rw.s8 : make_uint2(0, 0);
+    const int slo = (int8_t)byte_of(s8.x, 2 * u + half), shi = (int8_t)byte_of(s8.y, 2 * u + half);
+    uint32_t h0[4], l0[4], h1[4], l1[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                lo[i] = (lw[i] & 0x0F0F0F0Fu) | (((hw[i] >> (2 * u)) & 0x03030303u) << 4);
-                hi[i] = ((lw[i] >> 4) & 0x0F0F0F0Fu) | (((hw[i] >> (2 * u + 4)) & 0x03030303u) << 4);
-            }
-            s8 = *reinterpret_cast<const uint2 *>(w + pl.off[2] + sb * 16 + 8 * hh);
-            dbits = *reinterpret_cast<const uint16_t *>(w + pl.off[3] + sb * 2);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0x20202020u;  // q = 32: w' = 0
-        }
-        const int sa = (int8_t)byte_of(s8.x, 2 * u), sb_ = (int8_t)byte_of(s8.x, 2 * u + 1);
-        const int sc_ = (int8_t)byte_of(s8.y, 2 * u), sd = (int8_t)byte_of(s8.y, 2 * u + 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            digits_q6(lo[i], sa, h0[i], l0[i]);
-            digits_q6(lo[i + 4], sb_, h0[i + 4], l0[i + 4]);
-            digits_q6(hi[i], sc_, h1[i], l1[i]);
-            digits_q6(hi[i + 4], sd, h1[i + 4], l1[i + 4]);
-        }
-        const int k0 = 128 * hh + 32 * u;
-        store_digits<FMT>(wh, wl, r, k0, h0, l0);
-        store_digits<FMT>(wh, wl, r, k0 + 64, h1, l1);
-        if (c == 0) {
-            dn[r] = valid ? f16_bits_to_float(dbits) : 0.0f;
-            dmn[r] = 0.0f;
-        }
-        return;
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (lw[i] & 0x0F0F0F0Fu) | (((hw[i] >> (2 * u)) & 0x03030303u) << 4);
+        const uint32_t hi = ((lw[i] >> 4) & 0x0F0F0F0Fu) | (((hw[i] >> (2 * u + 4)) & 0x03030303u) << 4);
+        digits_q6(lo, slo, h0[i], l0[i]);
+        digits_q6(hi, shi, h1[i], l1[i]);
     }
-    uint4 h = make_uint4(0, 0, 0, 0), q0 = h, q1 = h, hb0 = h, hb1 = h;
-    if (valid) {
-        h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
-        const int64_t qs_off = FMT == KQ_Q4_K ? pl.off[1] : pl.off[2];
-        const uint4 *qs = reinterpret_cast<const uint4 *>(w + qs_off + sb * 128 + 32 * c);
-        q0 = qs[0];
-        q1 = qs[1];
-        if (FMT == KQ_Q5_K) {
-            const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 32);
-            hb0 = qh[0];
-            hb1 = qh[1];
-        }
+    const int k0 = 128 * hh + 32 * u + 16 * half;
+    store_half(wh, wl, r, k0, h0, l0);
+    store_half(wh, wl, r, k0 + 64, h1, l1);
+    if (h == 0) {
+        dn[r] = valid ? f16_bits_to_float(rw.d) : 0.0f;
+        dmn[r] = 0.0f;
     }
-    uint32_t lo[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    const uint32_t hb[8] = {hb0.x, hb0.y, hb0.z, hb0.w, hb1.x, hb1.y, hb1.z, hb1.w};
-    uint32_t hi[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        hi[i] = (lo[i] >> 4) & 0x0F0F0F0Fu;
-        lo[i] &= 0x0F0F0F0Fu;
-        if (FMT == KQ_Q5_K) {
-            lo[i] |= ((hb[i] >> (2 * c)) & 0x01010101u) << 4;
-            hi[i] |= ((hb[i] >> (2 * c + 1)) & 0x01010101u) << 4;
-        }
-    }
+}
+
+template <int FMT>
+__device__ inline void unpack_half(const Half<FMT> &rw, bool valid, int r, int h, int8_t *wh, int8_t *wl,
+                                   _Float16 *mexp, float *dn, float *dmn)
+{
+    const int c = h >> 1, half = h & 1;
+    const uint4 hd = valid ? rw.h : make_uint4(0, 0, 0, 0);
+    const uint32_t qw[4] = {rw.q.x, rw.q.y, rw.q.z, rw.q.w};
     int sc0, m0, sc1, m1;
-    scale_min_6bit(h.y, h.z, h.w, 2 * c, sc0, m0);
-    scale_min_6bit(h.y, h.z, h.w, 2 * c + 1, sc1, m1);
+    scale_min_6bit(hd.y, hd.z, hd.w, 2 * c, sc0, m0);
+    scale_min_6bit(hd.y, hd.z, hd.w, 2 * c + 1, sc1, m1);
+    uint32_t h0[4], l0[4], h1[4], l1[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        digits_q45(lo[i], sc0, h0[i], l0[i]);
-        digits_q45(hi[i], sc1, h1[i], l1[i]);
+    for (int i = 0; i < 4; ++i) {
+        uint32_t lo = qw[i] & 0x0F0F0F0Fu, hi = (qw[i] >> 4) & 0x0F0F0F0Fu;
+        if constexpr (FMT == KQ_Q5_K) {
+            const uint32_t hb = i == 0 ? rw.qh.x : i == 1 ? rw.qh.y : i == 2 ? rw.qh.z : rw.qh.w;
+            lo |= ((hb >> (2 * c)) & 0x01010101u) << 4;
+            hi |= ((hb >> (2 * c + 1)) & 0x01010101u) << 4;
+        }
+        digits_q45(lo, sc0, h0[i], l0[i]);
+        digits_q45(hi, sc1, h1[i], l1[i]);
     }
-    store_digits<FMT>(wh, wl, r, 64 * c, h0, l0);
-    store_digits<FMT>(wh, wl, r, 64 * c + 32, h1, l1);
-    // min of sub-block j pairs with bsums 2j and 2j+1
-    _Float16 *me = mexp + r * 16 + 4 * c;
-    me[0] = me[1] = (_Float16)m0;
-    me[2] = me[3] = (_Float16)m1;
-    if (c == 0) {
-        dn[r] = f16_bits_to_float(h.x & 0xFFFFu);
-        dmn[r] = f16_bits_to_float(h.x >> 16);
+    const int k0 = 64 * c + 16 * half;
+    store_half(wh, wl, r, k0, h0, l0);
+    store_half(wh, wl, r, k0 + 32, h1, l1);
+    if (half == 0) {
+        // min of sub-block j pairs with bsums 2j and 2j+1
+        _Float16 *me = mexp + r * 16 + 4 * c;
+        me[0] = me[1] = (_Float16)m0;
+        me[2] = me[3] = (_Float16)m1;
+    }
+    if (h == 0) {
+        dn[r] = f16_bits_to_float(hd.x & 0xFFFFu);
+        dmn[r] = f16_bits_to_float(hd.x >> 16);
     }
 }
 
@@ -189,29 +203,90 @@ __device__ inline void tile_of(int b, int G, int mtiles, int &nt, int &mt)
 
 }  // namespace
 
-template <int FMT, int WM, int TN, bool PART>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
+template <int FMT, int TN, bool PART>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                    const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                    const int16_t *__restrict__ xbs, int64_t mtok,
                                                    float *__restrict__ y, int32_t *__restrict__ Pout,
                                                    int32_t *__restrict__ Mout, int mtiles)
 {
-    constexpr int WN = 4 / WM;
-    constexpr int BM = 64 * WM, BN = 32 * TN * WN;
-    __shared__ __align__(16) int8_t wh[BN * LDS_STRIDE];
-    __shared__ __align__(16) int8_t wl[BN * LDS_STRIDE];
-    __shared__ __align__(16) _Float16 mexp[BN * 16];
-    __shared__ float dn[BN], dmn[BN];
-    __shared__ __align__(16) float d8s[BM];
+    constexpr int BM = 256, BN = 32 * TN;
+    constexpr int TASKS = BN * 8;  // 32-weight unpack tasks per panel
+    constexpr int TPT = (TASKS + 255) / 256;
+    __shared__ __align__(16) int8_t wh[2][BN * LDS_STRIDE];
+    __shared__ __align__(16) int8_t wl[2][BN * LDS_STRIDE];
+    __shared__ __align__(16) _Float16 mexp[2][BN * 16];
+    __shared__ float dn[2][BN], dmn[2][BN];
+    __shared__ __align__(16) float d8s[2][BM];
 
     int nt, mt;
     tile_of(blockIdx.x, gridDim.x, mtiles, nt, mt);
     const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave % WM, wn = wave / WM;
+    const int lane = threadIdx.x & 63, wm = threadIdx.x >> 6;
     const int l32 = lane & 31, lh = lane >> 5;
     const int64_t K = (int64_t)nsb * QK, KB = K / 16;
     const Planes pl = planes_of(FMT, n, nsb);
+
+    // Unpack tasks of this thread: rows past n read row n-1 (in bounds)
+    // and unpack as zero weights.
+    Half<FMT> raw[TPT];
+    int64_t wrow[TPT];
+    bool wvalid[TPT];
+#pragma unroll
+    for (int q = 0; q < TPT; ++q) {
+        const int64_t row = n0 + ((threadIdx.x + 256 * q) >> 3);
+        wvalid[q] = row < n;
+        wrow[q] = (wvalid[q] ? row : n - 1) * nsb;
+    }
+    const int64_t t_d8 = m0 + threadIdx.x;  // this thread's d8 slot
+    const float *xs_row = xs + (t_d8 < mtok ? t_d8 : mtok - 1) * nsb;
+    float d8n = 0.0f;
+    auto load_w = [&](int s) {
+#pragma unroll
+        for (int q = 0; q < TPT; ++q)
+            if (threadIdx.x + 256 * q < TASKS) load_half(raw[q], w, pl, wrow[q] + s, (threadIdx.x + 256 * q) & 7);
+        d8n = t_d8 < mtok ? xs_row[s] : 0.0f;
+    };
+    auto unpack_w = [&](int b) {
+#pragma unroll
+        for (int q = 0; q < TPT; ++q) {
+            const int task = threadIdx.x + 256 * q;
+            if (task < TASKS) unpack_half(raw[q], wvalid[q], task >> 3, task & 7, wh[b], wl[b], mexp[b], dn[b], dmn[b]);
+        }
+        d8s[b][threadIdx.x] = d8n;
+    };
+
+    // Q8_K codes (MFMA A operand: the lane's token, k bytes 16*lh + 32*ks)
+    // and bsums (f16 A operand of the min term) of the wave's 64 tokens;
+    // tokens past m read token m-1 and are never stored
+    const int8_t *arow[2];
+    const int16_t *brow[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        int64_t t = m0 + wm * 64 + mi * 32 + l32;
+        t = t < mtok ? t : mtok - 1;
+        arow[mi] = xq + t * K + 16 * lh;
+        brow[mi] = xbs + t * KB + 8 * lh;
+    }
+    i32x4 A[2][8];
+    f16x8 Ab[2];
+    auto load_a = [&](int s) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                A[mi][ks] = *reinterpret_cast<const i32x4 *>(arow[mi] + (int64_t)s * QK + 32 * ks);
+            if constexpr (FMT != KQ_Q6_K) {
+                const uint4 bq = *reinterpret_cast<const uint4 *>(brow[mi] + (int64_t)s * 16);
+                const uint32_t bw[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    Ab[mi][2 * e] = (_Float16)(int16_t)(bw[e] & 0xFFFF);
+                    Ab[mi][2 * e + 1] = (_Float16)(int16_t)(bw[e] >> 16);
+                }
+            }
+        }
+    };
 
     f32x16 accf[2][TN];
 #pragma unroll
@@ -219,130 +294,100 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) accf[mi][ni] = f32x16{};
 
-    for (int s = 0; s < nsb; ++s) {
-        __syncthreads();  // the previous superblock's panel is consumed
-        for (int task = threadIdx.x; task < BN * 4; task += 256) {
-            const int r = task >> 2, c = task & 3;
-            const int64_t row = n0 + r;
-            const bool valid = row < n;
-            unpack_task<FMT>(w, pl, valid ? row * nsb + s : 0, valid, r, c, wh, wl, mexp, dn, dmn);
-        }
-        for (int i = threadIdx.x; i < BM; i += 256) {
-            const int64_t t = m0 + i;
-            d8s[i] = t < mtok ? xs[t * nsb + s] : 0.0f;
-        }
-        // A operands (Q8_K codes) and the bsums of this superblock
-        i32x4 A[2][8];
-        f16x8 Ab[2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-            const int64_t t = m0 + wm * 64 + mi * 32 + l32;
-            const bool tv = t < mtok;
-            const int8_t *ap = xq + (tv ? t : 0) * K + (int64_t)s * QK + 16 * lh;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) A[mi][ks] = tv ? *reinterpret_cast<const i32x4 *>(ap + 32 * ks) : i32x4{};
-            const uint4 b = tv ? *reinterpret_cast<const uint4 *>(xbs + t * KB + (int64_t)s * 16 + 8 * lh)
-                               : make_uint4(0, 0, 0, 0);
-            const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Ab[mi][2 * e] = (_Float16)(int16_t)(bw[e] & 0xFFFF);
-                Ab[mi][2 * e + 1] = (_Float16)(int16_t)(bw[e] >> 16);
-            }
-        }
-        __syncthreads();  // the panel is complete
+    load_w(0);
+    load_a(0);
+    unpack_w(0);
+    if (nsb > 1) load_w(1);
+    __syncthreads();
 
-        i32x16 acci[2][TN];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < TN; ++ni) acci[mi][ni] = i32x16{};
-        // high-digit pass
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-            for (int ni = 0; ni < TN; ++ni) {
-                const int rl = wn * 32 * TN + ni * 32 + l32;
-                const i32x4 B = *reinterpret_cast<const i32x4 *>(wh + rl * LDS_STRIDE + 32 * ks + 16 * lh);
-#pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
-                    acci[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acci[mi][ni], 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < TN; ++ni) acci[mi][ni] = acci[mi][ni] * 128;
-        // low-digit pass
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-            for (int ni = 0; ni < TN; ++ni) {
-                const int rl = wn * 32 * TN + ni * 32 + l32;
-                const i32x4 B = *reinterpret_cast<const i32x4 *>(wl + rl * LDS_STRIDE + 32 * ks + 16 * lh);
-#pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
-                    acci[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acci[mi][ni], 0, 0, 0);
-            }
-        }
-        // min term and the per-superblock float fold
+    for (int s = 0; s < nsb; ++s) {
+        const int b = s & 1;
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) {
-            const int rl = wn * 32 * TN + ni * 32 + l32;
-            const float dv = dn[rl], dm = dmn[rl];
-            f16x8 Bm{};
-            if (FMT != KQ_Q6_K) Bm = *reinterpret_cast<const f16x8 *>(mexp + rl * 16 + 8 * lh);
+            const int rl = ni * 32 + l32;
+            i32x16 acci[2] = {i32x16{}, i32x16{}};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const i32x4 B = *reinterpret_cast<const i32x4 *>(wh[b] + rl * LDS_STRIDE + 32 * ks + 16 * lh);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+                    acci[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acci[mi], 0, 0, 0);
+            }
+            // the unpack of the next superblock overlaps these MFMAs
+            if (ni == 0 && s + 1 < nsb) unpack_w(b ^ 1);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) acci[mi] = acci[mi] * 128;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + rl * LDS_STRIDE + 32 * ks + 16 * lh);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+                    acci[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acci[mi], 0, 0, 0);
+            }
+            // min term
+            f32x16 mf[2] = {f32x16{}, f32x16{}};
+            if constexpr (FMT != KQ_Q6_K) {
+                const f16x8 Bm = *reinterpret_cast<const f16x8 *>(mexp[b] + rl * 16 + 8 * lh);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+                    mf[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab[mi], Bm, mf[mi], 0, 0, 0);
+            }
+            if (ni == TN - 1 && s + 1 < nsb) {
+                // every MFMA reading A(s) is issued: refill A with s+1 while
+                // the epilogue below runs
+                load_a(s + 1);
+            }
+            // the one float fold of this superblock for tile column ni
+            const float dv = dn[b][rl], dm = dmn[b][rl];
             const int64_t col = n0 + rl;
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi) {
-                f32x16 mf{};
-                if (FMT != KQ_Q6_K) mf = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab[mi], Bm, mf, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int tl = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                    const float Pf = (float)acci[mi][ni][i];
-                    const float u = FMT == KQ_Q6_K ? dv * Pf : fmaf(dv, Pf, -(dm * mf[i]));
-                    accf[mi][ni][i] = fmaf(d8s[tl], u, accf[mi][ni][i]);
+                    const float Pf = (float)acci[mi][i];
+                    const float u = FMT == KQ_Q6_K ? dv * Pf : fmaf(dv, Pf, -(dm * mf[mi][i]));
+                    accf[mi][ni][i] = fmaf(d8s[b][tl], u, accf[mi][ni][i]);
                     if (PART) {
                         const int64_t t = m0 + tl;
                         if (t < mtok && col < n) {
                             const int64_t o = (t * n + col) * nsb + s;
-                            Pout[o] = acci[mi][ni][i];
-                            if (Mout) Mout[o] = FMT == KQ_Q6_K ? 0 : (int)mf[i];
+                            Pout[o] = acci[mi][i];
+                            if (Mout) Mout[o] = FMT == KQ_Q6_K ? 0 : (int)mf[mi][i];
                         }
                     }
                 }
             }
         }
+        if (s + 2 < nsb) load_w(s + 2);
+        __syncthreads();  // panel s+1 complete; panel s free for s+2
     }
 
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) {
-            const int64_t col = n0 + wn * 32 * TN + ni * 32 + l32;
-            if (col >= n) continue;
+        for (int i = 0; i < 16; ++i) {
+            const int64_t t = m0 + wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+            if (t >= mtok) continue;
+            float *yr = y + t * n + n0 + l32;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t t = m0 + wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                if (t < mtok) y[t * n + col] = accf[mi][ni][i];
-            }
+            for (int ni = 0; ni < TN; ++ni)
+                if (n0 + ni * 32 + l32 < n) yr[ni * 32] = accf[mi][ni][i];
         }
 }
 
-template <int FMT, int WM, int TN>
+template <int FMT, int TN>
 static void launch_cfg(bool part, int64_t n, int nsb, const uint8_t *w, const int8_t *xq, const float *xs,
                        const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
 {
-    constexpr int WN = 4 / WM;
-    constexpr int BM = 64 * WM, BN = 32 * TN * WN;
+    constexpr int BM = 256, BN = 32 * TN;
     const int64_t ntiles = (n + BN - 1) / BN, mtiles = (m + BM - 1) / BM;
     const dim3 g((unsigned)(ntiles * mtiles)), b(256);
     if (part)
-        hipLaunchKernelGGL((gemm_kernel<FMT, WM, TN, true>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M,
+        hipLaunchKernelGGL((gemm_kernel<FMT, TN, true>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M,
                            (int)mtiles);
     else
-        hipLaunchKernelGGL((gemm_kernel<FMT, WM, TN, false>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M,
+        hipLaunchKernelGGL((gemm_kernel<FMT, TN, false>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M,
                            (int)mtiles);
 }
 
@@ -350,12 +395,8 @@ template <int FMT>
 static void launch_fmt(bool part, int64_t n, int nsb, const uint8_t *w, const int8_t *xq, const float *xs,
                        const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
 {
-    // 256 x 64 tiles when that fills the chip, else 256 x 32
-    const int64_t tiles_64 = ((n + 63) / 64) * ((m + 255) / 256);
-    if (tiles_64 >= 256)
-        launch_cfg<FMT, 4, 2>(part, n, nsb, w, xq, xs, xbs, m, y, P, M, st);
-    else
-        launch_cfg<FMT, 4, 1>(part, n, nsb, w, xq, xs, xbs, m, y, P, M, st);
+    // 256 x 32 tiles: the register budget of two resident workgroups per CU
+    launch_cfg<FMT, 1>(part, n, nsb, w, xq, xs, xbs, m, y, P, M, st);
 }
 
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,

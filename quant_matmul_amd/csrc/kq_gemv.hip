@@ -22,65 +22,44 @@ namespace kq {
 
 namespace {
 
-// Raw bytes one lane needs from one superblock, loaded before any compute
-// so a wave has every superblock of its share in flight at once.
-template <int FMT>
-struct Raw;
-template <>
-struct Raw<KQ_Q4_K> {
-    uint4 h, q0, q1;
-};
-template <>
-struct Raw<KQ_Q5_K> {
-    uint4 h, q0, q1, qh0, qh1;
-};
-template <>
-struct Raw<KQ_Q6_K> {
-    uint4 l0, l1, h0, h1;
-    uint2 s8;
-    uint32_t d;
-};
-
-// Q4_K / Q5_K: lane c covers sub-blocks 2c (low nibbles of quant bytes
-// 32c..32c+31) and 2c+1 (their high nibbles).
-__device__ inline void load_raw(Raw<KQ_Q4_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
-{
-    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
-    const uint4 *qs = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 128 + 32 * c);
-    r.q0 = qs[0];
-    r.q1 = qs[1];
-}
-__device__ inline void load_raw(Raw<KQ_Q5_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
-{
-    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
-    const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 32);
-    r.qh0 = qh[0];
-    r.qh1 = qh[1];
-    const uint4 *qs = reinterpret_cast<const uint4 *>(w + pl.off[2] + sb * 128 + 32 * c);
-    r.q0 = qs[0];
-    r.q1 = qs[1];
-}
-// Q6_K: lane c = 2h + u covers the low-array bytes 64h + 32u .. +31.
-__device__ inline void load_raw(Raw<KQ_Q6_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int c)
-{
-    const int h = c >> 1, u = c & 1;
-    const uint4 *ql = reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 128 + 64 * h + 32 * u);
-    const uint4 *qh = reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 64 + 32 * h);
-    r.l0 = ql[0];
-    r.l1 = ql[1];
-    r.h0 = qh[0];
-    r.h1 = qh[1];
-    r.s8 = *reinterpret_cast<const uint2 *>(w + pl.off[2] + sb * 16 + 8 * h);
-    r.d = *reinterpret_cast<const uint16_t *>(w + pl.off[3] + sb * 2);
-}
-
 struct Lane {
     int p, m;  // this lane's share of P and M for one token
 };
 
+// The Q8_K codes and bsums one lane dots against its 64 weights, for one
+// token of one superblock (a: the token's codes of the superblock, bs: its
+// 16 bsums).
+struct Act {
+    uint4 a0, a1, a2, a3;
+    uint4 b;
+};
+
+template <int FMT>
+__device__ inline void load_act(Act &r, const int8_t *__restrict__ a, const int16_t *__restrict__ bs, int c)
+{
+    if constexpr (FMT == KQ_Q6_K) {
+        // codes 128h + 32u + 0..31 and + 64; bsums 8h..8h+7
+        const int h = c >> 1, u = c & 1;
+        const uint4 *at = reinterpret_cast<const uint4 *>(a + 128 * h + 32 * u);
+        r.a0 = at[0];
+        r.a1 = at[1];
+        r.a2 = at[4];
+        r.a3 = at[5];
+        r.b = *reinterpret_cast<const uint4 *>(bs + 8 * h);
+    } else {
+        // codes 64c..64c+63; bsums 4c..4c+3
+        const uint4 *ap = reinterpret_cast<const uint4 *>(a + 64 * c);
+        r.a0 = ap[0];
+        r.a1 = ap[1];
+        r.a2 = ap[2];
+        r.a3 = ap[3];
+        const uint2 b = *reinterpret_cast<const uint2 *>(bs + 4 * c);
+        r.b = make_uint4(b.x, b.y, 0, 0);
+    }
+}
+
 template <int FMT, int T>
-__device__ inline void compute_q45(const Raw<FMT> &r, int c, const int8_t *__restrict__ a, int64_t K,
-                                   const int16_t *__restrict__ bs, int64_t KB, Lane (&out)[T], float &d,
+__device__ inline void compute_q45(const Raw<FMT> &r, int c, const Act (&act)[T], Lane (&out)[T], float &d,
                                    float &dmin)
 {
     uint32_t lo[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
@@ -106,8 +85,7 @@ __device__ inline void compute_q45(const Raw<FMT> &r, int c, const int8_t *__res
     scale_min_6bit(r.h.y, r.h.z, r.h.w, 2 * c + 1, sc1, m1);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const uint4 *ap = reinterpret_cast<const uint4 *>(a + t * K + 64 * c);
-        const uint4 A0 = ap[0], A1 = ap[1], A2 = ap[2], A3 = ap[3];
+        const uint4 A0 = act[t].a0, A1 = act[t].a1, A2 = act[t].a2, A3 = act[t].a3;
         int dl = 0, dh = 0;
         dl = sdot4(lo[0], A0.x, dl); dl = sdot4(lo[1], A0.y, dl);
         dl = sdot4(lo[2], A0.z, dl); dl = sdot4(lo[3], A0.w, dl);
@@ -118,7 +96,7 @@ __device__ inline void compute_q45(const Raw<FMT> &r, int c, const int8_t *__res
         dh = sdot4(hi[4], A3.x, dh); dh = sdot4(hi[5], A3.y, dh);
         dh = sdot4(hi[6], A3.z, dh); dh = sdot4(hi[7], A3.w, dh);
         // bsums 4c..4c+3: the first two cover sub-block 2c, the last two 2c+1
-        const uint2 b = *reinterpret_cast<const uint2 *>(bs + t * KB + 4 * c);
+        const uint2 b = make_uint2(act[t].b.x, act[t].b.y);
         const int b0 = (int16_t)(b.x & 0xFFFF), b1 = (int16_t)(b.x >> 16);
         const int b2 = (int16_t)(b.y & 0xFFFF), b3 = (int16_t)(b.y >> 16);
         out[t].p = sc0 * dl + sc1 * dh;
@@ -132,8 +110,7 @@ __device__ inline void compute_q45(const Raw<FMT> &r, int c, const int8_t *__res
 // high two bits come from bits 2u.. (resp. 2u+4..) of high byte 32h + l.
 // Signed scales; P = iacc - 32*bacc, exact in int32.
 template <int T>
-__device__ inline void compute_q6(const Raw<KQ_Q6_K> &r, int c, const int8_t *__restrict__ a, int64_t K,
-                                  const int16_t *__restrict__ bs, int64_t KB, Lane (&out)[T], float &d)
+__device__ inline void compute_q6(const Raw<KQ_Q6_K> &r, int c, const Act (&act)[T], Lane (&out)[T], float &d)
 {
     const int h = c >> 1, u = c & 1;
     const uint32_t lw[8] = {r.l0.x, r.l0.y, r.l0.z, r.l0.w, r.l1.x, r.l1.y, r.l1.z, r.l1.w};
@@ -149,11 +126,7 @@ __device__ inline void compute_q6(const Raw<KQ_Q6_K> &r, int c, const int8_t *__
     const int sc_ = (int8_t)byte_of(r.s8.y, 2 * u), sd = (int8_t)byte_of(r.s8.y, 2 * u + 1);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const int8_t *at = a + t * K + 128 * h + 32 * u;
-        const uint4 A0 = reinterpret_cast<const uint4 *>(at)[0];
-        const uint4 A1 = reinterpret_cast<const uint4 *>(at)[1];
-        const uint4 A2 = reinterpret_cast<const uint4 *>(at + 64)[0];
-        const uint4 A3 = reinterpret_cast<const uint4 *>(at + 64)[1];
+        const uint4 A0 = act[t].a0, A1 = act[t].a1, A2 = act[t].a2, A3 = act[t].a3;
         int d0 = 0, d1 = 0, d2 = 0, d3 = 0;
         d0 = sdot4(lo[0], A0.x, d0); d0 = sdot4(lo[1], A0.y, d0);
         d0 = sdot4(lo[2], A0.z, d0); d0 = sdot4(lo[3], A0.w, d0);
@@ -164,7 +137,7 @@ __device__ inline void compute_q6(const Raw<KQ_Q6_K> &r, int c, const int8_t *__
         d3 = sdot4(hi[4], A3.x, d3); d3 = sdot4(hi[5], A3.y, d3);
         d3 = sdot4(hi[6], A3.z, d3); d3 = sdot4(hi[7], A3.w, d3);
         // bsums 8h..8h+7: 2u, 2u+1 pair with the low half, 2u+4, 2u+5 the high
-        const uint4 b = *reinterpret_cast<const uint4 *>(bs + t * KB + 8 * h);
+        const uint4 b = act[t].b;
         const uint32_t blo = u ? b.y : b.x, bhi = u ? b.w : b.z;
         const int ba = (int16_t)(blo & 0xFFFF), bb = (int16_t)(blo >> 16);
         const int bc = (int16_t)(bhi & 0xFFFF), bd = (int16_t)(bhi >> 16);
@@ -177,22 +150,34 @@ __device__ inline void compute_q6(const Raw<KQ_Q6_K> &r, int c, const int8_t *__
 
 }  // namespace
 
-// One workgroup = 16 rows x all superblocks; its waves take contiguous runs
-// of `per_wave` superblocks, U at a time with every load of the U issued
-// before the first is consumed.
-template <int FMT, int T, int U, bool PART>
+template <int CTRL>
+__device__ inline float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// One workgroup = 16/SL rows x all superblocks.  A wave step covers SL
+// adjacent superblocks of each of its 16/SL rows (quad q = sig + SL*rho of
+// the wave: superblock slot sig, row rho), so small-n matrices still spread
+// over many workgroups; the waves of a workgroup take contiguous runs of
+// `per_wave` steps, U steps at a time with every weight load of the U issued
+// before the first is consumed.  The SL slot sums of a row meet by DPP
+// mirrors, the waves' sums in LDS.
+template <int FMT, int T, int U, int SL, bool PART>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                     const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                     const int16_t *__restrict__ xbs, float *__restrict__ y,
                                                     int32_t *__restrict__ Pout, int32_t *__restrict__ Mout,
                                                     int per_wave)
 {
-    __shared__ float red[16][T][16];
+    constexpr int RPW = 16 / SL;
+    __shared__ float red[16][T][RPW];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
-    const int c = lane & 3, rho = lane >> 2;
-    const int64_t row = (int64_t)blockIdx.x * 16 + rho;
+    const int c = lane & 3, quad = lane >> 2;
+    const int sig = quad % SL, rho = quad / SL;
+    const int64_t row = (int64_t)blockIdx.x * RPW + rho;
     const bool valid = row < n;
     const int64_t K = (int64_t)nsb * QK, KB = K / 16;
     const Planes pl = planes_of(FMT, n, nsb);
@@ -203,31 +188,87 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = 0.0f;
 
-    const int s_begin = wave * per_wave;
-    const int s_end = min(nsb, s_begin + per_wave);
-    for (int s0 = s_begin; s0 < s_end; s0 += U) {
-        Raw<FMT> raw[U];
+    const int nsteps = (nsb + SL - 1) / SL;
+    const int j_begin = wave * per_wave;
+    const int j_end = min(nsteps, j_begin + per_wave);
+    // this lane's superblock at step j, clamped in bounds (out-of-range
+    // slots re-read a valid superblock and contribute nothing)
+    auto sb_at = [&](int j) { return min(min(j, j_end - 1) * SL + sig, nsb - 1); };
+
+    // Small batches stage the whole Q8_K image (codes + bsums, T*K*9/8
+    // bytes) in LDS with coalesced 16-byte loads, so no lane waits on an L2
+    // round trip for its codes after its weights land; larger batches read
+    // the codes straight from L2.  Memory counters retire in issue order, so
+    // the staging loads go out before the weight loads: writing them to LDS
+    // then waits only for themselves, and their L2 latency hides under the
+    // HBM fetch of the weights.
+    constexpr bool LDSA = T <= 2;
+    constexpr int SMAX = 2;  // staged 16-byte chunks held per thread
+    extern __shared__ __align__(16) uint8_t stage[];
+    const int64_t nq = T * K / 16, nst = nq + T * K / 128;  // chunks: codes, then bsums
+    auto src_chunk = [&](int64_t i) {
+        return i < nq ? reinterpret_cast<const uint4 *>(xq)[i] : reinterpret_cast<const uint4 *>(xbs)[i - nq];
+    };
+    uint4 st[SMAX];
+    if constexpr (LDSA) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (s0 + u < s_end) load_raw(raw[u], w, pl, rbase + s0 + u, c);
+        for (int j = 0; j < SMAX; ++j) {
+            const int64_t i = threadIdx.x + (int64_t)j * blockDim.x;
+            if (i < nst) st[j] = src_chunk(i);
+        }
+    }
+
+    // unconditional, so the count of loads in flight is static and the
+    // staging write below waits only for the staging loads
+    Raw<FMT> raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_raw(raw[u], w, pl, rbase + sb_at(j_begin + u), c);
+
+    const int8_t *aq = xq;
+    const int16_t *ab = xbs;
+    if constexpr (LDSA) {
+        uint4 *dst = reinterpret_cast<uint4 *>(stage);
+#pragma unroll
+        for (int j = 0; j < SMAX; ++j) {
+            const int64_t i = threadIdx.x + (int64_t)j * blockDim.x;
+            if (i < nst) dst[i] = st[j];
+        }
+        for (int64_t i = threadIdx.x + (int64_t)SMAX * blockDim.x; i < nst; i += blockDim.x) dst[i] = src_chunk(i);
+        __syncthreads();
+        aq = reinterpret_cast<const int8_t *>(stage);
+        ab = reinterpret_cast<const int16_t *>(stage + T * K);
+    }
+
+    for (int j0 = j_begin; j0 < j_end; j0 += U) {
+        if (j0 != j_begin) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_raw(raw[u], w, pl, rbase + sb_at(j0 + u), c);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = s0 + u;
-            if (s >= s_end) break;
+            const int j = j0 + u;
+            if (j >= j_end) break;
+            const int s = sb_at(j);
+            const bool live = j * SL + sig < nsb;  // slot holds a real superblock
+            Act cur[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                load_act<FMT>(cur[t], aq + t * K + (int64_t)s * QK, ab + t * KB + (int64_t)s * 16, c);
             Lane part[T];
             float d, dmin = 0.0f;
             if constexpr (FMT == KQ_Q6_K)
-                compute_q6<T>(raw[u], c, xq + (int64_t)s * QK, K, xbs + (int64_t)s * 16, KB, part, d);
+                compute_q6<T>(raw[u], c, cur, part, d);
             else
-                compute_q45<FMT, T>(raw[u], c, xq + (int64_t)s * QK, K, xbs + (int64_t)s * 16, KB, part, d,
-                                    dmin);
+                compute_q45<FMT, T>(raw[u], c, cur, part, d, dmin);
+            d = live ? d : 0.0f;
+            dmin = live ? dmin : 0.0f;
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 // DPP sums run with every lane of the wave active
                 const int P = quad_sum(part[t].p);
                 const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
                 const float d8 = xs[t * nsb + s];
-                if (PART && c == 0 && valid) {
+                if (PART && c == 0 && valid && live) {
                     const int64_t o = ((int64_t)t * n + row) * nsb + s;
                     Pout[o] = P;
                     if (Mout) Mout[o] = M;
@@ -238,14 +279,20 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
         }
     }
 
-    if (c == 0) {
+    // sum the SL superblock slots of each row (identical across a quad)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if constexpr (SL >= 2) acc[t] += dpp_f<0x141>(acc[t]);  // row_half_mirror: quad pairs
+        if constexpr (SL >= 4) acc[t] += dpp_f<0x140>(acc[t]);  // row_mirror: quad 0<->3, 1<->2
+    }
+    if (c == 0 && sig == 0) {
 #pragma unroll
         for (int t = 0; t < T; ++t) red[wave][t][rho] = acc[t];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 16 * T; i += blockDim.x) {
-        const int t = i >> 4, r = i & 15;
-        const int64_t rr = (int64_t)blockIdx.x * 16 + r;
+    for (int i = threadIdx.x; i < RPW * T; i += blockDim.x) {
+        const int t = i / RPW, r = i % RPW;
+        const int64_t rr = (int64_t)blockIdx.x * RPW + r;
         if (rr < n) {
             float v = 0.0f;
             for (int wv = 0; wv < nw; ++wv) v += red[wv][t][r];
@@ -266,37 +313,43 @@ struct GemvArgs {
     int per_wave;
 };
 
-template <int FMT, int T, int U, bool PART>
+template <int FMT, int T, int U, int SL, bool PART>
 static void launch_one(dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
-    hipLaunchKernelGGL((gemv_kernel<FMT, T, U, PART>), g, b, 0, st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs, a.y,
-                       a.P, a.M, a.per_wave);
+    const size_t lds = T <= 2 ? (size_t)T * a.nsb * QK * 9 / 8 : 0;  // staged Q8_K image
+    hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART>), g, b, lds, st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs,
+                       a.y, a.P, a.M, a.per_wave);
 }
 
 template <int FMT, int T>
-static void launch_u(int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_u(int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
-    if (part) return launch_one<FMT, T, 4, true>(g, b, st, a);
+    if (sl == 4) {
+        if (part) return launch_one<FMT, T, 2, 4, true>(g, b, st, a);
+        if (u == 1) return launch_one<FMT, T, 1, 4, false>(g, b, st, a);
+        return launch_one<FMT, T, 2, 4, false>(g, b, st, a);
+    }
+    if (part) return launch_one<FMT, T, 4, 1, true>(g, b, st, a);
     switch (u) {
-    case 1: return launch_one<FMT, T, 1, false>(g, b, st, a);
-    case 2: return launch_one<FMT, T, 2, false>(g, b, st, a);
-    case 3: return launch_one<FMT, T, 3, false>(g, b, st, a);
-    default: return launch_one<FMT, T, 4, false>(g, b, st, a);
+    case 1: return launch_one<FMT, T, 1, 1, false>(g, b, st, a);
+    case 2: return launch_one<FMT, T, 2, 1, false>(g, b, st, a);
+    case 3: return launch_one<FMT, T, 3, 1, false>(g, b, st, a);
+    default: return launch_one<FMT, T, 4, 1, false>(g, b, st, a);
     }
 }
 
 template <int FMT>
-static void launch_t(int t, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_t(int t, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
     switch (t) {
-    case 1: return launch_u<FMT, 1>(u, part, g, b, st, a);
-    case 2: return launch_u<FMT, 2>(u, part, g, b, st, a);
-    case 3: return launch_u<FMT, 3>(u, part, g, b, st, a);
-    case 4: return launch_u<FMT, 4>(u, part, g, b, st, a);
-    case 5: return launch_u<FMT, 5>(u, part, g, b, st, a);
-    case 6: return launch_u<FMT, 6>(u, part, g, b, st, a);
-    case 7: return launch_u<FMT, 7>(u, part, g, b, st, a);
-    default: return launch_u<FMT, 8>(u, part, g, b, st, a);
+    case 1: return launch_u<FMT, 1>(sl, u, part, g, b, st, a);
+    case 2: return launch_u<FMT, 2>(sl, u, part, g, b, st, a);
+    case 3: return launch_u<FMT, 3>(sl, u, part, g, b, st, a);
+    case 4: return launch_u<FMT, 4>(sl, u, part, g, b, st, a);
+    case 5: return launch_u<FMT, 5>(sl, u, part, g, b, st, a);
+    case 6: return launch_u<FMT, 6>(sl, u, part, g, b, st, a);
+    case 7: return launch_u<FMT, 7>(sl, u, part, g, b, st, a);
+    default: return launch_u<FMT, 8>(sl, u, part, g, b, st, a);
     }
 }
 
@@ -304,21 +357,26 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
                 const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st)
 {
     const int64_t nsb = k / QK;
-    const int64_t groups = (n + 15) / 16;
+    // 16 rows per workgroup when that gives two or more workgroups per CU,
+    // else 4 rows x 4 adjacent superblocks per wave step
+    const int sl = t <= 2 ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
+    const int64_t groups = (n + 16 / sl - 1) / (16 / sl);
+    const int64_t nsteps = (nsb + sl - 1) / sl;
     // about 16 waves per CU in flight, at most 16 waves per workgroup, and
-    // every wave of a workgroup with the same share of superblocks
+    // every wave of a workgroup with the same share of steps
     int64_t nw = (4096 + groups - 1) / groups;
     nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
-    nw = nw > nsb ? nsb : nw;
-    const int64_t per_wave = (nsb + nw - 1) / nw;
-    nw = (nsb + per_wave - 1) / per_wave;
-    const int u = per_wave >= 4 ? 4 : (int)per_wave;
+    nw = nw > nsteps ? nsteps : nw;
+    const int64_t per_wave = (nsteps + nw - 1) / nw;
+    nw = (nsteps + per_wave - 1) / per_wave;
+    const int umax = sl == 4 ? 2 : 4;
+    const int u = per_wave >= umax ? umax : (int)per_wave;
     GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave};
     const dim3 g((unsigned)groups), b((unsigned)(64 * nw));
     const bool part = P != nullptr;
-    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, u, part, g, b, st, a);
-    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, u, part, g, b, st, a);
-    else launch_t<KQ_Q6_K>((int)t, u, part, g, b, st, a);
+    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, sl, u, part, g, b, st, a);
+    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, sl, u, part, g, b, st, a);
+    else launch_t<KQ_Q6_K>((int)t, sl, u, part, g, b, st, a);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 
