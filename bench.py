@@ -15,6 +15,10 @@ enough distinct copies that one step's rotation reads over 1 GiB of weights,
 so the 256 MB Infinity Cache cannot serve them from cache: every GEMV reads
 its weights from HBM.
 
+The GEMV leg runs kq_quantize_q8k then kq_gemv; the fused entry point
+kq_gemv_f32 (Q8_K quantisation inside the GEMV kernel, one launch) is timed
+beside it as gemv_fused.
+
 Printed: one JSON line.  Each leg is captured into a HIP graph (one per
 weight copy) and replayed, so the GPU runs its launches back to back.
 `value` is the GEMV leg's throughput in GB/s of algorithmic bytes (packed
@@ -42,9 +46,29 @@ GEMM_M = 512
 BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 
 
-def gemv_bytes(fmt, n, k, t=1):
+# HBM traffic of kq_gemv per launch, averaged over the six matrices of a
+# step: FETCH_SIZE + WRITE_SIZE counter passes scaled by a plain-copy
+# reference (profiles/kq_gemv_hbm_traffic_qwen3_4b_ffn.md).  It holds only
+# for the GEMV sources it was measured on; with any other sources the
+# roofline reports traffic as null.
+GEMV_TRAFFIC = {"src_sha256_16": "c32ca253a2f82f95", "bytes_per_launch": 17422080}
+
+
+def gemv_src_hash():
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "quant_matmul_amd", "csrc")
+    data = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("kq_gemv.hip", "kq_common.h"))
+    return hashlib.sha256(data).hexdigest()[:16]
+
+
+def gemv_bytes(fmt, n, k, t=1, fused=True):
+    """Algorithmic bytes of one GEMV: packed weights + the activation as the
+    call takes it (f32 for the fused entry, else the 292-byte-per-256 Q8_K
+    image) + the f32 output."""
     nsb = k // 256
-    return n * nsb * BYTES[fmt] + t * nsb * 292 + 4 * t * n
+    act = 4 * t * k if fused else t * nsb * 292
+    return n * nsb * BYTES[fmt] + act + 4 * t * n
 
 
 def parse():
@@ -81,7 +105,7 @@ def cpu_baseline(seconds):
                 xq, xs, xbs = oracle.quantize_q8k(x)
                 oracle.matmul(fmt, recs, xq, xs, xbs)
                 t_used += time.perf_counter() - t0
-                done_bytes += gemv_bytes(fmt, rows, k)
+                done_bytes += gemv_bytes(fmt, rows, k, fused=False)
                 matrices += 1
         if time.perf_counter() - start > 4 * seconds:
             break
@@ -141,10 +165,16 @@ def main():
     # replayed, so the GPU runs the launches back to back instead of
     # waiting on Python's launch rate.
     def gemv_leg(c):
+        # decode: quantise the f32 activation to Q8_K, then the GEMV
         for j, (fmt, n, k, pl) in enumerate(mats):
             x1, (xq, xs, xbs), _, _ = acts[k]
             kq.kq_quantize_q8k(x1, 1, k, xq, xs, xbs)
             kq.kq_gemv(fmt, pl[c], n, k, xq, xs, xbs, 1, ys[j][0])
+
+    def gemv_leg_fused(c):
+        # the same with the quantiser fused into the GEMV (kq_gemv_f32)
+        for j, (fmt, n, k, pl) in enumerate(mats):
+            kq.kq_gemv_f32(fmt, pl[c], n, k, acts[k][0], 1, ys[j][0])
 
     def gemm_leg(c):
         for j, (fmt, n, k, pl) in enumerate(mats):
@@ -176,6 +206,7 @@ def main():
     graphs = {}
     if "gemv" in legs:
         graphs["gemv"] = [capture(gemv_leg, c) for c in range(copies)]
+        graphs["gemv2"] = [capture(gemv_leg_fused, c) for c in range(copies)]
     if "gemm" in legs:
         graphs["gemm"] = [capture(gemm_leg, c) for c in range(copies)]
     # activations quantised once for the kernel-only graphs
@@ -185,13 +216,13 @@ def main():
         kq.kq_quantize_q8k(xm, GEMM_M, k, *qm)
     reps = {"gemv": 8 * copies, "gemm": copies}
     kgraphs = {kind: [capture(kernel_only, kind, j, reps[kind]) for j in range(len(mats))]
-               for kind in graphs}
+               for kind in ("gemv", "gemm") if kind in graphs}
     torch.cuda.synchronize()
 
     def run_steps(nsteps, rec):
         for i in range(nsteps):
             c = i % copies
-            for kind in ("gemv", "gemm"):
+            for kind in ("gemv", "gemv2", "gemm"):
                 if kind in graphs:
                     a, b = ev(), ev()
                     a.record(stream)
@@ -199,12 +230,12 @@ def main():
                     b.record(stream)
                     rec[kind].append((a, b))
 
-    run_steps(args.warmup, {"gemv": [], "gemm": []})
+    run_steps(args.warmup, {"gemv": [], "gemv2": [], "gemm": []})
     torch.cuda.synchronize()
 
     # ------------------------------------------------------ timed region --
-    rec = {"gemv": [], "gemm": []}
-    krec = {kind: [] for kind in graphs}
+    rec = {"gemv": [], "gemv2": [], "gemm": []}
+    krec = {kind: [] for kind in kgraphs}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = ev()
@@ -212,7 +243,7 @@ def main():
     run_steps(args.steps, rec)
     end = ev()
     end.record(stream)
-    for kind in graphs:  # kernel-only replays: the roofline's launch durations
+    for kind in kgraphs:  # kernel-only replays: the roofline's launch durations
         for j in range(len(mats)):
             a, b = ev(), ev()
             a.record(stream)
@@ -238,19 +269,27 @@ def main():
     per = {}
     if "gemv" in graphs:
         leg_ms = ms(rec["gemv"])
-        leg_bytes = args.steps * sum(gemv_bytes(f, n, k) for f, n, k, _ in mats)
+        leg_bytes = args.steps * sum(gemv_bytes(f, n, k, fused=False) for f, n, k, _ in mats)
         out["value"] = leg_bytes / (leg_ms * 1e-3) / 1e9
         out["gemv_leg_ms_per_step"] = leg_ms / args.steps
-        kb = sum(reps["gemv"] * gemv_bytes(f, n, k) for f, n, k, _ in mats)
+        leg2_ms = ms(rec["gemv2"])
+        leg2_bytes = args.steps * sum(gemv_bytes(f, n, k, fused=True) for f, n, k, _ in mats)
+        out["gemv_fused"] = {"value": leg2_bytes / (leg2_ms * 1e-3) / 1e9, "unit": "GB/s",
+                             "note": "kq_gemv_f32: Q8_K quantisation inside the GEMV, one launch per matrix"}
+        kb = sum(reps["gemv"] * gemv_bytes(f, n, k, fused=False) for f, n, k, _ in mats)
         kms = ms(krec["gemv"])
         ach = kb / (kms * 1e-3) / 1e9
+        traffic = (GEMV_TRAFFIC["bytes_per_launch"]
+                   if gemv_src_hash() == GEMV_TRAFFIC["src_sha256_16"] else None)
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBPS, "traffic": None, "kernel": "kq::gemv_kernel",
+                           "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
+                           "algorithmic_bytes_per_launch": kb / (reps["gemv"] * len(mats)),
+                           "kernel": "kq::gemv_kernel (kq_gemv)",
                            "avg_launch_us": kms * 1e3 / (reps["gemv"] * len(mats))}
         for j, (f, n, k, _) in enumerate(mats):
             us = krec["gemv"][j][0].elapsed_time(krec["gemv"][j][1]) * 1e3 / reps["gemv"]
             per.setdefault(f"{f}_{n}x{k}", {})["gemv"] = {
-                "us": us, "GBps": gemv_bytes(f, n, k) / (us * 1e-6) / 1e9}
+                "us": us, "GBps": gemv_bytes(f, n, k, fused=False) / (us * 1e-6) / 1e9}
     if "gemm" in graphs:
         leg_ms = ms(rec["gemm"])
         ops_step = sum(2 * GEMM_M * n * k for _, n, k, _ in mats)

@@ -98,6 +98,19 @@ int kq_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs,
 int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
             const int16_t *xbs, int64_t t, float *y, void *stream);
 
+/* Decode GEMV with the Q8_K quantisation fused in: f32 activations
+ * x[t][k], t in 1..8, in; y[t][n] out.  The quantisation is the one of
+ * kq_quantize_q8k, bit for bit; the kernel-arc page's chain regrain
+ * (commit message of that name) quantises inside the consuming chain at
+ * whole-superblock granules -- here inside the GEMV, which saves the
+ * separate quantiser launch and the image's round trip.  For t <= 2 this
+ * is one kernel: every workgroup quantises x into LDS; xq/xs/xbs may then
+ * be NULL (all three), or receive the Q8_K image.  For t > 2 the image
+ * buffers are required and the call runs kq_quantize_q8k then kq_gemv.
+ * x must be 16-byte aligned and finite. */
+int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float *x, int64_t t,
+                float *y, int8_t *xq, float *xs, int16_t *xbs, void *stream);
+
 /* Prefill GEMM, m >= 1 tokens: y[m][n], same contract as kq_gemv. */
 int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
             const int16_t *xbs, int64_t m, float *y, void *stream);

@@ -26,7 +26,7 @@ KQ_OK, KQ_EINVAL, KQ_EFORMAT, KQ_EALIGN, KQ_ELAUNCH = 0, -1, -2, -3, -4
 
 # every entry point of include/kq.h
 SYMBOLS = ("kq_record_bytes", "kq_packed_bytes", "kq_pack", "kq_unpack", "kq_quantize_q8k",
-           "kq_gemv", "kq_gemm", "kq_gemv_partials", "kq_gemm_partials", "kq_strerror")
+           "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemv_partials", "kq_gemm_partials", "kq_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quant_matmul_amd.build`")
@@ -42,12 +42,13 @@ lib.kq_unpack.argtypes = [_int, _p, _i64, _i64, _p, _p]
 lib.kq_quantize_q8k.argtypes = [_p, _i64, _i64, _p, _p, _p, _p]
 lib.kq_gemv.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
 lib.kq_gemm.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
+lib.kq_gemv_f32.argtypes = [_int, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
 lib.kq_gemv_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
 lib.kq_gemm_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
 lib.kq_strerror.argtypes = [_int]
 lib.kq_strerror.restype = ctypes.c_char_p
-for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_gemv", "kq_gemm", "kq_gemv_partials",
-           "kq_gemm_partials"):
+for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_gemv", "kq_gemv_f32", "kq_gemm",
+           "kq_gemv_partials", "kq_gemm_partials"):
     getattr(lib, _f).restype = _int
 
 
@@ -108,6 +109,11 @@ def kq_quantize_q8k(x, t: int, k: int, xq, xs, xbs, stream=None):
 def kq_gemv(fmt, w_planes, n: int, k: int, xq, xs, xbs, t: int, y, stream=None):
     _ok(lib.kq_gemv(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), t, _ptr(y),
                     _stream(stream)), "kq_gemv")
+
+
+def kq_gemv_f32(fmt, w_planes, n: int, k: int, x, t: int, y, xq=None, xs=None, xbs=None, stream=None):
+    _ok(lib.kq_gemv_f32(_fmt(fmt), _ptr(w_planes), n, k, _ptr(x), t, _ptr(y), _ptr(xq), _ptr(xs),
+                        _ptr(xbs), _stream(stream)), "kq_gemv_f32")
 
 
 def kq_gemm(fmt, w_planes, n: int, k: int, xq, xs, xbs, m: int, y, stream=None):

@@ -11,7 +11,8 @@ int launch_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float 
 int launch_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, hipStream_t stream);
 int launch_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, hipStream_t stream);
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st);
+                const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
+                const float *x = nullptr, int8_t *oq = nullptr, float *os = nullptr, int16_t *obs = nullptr);
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
                 const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st);
 }  // namespace kq
@@ -87,6 +88,24 @@ int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
             const int16_t *xbs, int64_t t, float *y, void *stream)
 {
     int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, t, 8, y, nullptr, nullptr, false);
+    if (rc) return rc;
+    return kq::launch_gemv(fmt, w_planes, n, k, xq, xs, xbs, t, y, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float *x, int64_t t, float *y,
+                int8_t *xq, float *xs, int16_t *xbs, void *stream)
+{
+    if (!known(fmt)) return KQ_EFORMAT;
+    if (check_nk(n, k) || t < 1 || t > 8 || !w_planes || !x || !y) return KQ_EINVAL;
+    const bool image = xq || xs || xbs;
+    if (image && !(xq && xs && xbs)) return KQ_EINVAL;  // all three or none
+    if (t > 2 && !image) return KQ_EINVAL;              // batches past 2 need the image buffers
+    if (!aligned(w_planes, 16) || !aligned(x, 16) || !aligned(y, 4)) return KQ_EALIGN;
+    if (image && (!aligned(xq, 16) || !aligned(xbs, 16) || !aligned(xs, 4))) return KQ_EALIGN;
+    if (t <= 2)
+        return kq::launch_gemv(fmt, w_planes, n, k, nullptr, nullptr, nullptr, t, y, nullptr, nullptr,
+                               (hipStream_t)stream, x, xq, xs, xbs);
+    int rc = kq::launch_quantize_q8k(x, t, k, xq, xs, xbs, (hipStream_t)stream);
     if (rc) return rc;
     return kq::launch_gemv(fmt, w_planes, n, k, xq, xs, xbs, t, y, nullptr, nullptr, (hipStream_t)stream);
 }

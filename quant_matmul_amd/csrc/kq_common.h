@@ -98,6 +98,54 @@ __device__ inline int quad_sum(int v)
     return v;
 }
 
+// Q8_K quantisation of one 256-value chunk by one wave: lane l holds values
+// 4l..4l+3.  amax over the chunk, d8 = amax/127 (binary32, correctly
+// rounded), code = rint(x/d8) (correctly rounded quotient, half to even)
+// clamped to [-127, 127]; an all-zero chunk gives d8 = 0 and zero codes.
+// Returns the lane's four codes packed in a dword; `qsum` receives the sum
+// of the 16 codes of the lane's quad (bsum g = l/4) and d8 the scale.
+template <int CTRL>
+__device__ inline float dpp_max(float v)
+{
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false)));
+}
+
+// Maximum over the 64 lanes (max is exact, so any order gives the same
+// bits): DPP within each row of 16, then the four row maxima.
+__device__ inline float wave_max(float v)
+{
+    v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max<0x141>(v);  // row_half_mirror
+    v = dpp_max<0x140>(v);  // row_mirror: every lane holds its row's max
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ inline uint32_t q8k_chunk(float4 v, int &qsum, float &d8)
+{
+    const float amax = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    d8 = 0.0f;
+    if (amax != 0.0f) {
+        d8 = __fdiv_rn(amax, 127.0f);
+        auto code = [d8](float f) {
+            const int a = (int)rintf(__fdiv_rn(f, d8));
+            return a > 127 ? 127 : (a < -127 ? -127 : a);
+        };
+        a0 = code(v.x);
+        a1 = code(v.y);
+        a2 = code(v.z);
+        a3 = code(v.w);
+    }
+    qsum = quad_sum(a0 + a1 + a2 + a3);
+    return (uint32_t)(a0 & 0xFF) | ((uint32_t)(a1 & 0xFF) << 8) | ((uint32_t)(a2 & 0xFF) << 16) |
+           ((uint32_t)(a3 & 0xFF) << 24);
+}
+
 // Raw bytes of one 64-weight share of a superblock, as loaded from the
 // planes by one lane (GEMV) or one unpack task (GEMM), before any compute.
 // Share c of a Q4_K/Q5_K superblock is sub-blocks 2c and 2c+1 (the low and

@@ -163,13 +163,21 @@ __device__ inline float dpp_f(float v)
 // `per_wave` steps, U steps at a time with every weight load of the U issued
 // before the first is consumed.  The SL slot sums of a row meet by DPP
 // mirrors, the waves' sums in LDS.
-template <int FMT, int T, int U, int SL, bool PART>
+//
+// FUSE (batch <= 2): the workgroup quantises the f32 activation x itself
+// into its LDS stage (the same per-chunk arithmetic as kq_quantize_q8k, so
+// the image is bit-identical) instead of reading a Q8_K image; workgroup 0
+// also writes that image out when oq is non-null.
+template <int FMT, int T, int U, int SL, bool PART, bool FUSE>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                     const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                     const int16_t *__restrict__ xbs, float *__restrict__ y,
                                                     int32_t *__restrict__ Pout, int32_t *__restrict__ Mout,
-                                                    int per_wave)
+                                                    int per_wave, const float *__restrict__ x,
+                                                    int8_t *__restrict__ oq, float *__restrict__ os,
+                                                    int16_t *__restrict__ obs)
 {
+    static_assert(!FUSE || T <= 2, "the fused quantiser stages the image in LDS");
     constexpr int RPW = 16 / SL;
     __shared__ float red[16][T][RPW];
     const int lane = threadIdx.x & 63;
@@ -210,11 +218,23 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
         return i < nq ? reinterpret_cast<const uint4 *>(xq)[i] : reinterpret_cast<const uint4 *>(xbs)[i - nq];
     };
     uint4 st[SMAX];
-    if constexpr (LDSA) {
+    if constexpr (LDSA && !FUSE) {
 #pragma unroll
         for (int j = 0; j < SMAX; ++j) {
             const int64_t i = threadIdx.x + (int64_t)j * blockDim.x;
             if (i < nst) st[j] = src_chunk(i);
+        }
+    }
+    // fused: wave w quantises chunks w, w + nw, ... of x (chunk = t*nsb + s);
+    // the first CMAX of them are loaded before the weights
+    constexpr int CMAX = 8;
+    const int nchunks = T * nsb;
+    float4 xr[FUSE ? CMAX : 1];
+    if constexpr (FUSE) {
+#pragma unroll
+        for (int j = 0; j < CMAX; ++j) {
+            const int ch = wave + j * nw;
+            if (ch < nchunks) xr[j] = reinterpret_cast<const float4 *>(x + (int64_t)ch * QK)[lane];
         }
     }
 
@@ -226,7 +246,39 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
 
     const int8_t *aq = xq;
     const int16_t *ab = xbs;
-    if constexpr (LDSA) {
+    const float *d8src = xs;
+    if constexpr (FUSE) {
+        int8_t *sq = reinterpret_cast<int8_t *>(stage);
+        int16_t *sbs = reinterpret_cast<int16_t *>(stage + T * K);
+        float *sd8 = reinterpret_cast<float *>(stage + T * K * 9 / 8);
+        auto quant = [&](int ch, float4 v) {
+            int qsum;
+            float d8;
+            const uint32_t packed = q8k_chunk(v, qsum, d8);
+            reinterpret_cast<uint32_t *>(sq + (int64_t)ch * QK)[lane] = packed;
+            if ((lane & 3) == 0) sbs[ch * 16 + (lane >> 2)] = (int16_t)qsum;
+            if (lane == 0) sd8[ch] = d8;
+        };
+#pragma unroll
+        for (int j = 0; j < CMAX; ++j) {
+            const int ch = wave + j * nw;
+            if (ch < nchunks) quant(ch, xr[j]);
+        }
+        for (int ch = wave + CMAX * nw; ch < nchunks; ch += nw)
+            quant(ch, reinterpret_cast<const float4 *>(x + (int64_t)ch * QK)[lane]);
+        __syncthreads();
+        if (oq != nullptr && blockIdx.x == 0) {
+            // the Q8_K image, for callers that keep it
+            for (int64_t i = threadIdx.x; i < T * K / 16; i += blockDim.x)
+                reinterpret_cast<uint4 *>(oq)[i] = reinterpret_cast<const uint4 *>(sq)[i];
+            for (int64_t i = threadIdx.x; i < T * K / 128; i += blockDim.x)
+                reinterpret_cast<uint4 *>(obs)[i] = reinterpret_cast<const uint4 *>(sbs)[i];
+            for (int i = threadIdx.x; i < nchunks; i += blockDim.x) os[i] = sd8[i];
+        }
+        aq = sq;
+        ab = sbs;
+        d8src = sd8;
+    } else if constexpr (LDSA) {
         uint4 *dst = reinterpret_cast<uint4 *>(stage);
 #pragma unroll
         for (int j = 0; j < SMAX; ++j) {
@@ -267,7 +319,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
                 // DPP sums run with every lane of the wave active
                 const int P = quad_sum(part[t].p);
                 const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
-                const float d8 = xs[t * nsb + s];
+                const float d8 = d8src[t * nsb + s];
                 if (PART && c == 0 && valid && live) {
                     const int64_t o = ((int64_t)t * n + row) * nsb + s;
                     Pout[o] = P;
@@ -311,14 +363,27 @@ struct GemvArgs {
     float *y;
     int32_t *P, *M;
     int per_wave;
+    const float *x;  // fused: f32 activations, and the optional image out
+    int8_t *oq;
+    float *os;
+    int16_t *obs;
 };
 
 template <int FMT, int T, int U, int SL, bool PART>
 static void launch_one(dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
-    const size_t lds = T <= 2 ? (size_t)T * a.nsb * QK * 9 / 8 : 0;  // staged Q8_K image
-    hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART>), g, b, lds, st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs,
-                       a.y, a.P, a.M, a.per_wave);
+    // staged Q8_K image (codes + bsums), plus the scales when fused
+    size_t lds = T <= 2 ? (size_t)T * a.nsb * QK * 9 / 8 : 0;
+    if constexpr (T <= 2 && !PART) {
+        if (a.x) {
+            lds += (size_t)T * a.nsb * sizeof(float);
+            hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, true>), g, b, lds, st, a.w, a.n, a.nsb, a.xq,
+                               a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.x, a.oq, a.os, a.obs);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false>), g, b, lds, st, a.w, a.n, a.nsb, a.xq, a.xs,
+                       a.xbs, a.y, a.P, a.M, a.per_wave, a.x, a.oq, a.os, a.obs);
 }
 
 template <int FMT, int T>
@@ -354,11 +419,14 @@ static void launch_t(int t, int sl, int u, bool part, dim3 g, dim3 b, hipStream_
 }
 
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st)
+                const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
+                const float *x, int8_t *oq, float *os, int16_t *obs)
 {
     const int64_t nsb = k / QK;
     // 16 rows per workgroup when that gives two or more workgroups per CU,
     // else 4 rows x 4 adjacent superblocks per wave step
+    // (the fused path keeps the same shape, so its y is bit-identical to
+    // quantise-then-GEMV)
     const int sl = t <= 2 ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
     const int64_t groups = (n + 16 / sl - 1) / (16 / sl);
     const int64_t nsteps = (nsb + sl - 1) / sl;
@@ -371,7 +439,7 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
     nw = (nsteps + per_wave - 1) / per_wave;
     const int umax = sl == 4 ? 2 : 4;
     const int u = per_wave >= umax ? umax : (int)per_wave;
-    GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave};
+    GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave, x, oq, os, obs};
     const dim3 g((unsigned)groups), b((unsigned)(64 * nw));
     const bool part = P != nullptr;
     if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, sl, u, part, g, b, st, a);

@@ -14,12 +14,6 @@
 
 namespace kq {
 
-__device__ inline float wave_max(float v)
-{
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
 __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restrict__ x, int64_t chunks,
                                                            int8_t *__restrict__ xq, float *__restrict__ xs,
                                                            int16_t *__restrict__ xbs)
@@ -29,29 +23,12 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restri
     if (chunk >= chunks) return;  // whole wave exits together
 
     const float4 v = reinterpret_cast<const float4 *>(x + chunk * QK)[lane];
-    const float amax = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-
-    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-    float d8 = 0.0f;
-    if (amax != 0.0f) {
-        d8 = __fdiv_rn(amax, 127.0f);
-        auto code = [d8](float f) {
-            int a = (int)rintf(__fdiv_rn(f, d8));
-            return a > 127 ? 127 : (a < -127 ? -127 : a);
-        };
-        a0 = code(v.x);
-        a1 = code(v.y);
-        a2 = code(v.z);
-        a3 = code(v.w);
-    }
-    const uint32_t packed = (uint32_t)(a0 & 0xFF) | ((uint32_t)(a1 & 0xFF) << 8) |
-                            ((uint32_t)(a2 & 0xFF) << 16) | ((uint32_t)(a3 & 0xFF) << 24);
+    int qsum;
+    float d8;
+    const uint32_t packed = q8k_chunk(v, qsum, d8);
     reinterpret_cast<uint32_t *>(xq + chunk * QK)[lane] = packed;
-
     // lanes 4g..4g+3 hold the 16 codes of group g
-    int s = a0 + a1 + a2 + a3;
-    s = quad_sum(s);
-    if ((lane & 3) == 0) xbs[chunk * 16 + (lane >> 2)] = (int16_t)s;
+    if ((lane & 3) == 0) xbs[chunk * 16 + (lane >> 2)] = (int16_t)qsum;
     if (lane == 0) xs[chunk] = d8;
 }
 

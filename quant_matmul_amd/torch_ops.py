@@ -8,8 +8,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (kq_gemm, kq_gemm_partials, kq_gemv, kq_gemv_partials, kq_pack, kq_packed_bytes,
-               kq_quantize_q8k, kq_record_bytes, kq_unpack)
+from . import (kq_gemm, kq_gemm_partials, kq_gemv, kq_gemv_f32, kq_gemv_partials, kq_pack,
+               kq_packed_bytes, kq_quantize_q8k, kq_record_bytes, kq_unpack)
 
 QK = 256
 
@@ -50,6 +50,15 @@ def gemv(fmt, planes, n: int, k: int, q8, stream=None) -> torch.Tensor:
     y = torch.empty((t, n), dtype=torch.float32, device=xq.device)
     kq_gemv(fmt, planes, n, k, xq, xs, xbs, t, y, stream)
     return y
+
+
+def gemv_f32(fmt, planes, n: int, k: int, x: torch.Tensor, keep_image: bool = False, stream=None):
+    """Fused quantise + GEMV; returns y, or (y, (xq, xs, xbs)) with keep_image."""
+    t = x.shape[0]
+    y = torch.empty((t, n), dtype=torch.float32, device=x.device)
+    q8 = q8k_buffers(t, k, x.device) if (keep_image or t > 2) else (None, None, None)
+    kq_gemv_f32(fmt, planes, n, k, x, t, y, *q8, stream)
+    return (y, q8) if keep_image else y
 
 
 def gemm(fmt, planes, n: int, k: int, q8, stream=None) -> torch.Tensor:

@@ -84,6 +84,24 @@ def test_partials_argument_checks():
         assert f(6, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 1, GOOD16, ODD, None, None) == kq.KQ_EALIGN
 
 
+def test_fused_gemv_argument_checks():
+    f = kq.lib.kq_gemv_f32
+    ok = dict(fmt=4, w=GOOD16, n=16, k=256, x=GOOD16, t=1, y=GOOD16, xq=None, xs=None, xbs=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["fmt"], a["w"], a["n"], a["k"], a["x"], a["t"], a["y"], a["xq"], a["xs"], a["xbs"], None)
+    assert call(fmt=0) == kq.KQ_EFORMAT
+    assert call(k=384) == kq.KQ_EINVAL
+    assert call(t=0) == kq.KQ_EINVAL and call(t=9) == kq.KQ_EINVAL
+    assert call(x=None) == kq.KQ_EINVAL and call(y=None) == kq.KQ_EINVAL
+    # the image buffers come all three or none, and batches past 2 need them
+    assert call(xq=GOOD16) == kq.KQ_EINVAL
+    assert call(t=3) == kq.KQ_EINVAL
+    assert call(x=GOOD16 + 4) == kq.KQ_EALIGN
+    assert call(xq=GOOD16 + 4, xs=GOOD16, xbs=GOOD16) == kq.KQ_EALIGN
+
+
 def test_quantize_and_pack_argument_checks():
     q = kq.lib.kq_quantize_q8k
     assert q(GOOD16, 0, 256, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL

@@ -117,6 +117,31 @@ def test_gemv_parity(fmt, t, n, k):
     assert torch.equal(y, y2)
 
 
+# ------------------------------------------------- fused quantise+GEMV --
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("n,k", [(256, 2560), (37, 256), (2560, 9728), (9728, 2560)])
+def test_gemv_f32_fused_matches_two_step(fmt, t, n, k):
+    c = Case(fmt, n, k, t, seed=30 + t)
+    xd = dev(c.x)
+    y, (xq, xs, xbs) = ops.gemv_f32(fmt, c.planes, n, k, xd, keep_image=True)
+    # the fused quantiser writes the same Q8_K image bits as the oracle
+    rq, rs, rbs = c.q8_host
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(xbs), rbs)
+    # and the same y as quantise-then-GEMV, bit for bit
+    y2 = ops.gemv(fmt, c.planes, n, k, c.q8)
+    assert torch.equal(y, y2)
+    if t <= 2:  # the image is optional for the one-kernel path
+        y3 = ops.gemv_f32(fmt, c.planes, n, k, xd)
+        assert torch.equal(y, y3)
+    rows = sample_rows(n) if n > 512 else None
+    y_o, _, _, R = c.oracle_rows(rows)
+    yh = host(y) if rows is None else host(y)[:, rows]
+    assert np.all(np.abs(yh.astype(np.float64) - y_o) <= TOL * R)
+
+
 # ------------------------------------------------------------ GEMM ------
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,n,k", [(128, 256, 2560), (129, 100, 768), (1, 64, 256), (300, 65, 512),
