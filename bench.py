@@ -155,7 +155,7 @@ def main():
     for i, (n, k) in enumerate(SHAPES):
         x1 = torch.from_numpy(synth.activations(1, k, synth.seed_for(1, 50 + i))).cuda()
         xm = torch.from_numpy(synth.activations(GEMM_M, k, synth.seed_for(2, 50 + i))).cuda()
-        acts[k] = (x1, ops.q8k_buffers(1, k), xm, ops.q8k_buffers(GEMM_M, k))
+        acts[k] = (x1, ops.q8k_buffers(1, k), xm, ops.q8k_tile_buffers(GEMM_M, k))
     ys = [(torch.empty((1, m[1]), device="cuda"), torch.empty((GEMM_M, m[1]), device="cuda"))
           for m in mats]
 
@@ -179,7 +179,7 @@ def main():
     def gemm_leg(c):
         for j, (fmt, n, k, pl) in enumerate(mats):
             _, _, xm, (xq, xs, xbs) = acts[k]
-            kq.kq_quantize_q8k(xm, GEMM_M, k, xq, xs, xbs)
+            kq.kq_quantize_q8k_tiles(xm, GEMM_M, k, xq, xs, xbs)
             kq.kq_gemm(fmt, pl[c], n, k, xq, xs, xbs, GEMM_M, ys[j][1])
 
     def kernel_only(kind, j, reps):
@@ -213,7 +213,7 @@ def main():
     for k in acts:
         x1, q1, xm, qm = acts[k]
         kq.kq_quantize_q8k(x1, 1, k, *q1)
-        kq.kq_quantize_q8k(xm, GEMM_M, k, *qm)
+        kq.kq_quantize_q8k_tiles(xm, GEMM_M, k, *qm)
     reps = {"gemv": 8 * copies, "gemm": copies}
     kgraphs = {kind: [capture(kernel_only, kind, j, reps[kind]) for j in range(len(mats))]
                for kind in ("gemv", "gemm") if kind in graphs}

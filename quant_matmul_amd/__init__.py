@@ -4,7 +4,7 @@ Argument marshalling only: every function below passes device pointers of
 torch tensors and the current HIP stream to the same-named C entry point in
 libkq.so, and raises KqError on a non-zero status.  Nothing here computes
 any part of the matmul.  The library must have been built in-tree
-(``python -m quant_matmul_amd.build``); importing this package without it
+(``python quant_matmul_amd/build.py``); importing this package without it
 raises ImportError -- there is no fallback.
 """
 from __future__ import annotations
@@ -26,10 +26,10 @@ KQ_OK, KQ_EINVAL, KQ_EFORMAT, KQ_EALIGN, KQ_ELAUNCH = 0, -1, -2, -3, -4
 
 # every entry point of include/kq.h
 SYMBOLS = ("kq_record_bytes", "kq_packed_bytes", "kq_pack", "kq_unpack", "kq_quantize_q8k",
-           "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemv_partials", "kq_gemm_partials", "kq_strerror")
+           "kq_q8k_tiles_bytes", "kq_quantize_q8k_tiles", "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemv_partials", "kq_gemm_partials", "kq_strerror")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quant_matmul_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python quant_matmul_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 _p, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -40,6 +40,9 @@ lib.kq_packed_bytes.restype = ctypes.c_size_t
 lib.kq_pack.argtypes = [_int, _p, _i64, _i64, _p, _p]
 lib.kq_unpack.argtypes = [_int, _p, _i64, _i64, _p, _p]
 lib.kq_quantize_q8k.argtypes = [_p, _i64, _i64, _p, _p, _p, _p]
+lib.kq_q8k_tiles_bytes.argtypes = [_i64, _i64]
+lib.kq_q8k_tiles_bytes.restype = ctypes.c_size_t
+lib.kq_quantize_q8k_tiles.argtypes = [_p, _i64, _i64, _p, _p, _p, _p]
 lib.kq_gemv.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
 lib.kq_gemm.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
 lib.kq_gemv_f32.argtypes = [_int, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
@@ -47,7 +50,7 @@ lib.kq_gemv_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p,
 lib.kq_gemm_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
 lib.kq_strerror.argtypes = [_int]
 lib.kq_strerror.restype = ctypes.c_char_p
-for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_gemv", "kq_gemv_f32", "kq_gemm",
+for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_quantize_q8k_tiles", "kq_gemv", "kq_gemv_f32", "kq_gemm",
            "kq_gemv_partials", "kq_gemm_partials"):
     getattr(lib, _f).restype = _int
 
@@ -106,6 +109,15 @@ def kq_quantize_q8k(x, t: int, k: int, xq, xs, xbs, stream=None):
         "kq_quantize_q8k")
 
 
+def kq_q8k_tiles_bytes(t: int, k: int) -> int:
+    return lib.kq_q8k_tiles_bytes(t, k)
+
+
+def kq_quantize_q8k_tiles(x, t: int, k: int, xq_tiles, xs, xbs, stream=None):
+    _ok(lib.kq_quantize_q8k_tiles(_ptr(x), t, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), _stream(stream)),
+        "kq_quantize_q8k_tiles")
+
+
 def kq_gemv(fmt, w_planes, n: int, k: int, xq, xs, xbs, t: int, y, stream=None):
     _ok(lib.kq_gemv(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), t, _ptr(y),
                     _stream(stream)), "kq_gemv")
@@ -116,8 +128,8 @@ def kq_gemv_f32(fmt, w_planes, n: int, k: int, x, t: int, y, xq=None, xs=None, x
                         _ptr(xbs), _stream(stream)), "kq_gemv_f32")
 
 
-def kq_gemm(fmt, w_planes, n: int, k: int, xq, xs, xbs, m: int, y, stream=None):
-    _ok(lib.kq_gemm(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), m, _ptr(y),
+def kq_gemm(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, stream=None):
+    _ok(lib.kq_gemm(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), m, _ptr(y),
                     _stream(stream)), "kq_gemm")
 
 
@@ -126,8 +138,8 @@ def kq_gemv_partials(fmt, w_planes, n: int, k: int, xq, xs, xbs, t: int, y, P, M
                              _ptr(y), _ptr(P), _ptr(M), _stream(stream)), "kq_gemv_partials")
 
 
-def kq_gemm_partials(fmt, w_planes, n: int, k: int, xq, xs, xbs, m: int, y, P, M, stream=None):
-    _ok(lib.kq_gemm_partials(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), m,
+def kq_gemm_partials(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, P, M, stream=None):
+    _ok(lib.kq_gemm_partials(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), m,
                              _ptr(y), _ptr(P), _ptr(M), _stream(stream)), "kq_gemm_partials")
 
 

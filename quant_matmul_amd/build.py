@@ -1,6 +1,8 @@
 """Build libkq.so (the kq C ABI + its gfx950 kernels) in-tree with hipcc.
 
-    python -m quant_matmul_amd.build
+    python quant_matmul_amd/build.py
+
+(run as a script, not `-m`: importing the package loads the library.)
 """
 from __future__ import annotations
 

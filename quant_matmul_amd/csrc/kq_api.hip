@@ -8,6 +8,8 @@
 namespace kq {
 int launch_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
                         hipStream_t stream);
+int launch_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
+                              hipStream_t stream);
 int launch_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, hipStream_t stream);
 int launch_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, hipStream_t stream);
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -40,11 +42,23 @@ int check_matmul(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq,
     if (t < 1 || t > tmax) return KQ_EINVAL;
     // the grid and every row-major offset stay inside int64 / uint32
     if (n * t > ((int64_t)1 << 40)) return KQ_EINVAL;
+    // the GEMM addresses 256 tokens of codes with 32-bit offsets
+    if (tmax > 8 && k > kq::GEMM_KMAX) return KQ_EINVAL;
     if (!w || !xq || !xs || !xbs || !y) return KQ_EINVAL;
     if (partials && (!P || (fmt != KQ_Q6_K && !M))) return KQ_EINVAL;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xbs, 16) || !aligned(xs, 4) || !aligned(y, 4))
         return KQ_EALIGN;
     if (partials && (!aligned(P, 4) || (M && !aligned(M, 4)))) return KQ_EALIGN;
+    return KQ_OK;
+}
+
+// t rows of k activations: the quantiser's grid (4 chunks per workgroup,
+// rows rounded up to 16) must fit gridDim.x < 2^31
+int check_quantize(const float *x, int64_t t, int64_t k, const int8_t *xq, const float *xs, const int16_t *xbs)
+{
+    if (t < 1 || t > INT_MAX || check_nk(1, k) || !x || !xq || !xs || !xbs) return KQ_EINVAL;
+    if ((t + 15) * (k / kq::QK) > ((int64_t)1 << 32)) return KQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xbs, 16) || !aligned(xs, 4)) return KQ_EALIGN;
     return KQ_OK;
 }
 
@@ -78,10 +92,23 @@ int kq_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml,
 
 int kq_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs, void *stream)
 {
-    if (t < 1 || t > INT_MAX || check_nk(1, k) || !x || !xq || !xs || !xbs) return KQ_EINVAL;
-    if (t * (k / kq::QK) > ((int64_t)1 << 36)) return KQ_EINVAL;
-    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xbs, 16) || !aligned(xs, 4)) return KQ_EALIGN;
+    int rc = check_quantize(x, t, k, xq, xs, xbs);
+    if (rc) return rc;
     return kq::launch_quantize_q8k(x, t, k, xq, xs, xbs, (hipStream_t)stream);
+}
+
+size_t kq_q8k_tiles_bytes(int64_t t, int64_t k)
+{
+    if (t < 1 || t > INT_MAX || check_nk(1, k)) return 0;
+    return (size_t)((t + 15) / 16 * 16) * (size_t)k;
+}
+
+int kq_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq_tiles, float *xs, int16_t *xbs,
+                          void *stream)
+{
+    int rc = check_quantize(x, t, k, xq_tiles, xs, xbs);
+    if (rc) return rc;
+    return kq::launch_quantize_q8k_tiles(x, t, k, xq_tiles, xs, xbs, (hipStream_t)stream);
 }
 
 int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,

@@ -22,6 +22,8 @@
 namespace kq {
 
 constexpr int QK = 256;
+// largest k the GEMM takes: 256 tokens of codes stay below 2^31 bytes
+constexpr int64_t GEMM_KMAX = ((int64_t)1 << 23) - QK;
 
 __host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 

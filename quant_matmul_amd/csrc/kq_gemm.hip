@@ -7,36 +7,45 @@
 //  * Panel unpack, once per (row panel, token block).  As in the page's kq
 //    v3 panel scratch ("The pieces", kq v3 item: unpack the packed planes
 //    once per (group, token-block) and amortise it over the token block),
-//    each workgroup unpacks the superblock of its BN weight rows into LDS
-//    once and reuses it for all BM tokens.  What lands in LDS is not the raw
-//    quant but the sub-scale-folded weight w' = sc*q (Q4_K/Q5_K, 0..1953) or
-//    sc*(q-32) (Q6_K, -4064..4096), split into two int8 digits
+//    each workgroup unpacks the superblock of its 32 weight rows into LDS
+//    once and reuses it for all 256 tokens.  What lands in LDS is not the
+//    raw quant but the sub-scale-folded weight w' = sc*q (Q4_K/Q5_K,
+//    0..1953) or sc*(q-32) (Q6_K, -4064..4096), split into two int8 digits
 //    w' = 128*h + l with l in 0..127: the MFMA cannot apply a per-row,
 //    per-sub-block scale, so folding it into the operand is what keeps the
 //    per-sub-block integer fold on the matrix cores.
-//  * Dense contraction: v_mfma_i32_32x32x32_i8, a high-digit pass, a shift by
-//    7, a low-digit pass into the same int32 accumulator -- which then holds
-//    P = sum_j sc_j * dot_j exactly (|P| < 2^27).
+//  * Dense contraction: v_mfma_i32_16x16x64_i8, a high-digit pass, a shift
+//    by 7, a low-digit pass into the same int32 accumulator -- which then
+//    holds P = sum_j sc_j * dot_j exactly (|P| < 2^27).
 //  * Min term: M = sum_g m_{g/2} * bsum_g is a 16-deep contraction per
-//    superblock, done on one v_mfma_f32_32x32x16_f16 (bsums |.| <= 2032 and
+//    superblock, done on v_mfma_f32_16x16x16_f16 (bsums |.| <= 2032 and
 //    m <= 63 are exact in f16, and |M| < 2^24 keeps the f32 sum exact).
 //  * Epilogue per superblock: acc += d8 * (d*P - dmin*M).
 //
-// Pipeline.  A workgroup is 4 waves over a 256-token x 32*TN-row tile; each
-// wave owns 64 tokens x 32*TN rows (2 x TN MFMA tiles).  Per superblock s
-// the Q8_K codes of the wave's tokens sit in registers (prefetched one
-// superblock ahead), the digit panel in one of two LDS buffers; while the
-// high-digit MFMAs of s run, the wave unpacks its share of superblock s+1
-// (whose packed bytes were prefetched) into the other buffer, so the VALU
-// unpack overlaps the matrix pipe.  One barrier per superblock.
+// A operand.  The codes come from the tile image of the Q8_K quantiser
+// (16 tokens x 64 codes per contiguous KiB), so each A fragment is one fully
+// coalesced 1 KiB load; with row-major codes the same fragment touches 16
+// half-used cache lines, and the L2-to-L1 traffic that costs, not the
+// matrix cores, bounded the kernel.  Codes and bsums are read through
+// buffer resources based at the workgroup's first token: tokens past the
+// image read as zero and their outputs are never stored.
+//
+// Pipeline.  A workgroup is 4 waves over a 256-token x 32-row tile; each
+// wave owns 64 tokens x 32 rows (4 x 2 MFMA tiles of 16x16).  Per
+// superblock s the wave's codes sit in registers, the digit panel in one of
+// two LDS buffers; while the high-digit MFMAs of s run, the wave unpacks its
+// share of superblock s+1 (whose packed bytes were prefetched) into the
+// other buffer, so the VALU unpack overlaps the matrix pipe, and each
+// 64-deep K step of the codes is refilled with superblock s+1 as soon as
+// its low-digit MFMAs are issued.  One barrier per superblock.
 #include "kq_common.h"
 
 namespace kq {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int LDS_STRIDE = 272;  // bytes per digit row: 256 + 16 pad
 
@@ -203,16 +212,15 @@ __device__ inline void tile_of(int b, int G, int mtiles, int &nt, int &mt)
 
 }  // namespace
 
-template <int FMT, int TN, bool PART>
+template <int FMT, bool PART>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
-                                                   const int8_t *__restrict__ xq, const float *__restrict__ xs,
-                                                   const int16_t *__restrict__ xbs, int64_t mtok,
-                                                   float *__restrict__ y, int32_t *__restrict__ Pout,
-                                                   int32_t *__restrict__ Mout, int mtiles)
+                                                      const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                                                      const int16_t *__restrict__ xbs, int64_t mtok,
+                                                      float *__restrict__ y, int32_t *__restrict__ Pout,
+                                                      int32_t *__restrict__ Mout, int mtiles)
 {
-    constexpr int BM = 256, BN = 32 * TN;
-    constexpr int TASKS = BN * 8;  // 32-weight unpack tasks per panel
-    constexpr int TPT = (TASKS + 255) / 256;
+    constexpr int BM = 256, BN = 32;
+    static_assert(BN * 8 == 256, "one 32-weight unpack task per thread");
     __shared__ __align__(16) int8_t wh[2][BN * LDS_STRIDE];
     __shared__ __align__(16) int8_t wl[2][BN * LDS_STRIDE];
     __shared__ __align__(16) _Float16 mexp[2][BN * 16];
@@ -222,181 +230,183 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     int nt, mt;
     tile_of(blockIdx.x, gridDim.x, mtiles, nt, mt);
     const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
-    const int lane = threadIdx.x & 63, wm = threadIdx.x >> 6;
-    const int l32 = lane & 31, lh = lane >> 5;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wm = tid >> 6;
+    const int l16 = lane & 15, lq = lane >> 4;
     const int64_t K = (int64_t)nsb * QK, KB = K / 16;
     const Planes pl = planes_of(FMT, n, nsb);
 
-    // Unpack tasks of this thread: rows past n read row n-1 (in bounds)
-    // and unpack as zero weights.
-    Half<FMT> raw[TPT];
-    int64_t wrow[TPT];
-    bool wvalid[TPT];
-#pragma unroll
-    for (int q = 0; q < TPT; ++q) {
-        const int64_t row = n0 + ((threadIdx.x + 256 * q) >> 3);
-        wvalid[q] = row < n;
-        wrow[q] = (wvalid[q] ? row : n - 1) * nsb;
-    }
-    const int64_t t_d8 = m0 + threadIdx.x;  // this thread's d8 slot
+    // unpack task of this thread (rows past n read row n-1, unpack as 0)
+    const int64_t wr = n0 + (tid >> 3);
+    const bool wvalid = wr < n;
+    const int64_t wrow = (wvalid ? wr : n - 1) * nsb;
+    Half<FMT> raw;
+    const int64_t t_d8 = m0 + tid;
     const float *xs_row = xs + (t_d8 < mtok ? t_d8 : mtok - 1) * nsb;
     float d8n = 0.0f;
     auto load_w = [&](int s) {
-#pragma unroll
-        for (int q = 0; q < TPT; ++q)
-            if (threadIdx.x + 256 * q < TASKS) load_half(raw[q], w, pl, wrow[q] + s, (threadIdx.x + 256 * q) & 7);
+        load_half(raw, w, pl, wrow + s, tid & 7);
         d8n = t_d8 < mtok ? xs_row[s] : 0.0f;
     };
     auto unpack_w = [&](int b) {
-#pragma unroll
-        for (int q = 0; q < TPT; ++q) {
-            const int task = threadIdx.x + 256 * q;
-            if (task < TASKS) unpack_half(raw[q], wvalid[q], task >> 3, task & 7, wh[b], wl[b], mexp[b], dn[b], dmn[b]);
-        }
-        d8s[b][threadIdx.x] = d8n;
+        unpack_half(raw, wvalid, tid >> 3, tid & 7, wh[b], wl[b], mexp[b], dn[b], dmn[b]);
+        d8s[b][tid] = d8n;
     };
 
-    // Q8_K codes (MFMA A operand: the lane's token, k bytes 16*lh + 32*ks)
-    // and bsums (f16 A operand of the min term) of the wave's 64 tokens;
-    // tokens past m read token m-1 and are never stored
-    const int8_t *arow[2];
-    const int16_t *brow[2];
+    // Codes (A operand, tile image: 16 tokens x 64 codes per KiB) and bsums
+    // (f16 A operand of the min term, row-major) of the wave's 64 tokens.
+    // The tile image holds tokens up to m rounded up to 16.
+    const uint64_t a_bytes = (uint64_t)(((mtok + 15) & ~(int64_t)15) - m0) * (uint64_t)K;
+    const uint64_t b_bytes = (uint64_t)(mtok - m0) * (uint64_t)KB * 2;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xq + m0 * K), 0, (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xbs + m0 * KB), 0, (int)(uint32_t)(b_bytes < 0xFFFFFFFFu ? b_bytes : 0xFFFFFFFFu), 0x00020000);
+    // 32-bit offsets: the caller bounds k so that 256 tokens of codes < 2^31
+    int aoff[4], boff[4];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        int64_t t = m0 + wm * 64 + mi * 32 + l32;
-        t = t < mtok ? t : mtok - 1;
-        arow[mi] = xq + t * K + 16 * lh;
-        brow[mi] = xbs + t * KB + 8 * lh;
+    for (int mi = 0; mi < 4; ++mi) {
+        aoff[mi] = (wm * 4 + mi) * 16 * (int)K + 16 * lane;
+        boff[mi] = (wm * 64 + mi * 16 + l16) * (int)KB * 2 + 8 * lq;
     }
-    i32x4 A[2][8];
-    f16x8 Ab[2];
-    auto load_a = [&](int s) {
+    i32x4 A[4][4];
+    f16x4 Ab[4];
+    auto load_a = [&](int s, int ks) {
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
+        for (int mi = 0; mi < 4; ++mi)
+            A[mi][ks] = __builtin_bit_cast(
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[mi] + (s * 4 + ks) * 1024, 0, 0));
+    };
+    auto load_bs = [&](int s) {
+        if constexpr (FMT != KQ_Q6_K) {
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                A[mi][ks] = *reinterpret_cast<const i32x4 *>(arow[mi] + (int64_t)s * QK + 32 * ks);
-            if constexpr (FMT != KQ_Q6_K) {
-                const uint4 bq = *reinterpret_cast<const uint4 *>(brow[mi] + (int64_t)s * 16);
-                const uint32_t bw[4] = {bq.x, bq.y, bq.z, bq.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    Ab[mi][2 * e] = (_Float16)(int16_t)(bw[e] & 0xFFFF);
-                    Ab[mi][2 * e + 1] = (_Float16)(int16_t)(bw[e] >> 16);
-                }
+            for (int mi = 0; mi < 4; ++mi) {
+                const i32x2 bq =
+                    __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rB, boff[mi] + s * 32, 0, 0));
+                Ab[mi][0] = (_Float16)(int16_t)(bq.x & 0xFFFF);
+                Ab[mi][1] = (_Float16)(int16_t)(bq.x >> 16);
+                Ab[mi][2] = (_Float16)(int16_t)(bq.y & 0xFFFF);
+                Ab[mi][3] = (_Float16)(int16_t)(bq.y >> 16);
             }
         }
     };
 
-    f32x16 accf[2][TN];
+    f32x4 accf[4][2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < TN; ++ni) accf[mi][ni] = f32x16{};
+    for (int mi = 0; mi < 4; ++mi) accf[mi][0] = accf[mi][1] = f32x4{};
 
     load_w(0);
-    load_a(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) load_a(0, ks);
+    load_bs(0);
     unpack_w(0);
     if (nsb > 1) load_w(1);
     __syncthreads();
 
     for (int s = 0; s < nsb; ++s) {
         const int b = s & 1;
+        i32x4 acc[4][2];
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) {
-            const int rl = ni * 32 + l32;
-            i32x16 acci[2] = {i32x16{}, i32x16{}};
+        for (int mi = 0; mi < 4; ++mi) acc[mi][0] = acc[mi][1] = i32x4{};
+        // high-digit pass
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const i32x4 B = *reinterpret_cast<const i32x4 *>(wh[b] + rl * LDS_STRIDE + 32 * ks + 16 * lh);
+        for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
-                    acci[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acci[mi], 0, 0, 0);
+            for (int nj = 0; nj < 2; ++nj) {
+                const i32x4 B = *reinterpret_cast<const i32x4 *>(wh[b] + (nj * 16 + l16) * LDS_STRIDE + 64 * ks + 16 * lq);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[mi][ks], B, acc[mi][nj], 0, 0, 0);
             }
-            // the unpack of the next superblock overlaps these MFMAs
-            if (ni == 0 && s + 1 < nsb) unpack_w(b ^ 1);
+        }
+        // the unpack of the next superblock overlaps these MFMAs
+        if (s + 1 < nsb) unpack_w(b ^ 1);
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) acci[mi] = acci[mi] * 128;
+        for (int mi = 0; mi < 4; ++mi) {
+            acc[mi][0] = acc[mi][0] * 128;
+            acc[mi][1] = acc[mi][1] * 128;
+        }
+        // low-digit pass; each 64-deep K step of the codes is dead after it
+        // and is refilled with superblock s+1 at once
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + rl * LDS_STRIDE + 32 * ks + 16 * lh);
+        for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
-                    acci[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acci[mi], 0, 0, 0);
+            for (int nj = 0; nj < 2; ++nj) {
+                const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + (nj * 16 + l16) * LDS_STRIDE + 64 * ks + 16 * lq);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[mi][ks], B, acc[mi][nj], 0, 0, 0);
             }
-            // min term
-            f32x16 mf[2] = {f32x16{}, f32x16{}};
-            if constexpr (FMT != KQ_Q6_K) {
-                const f16x8 Bm = *reinterpret_cast<const f16x8 *>(mexp[b] + rl * 16 + 8 * lh);
+            if (s + 1 < nsb) load_a(s + 1, ks);
+        }
+        // the one float fold of superblock s; the min term (exact f16 MFMA
+        // over the 16 bsums) is formed per 16-row column just before it
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
-                    mf[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab[mi], Bm, mf[mi], 0, 0, 0);
-            }
-            if (ni == TN - 1 && s + 1 < nsb) {
-                // every MFMA reading A(s) is issued: refill A with s+1 while
-                // the epilogue below runs
-                load_a(s + 1);
-            }
-            // the one float fold of this superblock for tile column ni
+        for (int nj = 0; nj < 2; ++nj) {
+            const int rl = nj * 16 + l16;
             const float dv = dn[b][rl], dm = dmn[b][rl];
             const int64_t col = n0 + rl;
+            f32x4 mf[4];
+            if constexpr (FMT != KQ_Q6_K) {
+                const f16x4 Bm = *reinterpret_cast<const f16x4 *>(mexp[b] + rl * 16 + 4 * lq);
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) {
+                for (int mi = 0; mi < 4; ++mi)
+                    mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ab[mi], Bm, f32x4{}, 0, 0, 0);
+            }
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int tl = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                    const float Pf = (float)acci[mi][i];
-                    const float u = FMT == KQ_Q6_K ? dv * Pf : fmaf(dv, Pf, -(dm * mf[mi][i]));
-                    accf[mi][ni][i] = fmaf(d8s[b][tl], u, accf[mi][ni][i]);
+            for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tl = wm * 64 + mi * 16 + 4 * lq + i;
+                    const float Pf = (float)acc[mi][nj][i];
+                    float u;
+                    if constexpr (FMT == KQ_Q6_K) u = dv * Pf;
+                    else u = fmaf(dv, Pf, -(dm * mf[mi][i]));
+                    accf[mi][nj][i] = fmaf(d8s[b][tl], u, accf[mi][nj][i]);
                     if (PART) {
                         const int64_t t = m0 + tl;
                         if (t < mtok && col < n) {
                             const int64_t o = (t * n + col) * nsb + s;
-                            Pout[o] = acci[mi][i];
-                            if (Mout) Mout[o] = FMT == KQ_Q6_K ? 0 : (int)mf[mi][i];
+                            Pout[o] = acc[mi][nj][i];
+                            if (Mout) {
+                                if constexpr (FMT == KQ_Q6_K) Mout[o] = 0;
+                                else Mout[o] = (int)mf[mi][i];
+                            }
                         }
                     }
                 }
             }
         }
+        if (s + 1 < nsb) load_bs(s + 1);
         if (s + 2 < nsb) load_w(s + 2);
         __syncthreads();  // panel s+1 complete; panel s free for s+2
     }
 
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t t = m0 + wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = m0 + wm * 64 + mi * 16 + 4 * lq + i;
             if (t >= mtok) continue;
-            float *yr = y + t * n + n0 + l32;
 #pragma unroll
-            for (int ni = 0; ni < TN; ++ni)
-                if (n0 + ni * 32 + l32 < n) yr[ni * 32] = accf[mi][ni][i];
+            for (int nj = 0; nj < 2; ++nj) {
+                const int64_t col = n0 + nj * 16 + l16;
+                if (col < n) y[t * n + col] = accf[mi][nj][i];
+            }
         }
-}
-
-template <int FMT, int TN>
-static void launch_cfg(bool part, int64_t n, int nsb, const uint8_t *w, const int8_t *xq, const float *xs,
-                       const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
-{
-    constexpr int BM = 256, BN = 32 * TN;
-    const int64_t ntiles = (n + BN - 1) / BN, mtiles = (m + BM - 1) / BM;
-    const dim3 g((unsigned)(ntiles * mtiles)), b(256);
-    if (part)
-        hipLaunchKernelGGL((gemm_kernel<FMT, TN, true>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M,
-                           (int)mtiles);
-    else
-        hipLaunchKernelGGL((gemm_kernel<FMT, TN, false>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M,
-                           (int)mtiles);
 }
 
 template <int FMT>
 static void launch_fmt(bool part, int64_t n, int nsb, const uint8_t *w, const int8_t *xq, const float *xs,
                        const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
 {
-    // 256 x 32 tiles: the register budget of two resident workgroups per CU
-    launch_cfg<FMT, 1>(part, n, nsb, w, xq, xs, xbs, m, y, P, M, st);
+    constexpr int BM = 256, BN = 32;
+    const int64_t ntiles = (n + BN - 1) / BN, mtiles = (m + BM - 1) / BM;
+    const dim3 g((unsigned)(ntiles * mtiles)), b(256);
+    if (part)
+        hipLaunchKernelGGL((gemm_kernel<FMT, true>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles);
+    else
+        hipLaunchKernelGGL((gemm_kernel<FMT, false>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles);
 }
 
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,

@@ -9,7 +9,8 @@ import numpy as np
 import torch
 
 from . import (kq_gemm, kq_gemm_partials, kq_gemv, kq_gemv_f32, kq_gemv_partials, kq_pack,
-               kq_packed_bytes, kq_quantize_q8k, kq_record_bytes, kq_unpack)
+               kq_packed_bytes, kq_q8k_tiles_bytes, kq_quantize_q8k, kq_quantize_q8k_tiles,
+               kq_record_bytes, kq_unpack)
 
 QK = 256
 
@@ -44,6 +45,20 @@ def quantize_q8k(x: torch.Tensor, stream=None):
     return xq, xs, xbs
 
 
+def q8k_tile_buffers(t: int, k: int, device="cuda"):
+    return (torch.empty(kq_q8k_tiles_bytes(t, k), dtype=torch.int8, device=device),
+            torch.empty((t, k // QK), dtype=torch.float32, device=device),
+            torch.empty((t, k // 16), dtype=torch.int16, device=device))
+
+
+def quantize_q8k_tiles(x: torch.Tensor, stream=None):
+    """Q8_K image for the GEMM: (codes in the tile image, xs, xbs)."""
+    t, k = x.shape
+    xq, xs, xbs = q8k_tile_buffers(t, k, x.device)
+    kq_quantize_q8k_tiles(x, t, k, xq, xs, xbs, stream)
+    return xq, xs, xbs
+
+
 def gemv(fmt, planes, n: int, k: int, q8, stream=None) -> torch.Tensor:
     xq, xs, xbs = q8
     t = xq.shape[0]
@@ -61,18 +76,20 @@ def gemv_f32(fmt, planes, n: int, k: int, x: torch.Tensor, keep_image: bool = Fa
     return (y, q8) if keep_image else y
 
 
-def gemm(fmt, planes, n: int, k: int, q8, stream=None) -> torch.Tensor:
-    xq, xs, xbs = q8
-    m = xq.shape[0]
+def gemm(fmt, planes, n: int, k: int, q8t, stream=None) -> torch.Tensor:
+    """q8t: the GEMM's image (tile codes, xs, xbs), as from quantize_q8k_tiles."""
+    xq, xs, xbs = q8t
+    m = xs.shape[0]
     y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
     kq_gemm(fmt, planes, n, k, xq, xs, xbs, m, y, stream)
     return y
 
 
 def matmul_partials(kind: str, fmt, planes, n: int, k: int, q8, stream=None):
-    """(y, P, M) from kq_gemv_partials (kind 'gemv') or kq_gemm_partials."""
+    """(y, P, M) from kq_gemv_partials (kind 'gemv', row image) or
+    kq_gemm_partials (kind 'gemm', tile image)."""
     xq, xs, xbs = q8
-    t = xq.shape[0]
+    t = xs.shape[0]
     dev = xq.device
     y = torch.empty((t, n), dtype=torch.float32, device=dev)
     P = torch.empty((t, n, k // QK), dtype=torch.int32, device=dev)

@@ -74,6 +74,30 @@ def test_gemm_argument_checks():
     assert f(4, GOOD16 + 8, 16, 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EALIGN
 
 
+def test_gemm_k_bound():
+    f = kq.lib.kq_gemm
+    kmax = (1 << 23) - 256
+    assert f(4, GOOD16, 16, kmax + 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EINVAL
+    # the bound is the GEMM's: the GEMV takes the same k (fails later, on alignment)
+    assert kq.lib.kq_gemv(4, GOOD16, 16, kmax + 256, GOOD16, GOOD16, GOOD16, 1, ODD, None) == kq.KQ_EALIGN
+    assert f(4, GOOD16, 16, kmax, GOOD16, GOOD16, GOOD16, 4, ODD, None) == kq.KQ_EALIGN
+
+
+def test_tile_image_bytes_and_checks():
+    assert kq.kq_q8k_tiles_bytes(1, 256) == 16 * 256
+    assert kq.kq_q8k_tiles_bytes(16, 512) == 16 * 512
+    assert kq.kq_q8k_tiles_bytes(17, 2560) == 32 * 2560
+    assert kq.kq_q8k_tiles_bytes(512, 9728) == 512 * 9728
+    assert kq.kq_q8k_tiles_bytes(0, 256) == 0 and kq.kq_q8k_tiles_bytes(4, 100) == 0
+    q = kq.lib.kq_quantize_q8k_tiles
+    assert q(GOOD16, 0, 256, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert q(GOOD16, 1, 300, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert q(GOOD16, 1, 256, None, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert q(GOOD16, 1, 256, GOOD16 + 8, GOOD16, GOOD16, None) == kq.KQ_EALIGN
+    # the grid bound: (t + 15) * k/256 chunks at most 2^32
+    assert q(GOOD16, (1 << 31) - 1, 1 << 16, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+
+
 def test_partials_argument_checks():
     for f in (kq.lib.kq_gemv_partials, kq.lib.kq_gemm_partials):
         # P missing

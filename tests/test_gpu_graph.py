@@ -19,14 +19,14 @@ def test_graph_replays_match_eager(fmt):
     planes = ops.pack(fmt, ops.upload_records(synth.weights(fmt, n, k, 21)), n, k)
     x1 = torch.from_numpy(synth.activations(t, k, 22)).cuda()
     xm = torch.from_numpy(synth.activations(m, k, 23)).cuda()
-    q1, qm = ops.q8k_buffers(t, k), ops.q8k_buffers(m, k)
+    q1, qm = ops.q8k_buffers(t, k), ops.q8k_tile_buffers(m, k)
     y1 = torch.empty((t, n), device="cuda")
     ym = torch.empty((m, n), device="cuda")
 
     def seq():
         kq.kq_quantize_q8k(x1, t, k, *q1)
         kq.kq_gemv(fmt, planes, n, k, *q1, t, y1)
-        kq.kq_quantize_q8k(xm, m, k, *qm)
+        kq.kq_quantize_q8k_tiles(xm, m, k, *qm)
         kq.kq_gemm(fmt, planes, n, k, *qm, m, ym)
 
     seq()

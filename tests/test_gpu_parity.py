@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import synth
+from q8k_tiles import from_tiles, to_tiles
 from quant_matmul_amd import torch_ops as ops
 import quant_matmul_amd as kq
 
@@ -39,6 +40,8 @@ class Case:
         self.q8_host = oracle.quantize_q8k(self.x)
         self.planes = ops.pack(fmt, ops.upload_records(self.recs), n, k)
         self.q8 = tuple(dev(a) for a in self.q8_host)
+        # the GEMM's image: the same codes re-laid as the tile image
+        self.q8t = (dev(to_tiles(self.q8_host[0])), self.q8[1], self.q8[2])
 
     def oracle_rows(self, rows=None):
         recs = self.recs if rows is None else self.recs[rows]
@@ -79,6 +82,19 @@ def test_quantize_bit_exact(t, k):
     xq, xs, xbs = ops.quantize_q8k(dev(x))
     rq, rs, rbs = oracle.quantize_q8k(x)
     assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(xbs), rbs)
+
+
+@pytest.mark.parametrize("t,k", [(1, 256), (16, 512), (21, 2560), (512, 9728), (130, 768)])
+def test_quantize_tiles_bit_exact(t, k):
+    x = synth.activations(t, k, 60 + t)
+    x[0, :256] = 0.0
+    xq, xs, xbs = ops.quantize_q8k_tiles(dev(x))
+    rq, rs, rbs = oracle.quantize_q8k(x)
+    codes = from_tiles(host(xq), t, k)
+    assert np.array_equal(codes[:t], rq)
+    assert not codes[t:].any()  # padding tokens are zero codes
     assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(host(xbs), rbs)
 
@@ -148,9 +164,9 @@ def test_gemv_f32_fused_matches_two_step(fmt, t, n, k):
                                    (256, 300, 1024)])
 def test_gemm_parity(fmt, m, n, k):
     c = Case(fmt, n, k, m, seed=m + n)
-    y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8)
+    y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
     check(c, y, P, M)
-    y2 = ops.gemm(fmt, c.planes, n, k, c.q8)
+    y2 = ops.gemm(fmt, c.planes, n, k, c.q8t)
     assert torch.equal(y, y2)
 
 
@@ -160,7 +176,7 @@ def test_gemv_and_gemm_partials_agree(fmt):
     n, k, t = 200, 2560, 8
     c = Case(fmt, n, k, t, seed=5)
     _, P1, M1 = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
-    _, P2, M2 = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8)
+    _, P2, M2 = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
     assert torch.equal(P1, P2)
     if fmt != "q6_k":
         assert torch.equal(M1, M2)
@@ -188,9 +204,9 @@ def test_gemm_pp512_full_size_sampled(fmt, n, k):
     m = 512
     x = synth.activations(m, k, 77)
     xd = dev(x)
-    q8 = ops.quantize_q8k(xd)  # quantised on device, as in the prefill path
+    q8 = ops.quantize_q8k_tiles(xd)  # quantised on device, as in the prefill path
     c = Case(fmt, n, k, m, seed=4, x=x)
-    for a, b in zip(q8, c.q8):
+    for a, b in zip(q8, c.q8t):
         assert torch.equal(a, b)
     y = ops.gemm(fmt, c.planes, n, k, q8)
     rows = sample_rows(n)[:24]
@@ -211,7 +227,7 @@ def test_outputs_fully_written_and_guards_intact(kind, fmt):
     buf[:g] = canary
     buf[-g:] = canary
     y = buf[g:g + t * n]
-    xq, xs, xbs = c.q8
+    xq, xs, xbs = c.q8 if kind == "gemv" else c.q8t
     f = kq.kq_gemv if kind == "gemv" else kq.kq_gemm
     f(fmt, c.planes, n, k, xq, xs, xbs, t, y)
     torch.cuda.synchronize()
@@ -224,6 +240,6 @@ def test_repeat_runs_are_bitwise_identical(kind):
     n, k = 2560, 9728
     t = 4 if kind == "gemv" else 256
     c = Case("q6_k", n, k, t, seed=12)
-    f = ops.gemv if kind == "gemv" else ops.gemm
-    ys = [f("q6_k", c.planes, n, k, c.q8) for _ in range(3)]
+    f, q8 = (ops.gemv, c.q8) if kind == "gemv" else (ops.gemm, c.q8t)
+    ys = [f("q6_k", c.planes, n, k, q8) for _ in range(3)]
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
