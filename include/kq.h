@@ -34,8 +34,9 @@
  *    stream).  Every call only enqueues work and returns; nothing
  *    synchronises.  Outputs are fully overwritten.
  *  - Layouts.  Row-major and dense: x[t][k], xq[t][k], xs[t][k/256],
- *    xbs[t][k/16], y[t][n], partials[t][n][k/256] -- except the codes the
- *    GEMM reads, which come in the tile image (kq_quantize_q8k_tiles).
+ *    xbs[t][k/16], y[t][n], partials[t][n][k/256] -- except the codes and
+ *    bsums the GEMM reads, which come in the tile image
+ *    (kq_quantize_q8k_tiles).
  *  - Alignment.  w_ggml, w_planes, x, xq and xbs must be 16-byte aligned;
  *    xs, y and the partials 4-byte aligned.
  *  - Errors.  All arguments are checked on the host before any HIP call, so
@@ -94,21 +95,23 @@ int kq_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml,
 int kq_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
                     void *stream);
 
-/* Bytes of the tile image of t tokens of k codes: t rounded up to a
- * multiple of 16, times k; 0 on bad arguments. */
+/* Bytes of the codes of the tile image of t tokens of k: t rounded up to a
+ * multiple of 32, times k; 0 on bad arguments.  Its bsums take 1/8 of that. */
 size_t kq_q8k_tiles_bytes(int64_t t, int64_t k);
 
-/* kq_quantize_q8k with the codes written as the tile image the GEMM reads
- * (xq_tiles, kq_q8k_tiles_bytes(t, k) bytes); xs and xbs are row-major as
- * above and bit-identical to kq_quantize_q8k's.  Tile image: tokens in
- * groups of 16; for group g and 64-code K chunk c a contiguous 1 KiB block
- * in which byte ((q*16 + r)*16 + e), q in 0..3, r and e in 0..15, is code
- * 64c + 16q + e of token 16g + r; blocks ordered by (g, c), c fastest:
- *   xq_tiles[(((g*(k/64) + c)*4 + q)*16 + r)*16 + e] = xq[16g + r][64c + 16q + e].
- * It is the A-operand order of the 16x16x64 int8 MFMA, so the GEMM loads
- * each operand in one coalesced 1 KiB read.  Tokens t .. (rounded up to 16)
- * - 1 get zero codes. */
-int kq_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq_tiles, float *xs, int16_t *xbs,
+/* kq_quantize_q8k writing the tile image the GEMM reads: the same Q8_K
+ * values (xs row-major and bit-identical), with the codes and bsums laid out
+ * as the operands of the int8 and f16 32x32 MFMAs.  Tokens in groups of 32:
+ *   codes, kq_q8k_tiles_bytes(t, k) bytes: for group g and 32-code K chunk
+ *     c a 1 KiB block; byte ((q*32 + r)*16 + e), q in 0..1, r in 0..31, e
+ *     in 0..15, is code 32c + 16q + e of token 32g + r:
+ *     xq_tiles[((g*(k/32) + c)*64 + q*32 + r)*16 + e] = xq[32g + r][32c + 16q + e];
+ *   bsums, IEEE binary16 (exact: |bsum| <= 2032), kq_q8k_tiles_bytes/8
+ *     bytes: for group g and superblock s a 1 KiB block;
+ *     xbs_tiles[((g*(k/256) + s)*64 + q*32 + r)*8 + e] = xbs[32g + r][16s + 8q + e].
+ * Each MFMA operand is then one coalesced 1 KiB load.  Tokens t .. (rounded
+ * up to 32) - 1 get zero codes and zero bsums. */
+int kq_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq_tiles, float *xs, uint16_t *xbs_tiles,
                           void *stream);
 
 /* Decode GEMV, batch t in 1..8: y[t][n] = W . a_t by the folds above,
@@ -130,10 +133,10 @@ int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float
                 float *y, int8_t *xq, float *xs, int16_t *xbs, void *stream);
 
 /* Prefill GEMM, m >= 1 tokens: y[m][n], the folds of kq_gemv.  The codes
- * are the tile image of kq_quantize_q8k_tiles (kq_q8k_tiles_bytes(m, k)
- * bytes); xs, xbs row-major.  k <= 2^23 - 256 (KQ_EINVAL above). */
+ * and bsums are the tile image of kq_quantize_q8k_tiles, xs row-major.
+ * k <= 2^23 - 256 (KQ_EINVAL above). */
 int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq_tiles, const float *xs,
-            const int16_t *xbs, int64_t m, float *y, void *stream);
+            const uint16_t *xbs_tiles, int64_t m, float *y, void *stream);
 
 /* kq_gemv that also stores each superblock's int32 partials:
  * P[t][n][k/256] and M[t][n][k/256] (Q6_K: P = iacc - 32*bacc and M = 0;
@@ -144,7 +147,7 @@ int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
 
 /* kq_gemm that also stores the int32 partials, as kq_gemv_partials. */
 int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq_tiles,
-                     const float *xs, const int16_t *xbs, int64_t m, float *y, int32_t *P,
+                     const float *xs, const uint16_t *xbs_tiles, int64_t m, float *y, int32_t *P,
                      int32_t *M, void *stream);
 
 /* Static text for a status code. */

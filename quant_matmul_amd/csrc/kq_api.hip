@@ -16,7 +16,7 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
                 const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
                 const float *x = nullptr, int8_t *oq = nullptr, float *os = nullptr, int16_t *obs = nullptr);
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st);
+                const void *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st);
 }  // namespace kq
 
 namespace {
@@ -100,15 +100,15 @@ int kq_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs,
 size_t kq_q8k_tiles_bytes(int64_t t, int64_t k)
 {
     if (t < 1 || t > INT_MAX || check_nk(1, k)) return 0;
-    return (size_t)((t + 15) / 16 * 16) * (size_t)k;
+    return (size_t)((t + 31) / 32 * 32) * (size_t)k;
 }
 
-int kq_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq_tiles, float *xs, int16_t *xbs,
+int kq_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq_tiles, float *xs, uint16_t *xbs_tiles,
                           void *stream)
 {
-    int rc = check_quantize(x, t, k, xq_tiles, xs, xbs);
+    int rc = check_quantize(x, t, k, xq_tiles, xs, (const int16_t *)xbs_tiles);
     if (rc) return rc;
-    return kq::launch_quantize_q8k_tiles(x, t, k, xq_tiles, xs, xbs, (hipStream_t)stream);
+    return kq::launch_quantize_q8k_tiles(x, t, k, xq_tiles, xs, (int16_t *)xbs_tiles, (hipStream_t)stream);
 }
 
 int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -146,17 +146,18 @@ int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
 }
 
 int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-            const int16_t *xbs, int64_t m, float *y, void *stream)
+            const uint16_t *xbs, int64_t m, float *y, void *stream)
 {
-    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, m, INT_MAX, y, nullptr, nullptr, false);
+    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, (const int16_t *)xbs, m, INT_MAX, y, nullptr, nullptr,
+                          false);
     if (rc) return rc;
     return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, (hipStream_t)stream);
 }
 
 int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                     const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *stream)
+                     const uint16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *stream)
 {
-    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, m, INT_MAX, y, P, M, true);
+    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, (const int16_t *)xbs, m, INT_MAX, y, P, M, true);
     if (rc) return rc;
     return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, (hipStream_t)stream);
 }

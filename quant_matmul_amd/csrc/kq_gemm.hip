@@ -14,50 +14,57 @@
 //    w' = 128*h + l with l in 0..127: the MFMA cannot apply a per-row,
 //    per-sub-block scale, so folding it into the operand is what keeps the
 //    per-sub-block integer fold on the matrix cores.
-//  * Dense contraction: v_mfma_i32_16x16x64_i8, a high-digit pass, a shift
+//  * Dense contraction: v_mfma_i32_32x32x32_i8, a high-digit pass, a shift
 //    by 7, a low-digit pass into the same int32 accumulator -- which then
-//    holds P = sum_j sc_j * dot_j exactly (|P| < 2^27).
+//    holds P = sum_j sc_j * dot_j exactly (|P| < 2^27).  The 32x32x32 form
+//    sustains about twice the int8 rate of the 16x16x64 form on gfx950.
 //  * Min term: M = sum_g m_{g/2} * bsum_g is a 16-deep contraction per
-//    superblock, done on v_mfma_f32_16x16x16_f16 (bsums |.| <= 2032 and
-//    m <= 63 are exact in f16, and |M| < 2^24 keeps the f32 sum exact).
+//    superblock, one v_mfma_f32_32x32x16_f16 (bsums |.| <= 2032 and m <= 63
+//    are exact in f16, and |M| < 2^24 keeps the f32 sum exact).
 //  * Epilogue per superblock: acc += d8 * (d*P - dmin*M).
 //
-// A operand.  The codes come from the tile image of the Q8_K quantiser
-// (16 tokens x 64 codes per contiguous KiB), so each A fragment is one fully
-// coalesced 1 KiB load; with row-major codes the same fragment touches 16
-// half-used cache lines, and the L2-to-L1 traffic that costs, not the
-// matrix cores, bounded the kernel.  Codes and bsums are read through
-// buffer resources based at the workgroup's first token: tokens past the
-// image read as zero and their outputs are never stored.
+// Operands from HBM.  The codes and the f16 bsums come from the tile image
+// of the Q8_K quantiser (32 tokens per 1 KiB operand), so each A operand is
+// one coalesced 1 KiB load with no conversion; row-major codes spread it
+// over 32 partly used cache lines, and that L2-to-L1 traffic, not the
+// matrix cores, bounded the kernel.  Both are read through buffer resources
+// based at the workgroup's first token: tokens past the image read as zero
+// and their outputs are never stored.
 //
 // Pipeline.  A workgroup is 4 waves over a 256-token x 32-row tile; each
-// wave owns 64 tokens x 32 rows (4 x 2 MFMA tiles of 16x16).  Per
-// superblock s the wave's codes sit in registers, the digit panel in one of
-// two LDS buffers; while the high-digit MFMAs of s run, the wave unpacks its
-// share of superblock s+1 (whose packed bytes were prefetched) into the
-// other buffer, so the VALU unpack overlaps the matrix pipe, and each
-// 64-deep K step of the codes is refilled with superblock s+1 as soon as
-// its low-digit MFMAs are issued.  One barrier per superblock.
+// wave owns 64 tokens x 32 rows (two 32x32 MFMA tiles).  Per superblock s
+// the wave's codes sit in registers, the digit panel in one of two LDS
+// buffers; while the high-digit MFMAs of s run, the wave unpacks its share
+// of superblock s+1 (whose packed bytes were prefetched) into the other
+// buffer, so the VALU unpack overlaps the matrix pipe, and each 32-deep K
+// step of the codes is refilled with superblock s+1 as soon as its
+// low-digit MFMAs are issued.  One barrier per superblock.
 #include "kq_common.h"
 
 namespace kq {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int LDS_STRIDE = 272;  // bytes per digit row: 256 + 16 pad
 
 namespace {
 
-// Split four folded weights (16-bit lanes e = w'0 | w'2 << 16 and
-// o = w'1 | w'3 << 16, each lane value in [0, 65535]) into their low digits
-// (bits 0..6) and high digits (bits 7..13), packed as four bytes each.
+// byte selectors of v_perm_b32 (bytes 0..3 = second operand, 4..7 = first)
+constexpr uint32_t SEL_EVEN = 0x0C020C00u;    // bytes 0, 2 -> 16-bit lanes
+constexpr uint32_t SEL_ODD = 0x0C030C01u;     // bytes 1, 3 -> 16-bit lanes
+constexpr uint32_t SEL_INTERLEAVE = 0x06020400u;  // low bytes of (e, o) lanes -> e0 o0 e1 o1
+
+// Digits of four 16-bit lane values (e = v0 | v2 << 16, o = v1 | v3 << 16,
+// each in [0, 16383]): low digits (bits 0..6) and high digits (bits 7..13)
+// packed as bytes v0 v1 v2 v3.  (e >> 7) keeps each lane's bits 7..14 in
+// that lane's low byte: the upper lane's bits move to bit 9 and up.
 __device__ inline void split_digits(uint32_t e, uint32_t o, uint32_t &hi, uint32_t &lo)
 {
-    lo = (e & 0x007F007Fu) | ((o & 0x007F007Fu) << 8);
-    hi = ((e >> 7) & 0x007F007Fu) | (((o >> 7) & 0x007F007Fu) << 8);
+    lo = __builtin_amdgcn_perm(o, e, SEL_INTERLEAVE) & 0x7F7F7F7Fu;
+    hi = __builtin_amdgcn_perm(o >> 7, e >> 7, SEL_INTERLEAVE);
 }
 
 // Four unsigned quants (one per byte of q, each <= 31) times scale sc
@@ -65,8 +72,8 @@ __device__ inline void split_digits(uint32_t e, uint32_t o, uint32_t &hi, uint32
 __device__ inline void digits_q45(uint32_t q, int sc, uint32_t &hi, uint32_t &lo)
 {
     // each 16-bit lane <= 31*63, and both factors fit 24 bits
-    const uint32_t e = (uint32_t)__umul24(q & 0x00FF00FFu, (uint32_t)sc);
-    const uint32_t o = (uint32_t)__umul24((q >> 8) & 0x00FF00FFu, (uint32_t)sc);
+    const uint32_t e = (uint32_t)__umul24(__builtin_amdgcn_perm(0u, q, SEL_EVEN), (uint32_t)sc);
+    const uint32_t o = (uint32_t)__umul24(__builtin_amdgcn_perm(0u, q, SEL_ODD), (uint32_t)sc);
     split_digits(e, o, hi, lo);
 }
 
@@ -79,8 +86,8 @@ __device__ inline void digits_q45(uint32_t q, int sc, uint32_t &hi, uint32_t &lo
 __device__ inline void digits_q6(uint32_t q, int sc, uint32_t &hi, uint32_t &lo)
 {
     const int bias = (4096 - 32 * sc) * 0x00010001;
-    const uint32_t e = (uint32_t)(__mul24((int)(q & 0x00FF00FFu), sc) + bias);
-    const uint32_t o = (uint32_t)(__mul24((int)((q >> 8) & 0x00FF00FFu), sc) + bias);
+    const uint32_t e = (uint32_t)(__mul24((int)__builtin_amdgcn_perm(0u, q, SEL_EVEN), sc) + bias);
+    const uint32_t o = (uint32_t)(__mul24((int)__builtin_amdgcn_perm(0u, q, SEL_ODD), sc) + bias);
     uint32_t hu;
     split_digits(e, o, hu, lo);
     hi = ((hu | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
@@ -215,7 +222,7 @@ __device__ inline void tile_of(int b, int G, int mtiles, int &nt, int &mt)
 template <int FMT, bool PART>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                       const int8_t *__restrict__ xq, const float *__restrict__ xs,
-                                                      const int16_t *__restrict__ xbs, int64_t mtok,
+                                                      const _Float16 *__restrict__ xbs, int64_t mtok,
                                                       float *__restrict__ y, int32_t *__restrict__ Pout,
                                                       int32_t *__restrict__ Mout, int mtiles)
 {
@@ -232,8 +239,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wm = tid >> 6;
-    const int l16 = lane & 15, lq = lane >> 4;
-    const int64_t K = (int64_t)nsb * QK, KB = K / 16;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int64_t K = (int64_t)nsb * QK;
     const Planes pl = planes_of(FMT, n, nsb);
 
     // unpack task of this thread (rows past n read row n-1, unpack as 0)
@@ -253,51 +260,46 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         d8s[b][tid] = d8n;
     };
 
-    // Codes (A operand, tile image: 16 tokens x 64 codes per KiB) and bsums
-    // (f16 A operand of the min term, row-major) of the wave's 64 tokens.
-    // The tile image holds tokens up to m rounded up to 16.
-    const uint64_t a_bytes = (uint64_t)(((mtok + 15) & ~(int64_t)15) - m0) * (uint64_t)K;
-    const uint64_t b_bytes = (uint64_t)(mtok - m0) * (uint64_t)KB * 2;
+    // Codes (A operand) and f16 bsums (A operand of the min term) of the
+    // wave's 64 tokens = two 32-token groups, from the tile image, which
+    // holds tokens up to m rounded up to 32.
+    const int64_t mpad = (mtok + 31) & ~(int64_t)31;
+    const uint64_t a_bytes = (uint64_t)(mpad - m0) * (uint64_t)K;
+    const uint64_t b_bytes = (uint64_t)(mpad - m0) * (uint64_t)nsb * 32;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(xq + m0 * K), 0, (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu), 0x00020000);
     const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(xbs + m0 * KB), 0, (int)(uint32_t)(b_bytes < 0xFFFFFFFFu ? b_bytes : 0xFFFFFFFFu), 0x00020000);
+        (void *)(xbs + m0 * nsb * 16), 0, (int)(uint32_t)(b_bytes < 0xFFFFFFFFu ? b_bytes : 0xFFFFFFFFu),
+        0x00020000);
     // 32-bit offsets: the caller bounds k so that 256 tokens of codes < 2^31
-    int aoff[4], boff[4];
+    int aoff[2], boff[2];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        aoff[mi] = (wm * 4 + mi) * 16 * (int)K + 16 * lane;
-        boff[mi] = (wm * 64 + mi * 16 + l16) * (int)KB * 2 + 8 * lq;
+    for (int mi = 0; mi < 2; ++mi) {
+        aoff[mi] = (wm * 2 + mi) * 32 * (int)K + 16 * lane;
+        boff[mi] = (wm * 2 + mi) * nsb * 1024 + 16 * lane;
     }
-    i32x4 A[4][4];
-    f16x4 Ab[4];
+    i32x4 A[2][8];
+    f16x8 Ab[2];
     auto load_a = [&](int s, int ks) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 2; ++mi)
             A[mi][ks] = __builtin_bit_cast(
-                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[mi] + (s * 4 + ks) * 1024, 0, 0));
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[mi] + (s * 8 + ks) * 1024, 0, 0));
     };
     auto load_bs = [&](int s) {
         if constexpr (FMT != KQ_Q6_K) {
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const i32x2 bq =
-                    __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rB, boff[mi] + s * 32, 0, 0));
-                Ab[mi][0] = (_Float16)(int16_t)(bq.x & 0xFFFF);
-                Ab[mi][1] = (_Float16)(int16_t)(bq.x >> 16);
-                Ab[mi][2] = (_Float16)(int16_t)(bq.y & 0xFFFF);
-                Ab[mi][3] = (_Float16)(int16_t)(bq.y >> 16);
-            }
+            for (int mi = 0; mi < 2; ++mi)
+                Ab[mi] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, boff[mi] + s * 1024, 0, 0));
         }
     };
 
-    f32x4 accf[4][2];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) accf[mi][0] = accf[mi][1] = f32x4{};
+    f32x16 accf[2];
+    accf[0] = accf[1] = f32x16{};
 
     load_w(0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) load_a(0, ks);
+    for (int ks = 0; ks < 8; ++ks) load_a(0, ks);
     load_bs(0);
     unpack_w(0);
     if (nsb > 1) load_w(1);
@@ -305,73 +307,56 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
 
     for (int s = 0; s < nsb; ++s) {
         const int b = s & 1;
-        i32x4 acc[4][2];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) acc[mi][0] = acc[mi][1] = i32x4{};
+        i32x16 acc[2];
+        acc[0] = acc[1] = i32x16{};
         // high-digit pass
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 8; ++ks) {
+            const i32x4 B = *reinterpret_cast<const i32x4 *>(wh[b] + l32 * LDS_STRIDE + 32 * ks + 16 * lh);
 #pragma unroll
-            for (int nj = 0; nj < 2; ++nj) {
-                const i32x4 B = *reinterpret_cast<const i32x4 *>(wh[b] + (nj * 16 + l16) * LDS_STRIDE + 64 * ks + 16 * lq);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[mi][ks], B, acc[mi][nj], 0, 0, 0);
-            }
+            for (int mi = 0; mi < 2; ++mi)
+                acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
         }
         // the unpack of the next superblock overlaps these MFMAs
         if (s + 1 < nsb) unpack_w(b ^ 1);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            acc[mi][0] = acc[mi][0] * 128;
-            acc[mi][1] = acc[mi][1] * 128;
-        }
-        // low-digit pass; each 64-deep K step of the codes is dead after it
+        acc[0] = acc[0] * 128;
+        acc[1] = acc[1] * 128;
+        // low-digit pass; each 32-deep K step of the codes is dead after it
         // and is refilled with superblock s+1 at once
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 8; ++ks) {
+            const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + l32 * LDS_STRIDE + 32 * ks + 16 * lh);
 #pragma unroll
-            for (int nj = 0; nj < 2; ++nj) {
-                const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + (nj * 16 + l16) * LDS_STRIDE + 64 * ks + 16 * lq);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[mi][ks], B, acc[mi][nj], 0, 0, 0);
-            }
+            for (int mi = 0; mi < 2; ++mi)
+                acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
             if (s + 1 < nsb) load_a(s + 1, ks);
         }
-        // the one float fold of superblock s; the min term (exact f16 MFMA
-        // over the 16 bsums) is formed per 16-row column just before it
+        // the one float fold of superblock s; lane l holds row n0 + l%32 and
+        // tokens 8*(r/4) + 4*(l/32) + r%4 of each 32-token group, r = 0..15
+        const float dv = dn[b][l32], dm = dmn[b][l32];
+        const int64_t col = n0 + l32;
+        f16x8 Bm;
+        if constexpr (FMT != KQ_Q6_K) Bm = *reinterpret_cast<const f16x8 *>(mexp[b] + l32 * 16 + 8 * lh);
 #pragma unroll
-        for (int nj = 0; nj < 2; ++nj) {
-            const int rl = nj * 16 + l16;
-            const float dv = dn[b][rl], dm = dmn[b][rl];
-            const int64_t col = n0 + rl;
-            f32x4 mf[4];
-            if constexpr (FMT != KQ_Q6_K) {
-                const f16x4 Bm = *reinterpret_cast<const f16x4 *>(mexp[b] + rl * 16 + 4 * lq);
+        for (int mi = 0; mi < 2; ++mi) {
+            f32x16 mf;
+            if constexpr (FMT != KQ_Q6_K) mf = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab[mi], Bm, f32x16{}, 0, 0, 0);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    mf[mi] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ab[mi], Bm, f32x4{}, 0, 0, 0);
-            }
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tl = wm * 64 + mi * 16 + 4 * lq + i;
-                    const float Pf = (float)acc[mi][nj][i];
-                    float u;
-                    if constexpr (FMT == KQ_Q6_K) u = dv * Pf;
-                    else u = fmaf(dv, Pf, -(dm * mf[mi][i]));
-                    accf[mi][nj][i] = fmaf(d8s[b][tl], u, accf[mi][nj][i]);
-                    if (PART) {
-                        const int64_t t = m0 + tl;
-                        if (t < mtok && col < n) {
-                            const int64_t o = (t * n + col) * nsb + s;
-                            Pout[o] = acc[mi][nj][i];
-                            if (Mout) {
-                                if constexpr (FMT == KQ_Q6_K) Mout[o] = 0;
-                                else Mout[o] = (int)mf[mi][i];
-                            }
+            for (int r = 0; r < 16; ++r) {
+                const int tl = wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const float Pf = (float)acc[mi][r];
+                float u;
+                if constexpr (FMT == KQ_Q6_K) u = dv * Pf;
+                else u = fmaf(dv, Pf, -(dm * mf[r]));
+                accf[mi][r] = fmaf(d8s[b][tl], u, accf[mi][r]);
+                if (PART) {
+                    const int64_t t = m0 + tl;
+                    if (t < mtok && col < n) {
+                        const int64_t o = (t * n + col) * nsb + s;
+                        Pout[o] = acc[mi][r];
+                        if (Mout) {
+                            if constexpr (FMT == KQ_Q6_K) Mout[o] = 0;
+                            else Mout[o] = (int)mf[r];
                         }
                     }
                 }
@@ -382,23 +367,21 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         __syncthreads();  // panel s+1 complete; panel s free for s+2
     }
 
+    const int64_t col = n0 + l32;
+    if (col < n) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t t = m0 + wm * 64 + mi * 16 + 4 * lq + i;
-            if (t >= mtok) continue;
-#pragma unroll
-            for (int nj = 0; nj < 2; ++nj) {
-                const int64_t col = n0 + nj * 16 + l16;
-                if (col < n) y[t * n + col] = accf[mi][nj][i];
+            for (int r = 0; r < 16; ++r) {
+                const int64_t t = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (t < mtok) y[t * n + col] = accf[mi][r];
             }
-        }
+    }
 }
 
 template <int FMT>
 static void launch_fmt(bool part, int64_t n, int nsb, const uint8_t *w, const int8_t *xq, const float *xs,
-                       const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
+                       const _Float16 *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
 {
     constexpr int BM = 256, BN = 32;
     const int64_t ntiles = (n + BN - 1) / BN, mtiles = (m + BM - 1) / BM;
@@ -410,14 +393,15 @@ static void launch_fmt(bool part, int64_t n, int nsb, const uint8_t *w, const in
 }
 
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
+                const void *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
 {
     const int nsb = (int)(k / QK);
     const uint8_t *wb = (const uint8_t *)w;
+    const _Float16 *bt = (const _Float16 *)xbs;
     const bool part = P != nullptr;
-    if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, xbs, m, y, P, M, st);
-    else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, xbs, m, y, P, M, st);
-    else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, xbs, m, y, P, M, st);
+    if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, st);
+    else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, st);
+    else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, st);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 

@@ -11,15 +11,18 @@
 // 16-byte load, one 4-byte store), the chunk's amax is a wave reduction, and
 // each 16-value bsum is the sum over a quad of lanes.
 //
-// Two code layouts.  The row image is xq[t][k].  The tile image feeds the
-// GEMM's MFMA A operand: tokens in groups of 16, and for each group and
-// each 64-code K chunk c a 1 KiB block holding, for q = 0..3, the codes
-// 64c + 16q .. +15 of the group's 16 tokens in token order -- byte
-// ((((g*(k/64) + c)*4 + q)*16 + r)*16 + e) is code 64c + 16q + e of token
-// 16g + r.  One v_mfma_i32_16x16x64_i8 operand is then one contiguous
-// 1 KiB load (lane l takes bytes 16l..16l+15), where the row image spreads
-// it over 16 half-used cache lines.  Tokens past t up to the next multiple
-// of 16 are written as zero codes.
+// Two layouts.  The row image is xq[t][k], xbs[t][k/16] int16.  The tile
+// image feeds the GEMM's MFMA operands directly: tokens in groups of 32;
+//  * codes: for group g and 32-code K chunk c a contiguous 1 KiB block in
+//    which byte ((q*32 + r)*16 + e), q in 0..1, is code 32c + 16q + e of
+//    token 32g + r -- the A operand of v_mfma_i32_32x32x32_i8, lane l = 32q
+//    + r taking bytes 16l..16l+15;
+//  * bsums: for group g and superblock s a 1 KiB block of f16 in which
+//    element (q*32 + r)*8 + e is bsum 8q + e of token 32g + r (exact: |bsum|
+//    <= 2032) -- the A operand of v_mfma_f32_32x32x16_f16.
+// One operand is then one coalesced 1 KiB load with no conversion, where
+// row-major codes spread it over 32 partly used cache lines.  Tokens past t
+// up to the next multiple of 32 get zero codes and zero bsums.
 #include "kq_common.h"
 
 namespace kq {
@@ -41,24 +44,33 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restri
     float d8;
     const uint32_t packed = q8k_chunk(v, qsum, d8);
     if constexpr (TILES) {
-        const int64_t C = (int64_t)nsb * 4, g = row >> 4;
-        const int r = (int)(row & 15), c = 4 * sb + (lane >> 4), q = (lane >> 2) & 3;
-        const int64_t off = (((g * C + c) * 4 + q) * 16 + r) * 16 + 4 * (lane & 3);
+        // lane owns codes 4*lane..+3 of the superblock: chunk c = 8*sb +
+        // lane/8, half q = (lane/4) & 1, byte 4*(lane & 3) of the piece
+        const int64_t g = row >> 5;
+        const int r = (int)(row & 31), q = (lane >> 2) & 1;
+        const int64_t c = (int64_t)sb * 8 + (lane >> 3);
+        const int64_t off = ((g * nsb * 8 + c) * 64 + q * 32 + r) * 16 + 4 * (lane & 3);
         *reinterpret_cast<uint32_t *>(xq + off) = packed;
+        // bsum j = lane/4 of this superblock, as f16, in the f16 operand order
+        if ((lane & 3) == 0) {
+            const int j = lane >> 2;
+            _Float16 *bt = reinterpret_cast<_Float16 *>(xbs);
+            bt[((g * nsb + sb) * 64 + (j >> 3) * 32 + r) * 8 + (j & 7)] = (_Float16)qsum;
+        }
+        if (real && lane == 0) xs[chunk] = d8;
     } else {
         reinterpret_cast<uint32_t *>(xq + chunk * QK)[lane] = packed;
+        // lanes 4g..4g+3 hold the 16 codes of group g
+        if ((lane & 3) == 0) xbs[chunk * 16 + (lane >> 2)] = (int16_t)qsum;
+        if (lane == 0) xs[chunk] = d8;
     }
-    if (!real) return;
-    // lanes 4g..4g+3 hold the 16 codes of group g
-    if ((lane & 3) == 0) xbs[chunk * 16 + (lane >> 2)] = (int16_t)qsum;
-    if (lane == 0) xs[chunk] = d8;
 }
 
 static int launch(bool tiles, const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
                   hipStream_t stream)
 {
     const int nsb = (int)(k / QK);
-    const int64_t rows = tiles ? (t + 15) / 16 * 16 : t;
+    const int64_t rows = tiles ? (t + 31) / 32 * 32 : t;
     const int per_block = 4;  // waves (chunks) per 256-thread workgroup
     const int64_t blocks = (rows * nsb + per_block - 1) / per_block;
     if (tiles)

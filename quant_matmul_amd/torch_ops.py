@@ -46,13 +46,15 @@ def quantize_q8k(x: torch.Tensor, stream=None):
 
 
 def q8k_tile_buffers(t: int, k: int, device="cuda"):
-    return (torch.empty(kq_q8k_tiles_bytes(t, k), dtype=torch.int8, device=device),
+    """(code tiles int8, xs float32 [t][k/256], bsum tiles float16)."""
+    nb = kq_q8k_tiles_bytes(t, k)
+    return (torch.empty(nb, dtype=torch.int8, device=device),
             torch.empty((t, k // QK), dtype=torch.float32, device=device),
-            torch.empty((t, k // 16), dtype=torch.int16, device=device))
+            torch.empty(nb // 16, dtype=torch.float16, device=device))
 
 
 def quantize_q8k_tiles(x: torch.Tensor, stream=None):
-    """Q8_K image for the GEMM: (codes in the tile image, xs, xbs)."""
+    """Q8_K image for the GEMM: (code tiles, xs, bsum tiles)."""
     t, k = x.shape
     xq, xs, xbs = q8k_tile_buffers(t, k, x.device)
     kq_quantize_q8k_tiles(x, t, k, xq, xs, xbs, stream)
@@ -77,7 +79,7 @@ def gemv_f32(fmt, planes, n: int, k: int, x: torch.Tensor, keep_image: bool = Fa
 
 
 def gemm(fmt, planes, n: int, k: int, q8t, stream=None) -> torch.Tensor:
-    """q8t: the GEMM's image (tile codes, xs, xbs), as from quantize_q8k_tiles."""
+    """q8t: the GEMM's image (code tiles, xs, bsum tiles), as from quantize_q8k_tiles."""
     xq, xs, xbs = q8t
     m = xs.shape[0]
     y = torch.empty((m, n), dtype=torch.float32, device=xq.device)

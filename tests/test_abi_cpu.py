@@ -84,9 +84,9 @@ def test_gemm_k_bound():
 
 
 def test_tile_image_bytes_and_checks():
-    assert kq.kq_q8k_tiles_bytes(1, 256) == 16 * 256
-    assert kq.kq_q8k_tiles_bytes(16, 512) == 16 * 512
-    assert kq.kq_q8k_tiles_bytes(17, 2560) == 32 * 2560
+    assert kq.kq_q8k_tiles_bytes(1, 256) == 32 * 256
+    assert kq.kq_q8k_tiles_bytes(32, 512) == 32 * 512
+    assert kq.kq_q8k_tiles_bytes(33, 2560) == 64 * 2560
     assert kq.kq_q8k_tiles_bytes(512, 9728) == 512 * 9728
     assert kq.kq_q8k_tiles_bytes(0, 256) == 0 and kq.kq_q8k_tiles_bytes(4, 100) == 0
     q = kq.lib.kq_quantize_q8k_tiles

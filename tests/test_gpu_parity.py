@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from q8k_tiles import from_tiles, to_tiles
+from q8k_tiles import bsum_tiles, from_bsum_tiles, from_tiles, to_tiles
 from quant_matmul_amd import torch_ops as ops
 import quant_matmul_amd as kq
 
@@ -41,7 +41,7 @@ class Case:
         self.planes = ops.pack(fmt, ops.upload_records(self.recs), n, k)
         self.q8 = tuple(dev(a) for a in self.q8_host)
         # the GEMM's image: the same codes re-laid as the tile image
-        self.q8t = (dev(to_tiles(self.q8_host[0])), self.q8[1], self.q8[2])
+        self.q8t = (dev(to_tiles(self.q8_host[0])), self.q8[1], dev(bsum_tiles(self.q8_host[2])))
 
     def oracle_rows(self, rows=None):
         recs = self.recs if rows is None else self.recs[rows]
@@ -86,7 +86,7 @@ def test_quantize_bit_exact(t, k):
     assert np.array_equal(host(xbs), rbs)
 
 
-@pytest.mark.parametrize("t,k", [(1, 256), (16, 512), (21, 2560), (512, 9728), (130, 768)])
+@pytest.mark.parametrize("t,k", [(1, 256), (32, 512), (21, 2560), (512, 9728), (130, 768)])
 def test_quantize_tiles_bit_exact(t, k):
     x = synth.activations(t, k, 60 + t)
     x[0, :256] = 0.0
@@ -96,7 +96,9 @@ def test_quantize_tiles_bit_exact(t, k):
     assert np.array_equal(codes[:t], rq)
     assert not codes[t:].any()  # padding tokens are zero codes
     assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
-    assert np.array_equal(host(xbs), rbs)
+    bs = from_bsum_tiles(host(xbs), t, k)
+    assert np.array_equal(bs[:t], rbs.astype(np.float64))
+    assert not bs[t:].any()
 
 
 # ------------------------------------------------------------ pack ------
