@@ -158,6 +158,8 @@ def main():
         acts[k] = (x1, ops.q8k_buffers(1, k), xm, ops.q8k_tile_buffers(GEMM_M, k))
     ys = [(torch.empty((1, m[1]), device="cuda"), torch.empty((GEMM_M, m[1]), device="cuda"))
           for m in mats]
+    # kq_gemm workspaces (zero-filled once; each call leaves them reusable)
+    wss = [ops.gemm_workspace(fmt, n, k, GEMM_M) for fmt, n, k, _ in mats]
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -180,7 +182,7 @@ def main():
         for j, (fmt, n, k, pl) in enumerate(mats):
             _, _, xm, (xq, xs, xbs) = acts[k]
             kq.kq_quantize_q8k_tiles(xm, GEMM_M, k, xq, xs, xbs)
-            kq.kq_gemm(fmt, pl[c], n, k, xq, xs, xbs, GEMM_M, ys[j][1])
+            kq.kq_gemm(fmt, pl[c], n, k, xq, xs, xbs, GEMM_M, ys[j][1], wss[j])
 
     def kernel_only(kind, j, reps):
         fmt, n, k, pl = mats[j]
@@ -190,7 +192,7 @@ def main():
             if kind == "gemv":
                 kq.kq_gemv(fmt, pl[c], n, k, *q1, 1, ys[j][0])
             else:
-                kq.kq_gemm(fmt, pl[c], n, k, *qm, GEMM_M, ys[j][1])
+                kq.kq_gemm(fmt, pl[c], n, k, *qm, GEMM_M, ys[j][1], wss[j])
 
     def capture(fn, *a):
         g = torch.cuda.CUDAGraph()

@@ -132,11 +132,24 @@ int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
 int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float *x, int64_t t,
                 float *y, int8_t *xq, float *xs, int16_t *xbs, void *stream);
 
+/* Bytes of the optional kq_gemm workspace for this shape on the current
+ * device (0: kq_gemm would not use one), or 0 on bad arguments. */
+size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
+
 /* Prefill GEMM, m >= 1 tokens: y[m][n], the folds of kq_gemv.  The codes
  * and bsums are the tile image of kq_quantize_q8k_tiles, xs row-major.
- * k <= 2^23 - 256 (KQ_EINVAL above). */
+ * k <= 2^23 - 256 (KQ_EINVAL above).
+ * workspace: NULL, or a 256-byte aligned device buffer of workspace_bytes
+ * >= kq_gemm_workspace_bytes bytes (no initial contents needed).  With it, a
+ * grid too small to fill the GPU is split along k: each split writes its
+ * partial sums to the workspace and a second kernel adds them into y in
+ * split order, so results are the same from call to call (they may differ
+ * from the unsplit sum in the last bits, within the fold's float
+ * tolerance).  Calls sharing one workspace must be ordered on one stream.
+ * A NULL or too small workspace runs unsplit. */
 int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq_tiles, const float *xs,
-            const uint16_t *xbs_tiles, int64_t m, float *y, void *stream);
+            const uint16_t *xbs_tiles, int64_t m, float *y, void *workspace, size_t workspace_bytes,
+            void *stream);
 
 /* kq_gemv that also stores each superblock's int32 partials:
  * P[t][n][k/256] and M[t][n][k/256] (Q6_K: P = iacc - 32*bacc and M = 0;
@@ -145,7 +158,8 @@ int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
                      const float *xs, const int16_t *xbs, int64_t t, float *y, int32_t *P,
                      int32_t *M, void *stream);
 
-/* kq_gemm that also stores the int32 partials, as kq_gemv_partials. */
+/* kq_gemm (unsplit, no workspace) that also stores the int32 partials, as
+ * kq_gemv_partials. */
 int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq_tiles,
                      const float *xs, const uint16_t *xbs_tiles, int64_t m, float *y, int32_t *P,
                      int32_t *M, void *stream);

@@ -26,7 +26,8 @@ KQ_OK, KQ_EINVAL, KQ_EFORMAT, KQ_EALIGN, KQ_ELAUNCH = 0, -1, -2, -3, -4
 
 # every entry point of include/kq.h
 SYMBOLS = ("kq_record_bytes", "kq_packed_bytes", "kq_pack", "kq_unpack", "kq_quantize_q8k",
-           "kq_q8k_tiles_bytes", "kq_quantize_q8k_tiles", "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemv_partials", "kq_gemm_partials", "kq_strerror")
+           "kq_q8k_tiles_bytes", "kq_quantize_q8k_tiles", "kq_gemv", "kq_gemv_f32",
+           "kq_gemm_workspace_bytes", "kq_gemm", "kq_gemv_partials", "kq_gemm_partials", "kq_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python quant_matmul_amd/build.py`")
@@ -44,7 +45,9 @@ lib.kq_q8k_tiles_bytes.argtypes = [_i64, _i64]
 lib.kq_q8k_tiles_bytes.restype = ctypes.c_size_t
 lib.kq_quantize_q8k_tiles.argtypes = [_p, _i64, _i64, _p, _p, _p, _p]
 lib.kq_gemv.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
-lib.kq_gemm.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
+lib.kq_gemm_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
+lib.kq_gemm_workspace_bytes.restype = ctypes.c_size_t
+lib.kq_gemm.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, ctypes.c_size_t, _p]
 lib.kq_gemv_f32.argtypes = [_int, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
 lib.kq_gemv_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
 lib.kq_gemm_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
@@ -128,9 +131,16 @@ def kq_gemv_f32(fmt, w_planes, n: int, k: int, x, t: int, y, xq=None, xs=None, x
                         _ptr(xbs), _stream(stream)), "kq_gemv_f32")
 
 
-def kq_gemm(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, stream=None):
+def kq_gemm_workspace_bytes(fmt, n: int, k: int, m: int) -> int:
+    return lib.kq_gemm_workspace_bytes(_fmt(fmt), n, k, m)
+
+
+def kq_gemm(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, workspace=None, workspace_bytes=None,
+            stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _ok(lib.kq_gemm(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), m, _ptr(y),
-                    _stream(stream)), "kq_gemm")
+                    _ptr(workspace), workspace_bytes, _stream(stream)), "kq_gemm")
 
 
 def kq_gemv_partials(fmt, w_planes, n: int, k: int, xq, xs, xbs, t: int, y, P, M, stream=None):

@@ -16,7 +16,9 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
                 const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
                 const float *x = nullptr, int8_t *oq = nullptr, float *os = nullptr, int16_t *obs = nullptr);
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                const void *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st);
+                const void *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *ws, size_t ws_bytes,
+                hipStream_t st);
+size_t gemm_workspace_bytes(int64_t n, int64_t k, int64_t m);
 }  // namespace kq
 
 namespace {
@@ -145,13 +147,21 @@ int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
     return kq::launch_gemv(fmt, w_planes, n, k, xq, xs, xbs, t, y, P, M, (hipStream_t)stream);
 }
 
+size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m)
+{
+    if (!known(fmt) || check_nk(n, k) || m < 1 || m > INT_MAX || k > kq::GEMM_KMAX) return 0;
+    return kq::gemm_workspace_bytes(n, k, m);
+}
+
 int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-            const uint16_t *xbs, int64_t m, float *y, void *stream)
+            const uint16_t *xbs, int64_t m, float *y, void *workspace, size_t workspace_bytes, void *stream)
 {
     int rc = check_matmul(fmt, w_planes, n, k, xq, xs, (const int16_t *)xbs, m, INT_MAX, y, nullptr, nullptr,
                           false);
     if (rc) return rc;
-    return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, (hipStream_t)stream);
+    if (workspace && !aligned(workspace, 256)) return KQ_EALIGN;
+    return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, workspace, workspace_bytes,
+                           (hipStream_t)stream);
 }
 
 int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -159,7 +169,7 @@ int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
 {
     int rc = check_matmul(fmt, w_planes, n, k, xq, xs, (const int16_t *)xbs, m, INT_MAX, y, P, M, true);
     if (rc) return rc;
-    return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, (hipStream_t)stream);
+    return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, nullptr, 0, (hipStream_t)stream);
 }
 
 const char *kq_strerror(int code)

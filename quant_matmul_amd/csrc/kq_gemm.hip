@@ -205,16 +205,14 @@ __device__ inline void unpack_half(const Half<FMT> &rw, bool valid, int r, int h
     }
 }
 
-// Workgroup tile index -> (row panel, token block), grouping the token
-// blocks of one row panel on one XCD (workgroup b runs on XCD b % 8), so the
-// panel's packed planes are fetched into that XCD's L2 once.
-__device__ inline void tile_of(int b, int G, int mtiles, int &nt, int &mt)
+// Workgroup index -> work item, grouping consecutive items on one XCD
+// (workgroup b runs on XCD b % 8).  Items are ordered (row panel, token
+// block, K split), so the token blocks of one row panel share that XCD's
+// L2 copy of the panel's packed planes.
+__device__ inline int item_of(int b, int G)
 {
     const int per = G / 8;
-    int L = b;
-    if (b < per * 8) L = (b % 8) * per + b / 8;
-    nt = L / mtiles;
-    mt = L % mtiles;
+    return b < per * 8 ? (b % 8) * per + b / 8 : b;
 }
 
 }  // namespace
@@ -224,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                                                       const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                       const _Float16 *__restrict__ xbs, int64_t mtok,
                                                       float *__restrict__ y, int32_t *__restrict__ Pout,
-                                                      int32_t *__restrict__ Mout, int mtiles)
+                                                      int32_t *__restrict__ Mout, int mtiles, int S)
 {
     constexpr int BM = 256, BN = 32;
     static_assert(BN * 8 == 256, "one 32-weight unpack task per thread");
@@ -234,8 +232,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     __shared__ float dn[2][BN], dmn[2][BN];
     __shared__ __align__(16) float d8s[2][BM];
 
-    int nt, mt;
-    tile_of(blockIdx.x, gridDim.x, mtiles, nt, mt);
+    // item = (tile, K split); split j of S covers superblocks [s0, s1)
+    const int item = item_of(blockIdx.x, gridDim.x);
+    const int tile = item / S, split = item - tile * S;
+    const int nt = tile / mtiles, mt = tile - nt * mtiles;
+    const int s0 = (int)((int64_t)nsb * split / S), s1 = (int)((int64_t)nsb * (split + 1) / S);
     const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wm = tid >> 6;
@@ -297,16 +298,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     f32x16 accf[2];
     accf[0] = accf[1] = f32x16{};
 
-    load_w(0);
+    load_w(s0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) load_a(0, ks);
-    load_bs(0);
+    for (int ks = 0; ks < 8; ++ks) load_a(s0, ks);
+    load_bs(s0);
     unpack_w(0);
-    if (nsb > 1) load_w(1);
+    if (s0 + 1 < s1) load_w(s0 + 1);
     __syncthreads();
 
-    for (int s = 0; s < nsb; ++s) {
-        const int b = s & 1;
+    for (int s = s0; s < s1; ++s) {
+        const int b = (s - s0) & 1;
         i32x16 acc[2];
         acc[0] = acc[1] = i32x16{};
         // high-digit pass
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                 acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
         }
         // the unpack of the next superblock overlaps these MFMAs
-        if (s + 1 < nsb) unpack_w(b ^ 1);
+        if (s + 1 < s1) unpack_w(b ^ 1);
         acc[0] = acc[0] * 128;
         acc[1] = acc[1] * 128;
         // low-digit pass; each 32-deep K step of the codes is dead after it
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
                 acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
-            if (s + 1 < nsb) load_a(s + 1, ks);
+            if (s + 1 < s1) load_a(s + 1, ks);
         }
         // the one float fold of superblock s; lane l holds row n0 + l%32 and
         // tokens 8*(r/4) + 4*(l/32) + r%4 of each 32-token group, r = 0..15
@@ -362,11 +363,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                 }
             }
         }
-        if (s + 1 < nsb) load_bs(s + 1);
-        if (s + 2 < nsb) load_w(s + 2);
+        if (s + 1 < s1) load_bs(s + 1);
+        if (s + 2 < s1) load_w(s + 2);
         __syncthreads();  // panel s+1 complete; panel s free for s+2
     }
 
+    // K split j of S writes its partial sums to slice j of y (y then
+    // points at the workspace), reduced in split order by sum_splits
+    float *yo = y + (int64_t)split * mtok * n;
     const int64_t col = n0 + l32;
     if (col < n) {
 #pragma unroll
@@ -374,34 +378,88 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t t = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (t < mtok) y[t * n + col] = accf[mi][r];
+                if (t < mtok) yo[t * n + col] = accf[mi][r];
             }
     }
 }
 
+// y = ((p_0 + p_1) + p_2) + ... over the S partial slices, in split order,
+// one float per thread (y is only 4-byte aligned)
+__global__ __launch_bounds__(256) void sum_splits(const float *__restrict__ p, int S, int64_t count,
+                                                  float *__restrict__ y)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    float acc = p[i];
+    for (int j = 1; j < S; ++j) acc += p[(int64_t)j * count + i];
+    y[i] = acc;
+}
+
+// K splits for a grid of `tiles` workgroups: enough to give about two
+// workgroups per CU (the occupancy of this kernel), each split at least 3
+// superblocks deep, at most 8.  The splits' partial sums go to a workspace
+// and a second kernel adds them in split order: a deterministic sum, and no
+// cross-workgroup signalling (on MI355X a device-scope fence writes back and
+// invalidates the whole L2 of the XCD, which costs more than the pass).
+static int pick_splits(int64_t tiles, int nsb)
+{
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+    }
+    const int64_t slots = 2 * (int64_t)cus;
+    int S = (int)(slots / tiles);
+    S = S < nsb / 3 ? S : nsb / 3;
+    S = S < 8 ? S : 8;
+    return S > 1 ? S : 1;
+}
+
+static int64_t tiles_of(int64_t n, int64_t m) { return ((n + 31) / 32) * ((m + 255) / 256); }
+
+size_t gemm_workspace_bytes(int64_t n, int64_t k, int64_t m)
+{
+    const int S = pick_splits(tiles_of(n, m), (int)(k / QK));
+    return S == 1 ? 0 : (size_t)S * (size_t)m * (size_t)n * 4;
+}
+
 template <int FMT>
 static void launch_fmt(bool part, int64_t n, int nsb, const uint8_t *w, const int8_t *xq, const float *xs,
-                       const _Float16 *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
+                       const _Float16 *xbs, int64_t m, float *y, int32_t *P, int32_t *M, int S, hipStream_t st)
 {
     constexpr int BM = 256, BN = 32;
     const int64_t ntiles = (n + BN - 1) / BN, mtiles = (m + BM - 1) / BM;
-    const dim3 g((unsigned)(ntiles * mtiles)), b(256);
+    const dim3 g((unsigned)(ntiles * mtiles * S)), b(256);
     if (part)
-        hipLaunchKernelGGL((gemm_kernel<FMT, true>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles);
+        hipLaunchKernelGGL((gemm_kernel<FMT, true>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles,
+                           S);
     else
-        hipLaunchKernelGGL((gemm_kernel<FMT, false>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles);
+        hipLaunchKernelGGL((gemm_kernel<FMT, false>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles,
+                           S);
 }
 
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                const void *xbs, int64_t m, float *y, int32_t *P, int32_t *M, hipStream_t st)
+                const void *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *ws, size_t ws_bytes,
+                hipStream_t st)
 {
     const int nsb = (int)(k / QK);
     const uint8_t *wb = (const uint8_t *)w;
     const _Float16 *bt = (const _Float16 *)xbs;
     const bool part = P != nullptr;
-    if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, st);
-    else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, st);
-    else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, st);
+    // split K only with a workspace large enough (and never for the partials)
+    int S = 1;
+    if (!part && ws && ws_bytes >= gemm_workspace_bytes(n, k, m)) S = pick_splits(tiles_of(n, m), nsb);
+    float *dst = S > 1 ? (float *)ws : y;
+    if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
+    else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
+    else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
+    if (S > 1) {
+        const int64_t count = m * n;
+        hipLaunchKernelGGL(sum_splits, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, (const float *)ws, S,
+                           count, y);
+    }
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 

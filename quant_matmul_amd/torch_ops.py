@@ -8,7 +8,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (kq_gemm, kq_gemm_partials, kq_gemv, kq_gemv_f32, kq_gemv_partials, kq_pack,
+from . import (kq_gemm, kq_gemm_partials, kq_gemm_workspace_bytes, kq_gemv, kq_gemv_f32, kq_gemv_partials, kq_pack,
                kq_packed_bytes, kq_q8k_tiles_bytes, kq_quantize_q8k, kq_quantize_q8k_tiles,
                kq_record_bytes, kq_unpack)
 
@@ -78,12 +78,21 @@ def gemv_f32(fmt, planes, n: int, k: int, x: torch.Tensor, keep_image: bool = Fa
     return (y, q8) if keep_image else y
 
 
-def gemm(fmt, planes, n: int, k: int, q8t, stream=None) -> torch.Tensor:
-    """q8t: the GEMM's image (code tiles, xs, bsum tiles), as from quantize_q8k_tiles."""
+def gemm_workspace(fmt, n: int, k: int, m: int, device="cuda"):
+    """A kq_gemm workspace for this shape (None if it takes none)."""
+    nb = kq_gemm_workspace_bytes(fmt, n, k, m)
+    return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+
+
+def gemm(fmt, planes, n: int, k: int, q8t, workspace="auto", stream=None) -> torch.Tensor:
+    """q8t: the GEMM's image (code tiles, xs, bsum tiles), as from
+    quantize_q8k_tiles.  workspace: "auto" allocates one, None runs unsplit."""
     xq, xs, xbs = q8t
     m = xs.shape[0]
+    if isinstance(workspace, str):
+        workspace = gemm_workspace(fmt, n, k, m, xq.device)
     y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
-    kq_gemm(fmt, planes, n, k, xq, xs, xbs, m, y, stream)
+    kq_gemm(fmt, planes, n, k, xq, xs, xbs, m, y, workspace, stream=stream)
     return y
 
 

@@ -65,22 +65,37 @@ def test_gemv_argument_checks():
         assert _gemv(**{name: ODD}) == kq.KQ_EALIGN, name
 
 
+def _gemm(fmt=4, w=GOOD16, n=16, k=256, xq=GOOD16, xs=GOOD16, xbs=GOOD16, m=4, y=GOOD16, ws=None, wsb=0):
+    return kq.lib.kq_gemm(fmt, w, n, k, xq, xs, xbs, m, y, ws, wsb, None)
+
+
 def test_gemm_argument_checks():
-    f = kq.lib.kq_gemm
-    assert f(8, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EFORMAT
-    assert f(4, GOOD16, 16, 512 + 16, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EINVAL
-    assert f(4, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 0, GOOD16, None) == kq.KQ_EINVAL
-    assert f(4, GOOD16, 16, 256, None, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EINVAL
-    assert f(4, GOOD16 + 8, 16, 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EALIGN
+    assert _gemm(fmt=8) == kq.KQ_EFORMAT
+    assert _gemm(k=512 + 16) == kq.KQ_EINVAL
+    assert _gemm(m=0) == kq.KQ_EINVAL
+    assert _gemm(xq=None) == kq.KQ_EINVAL
+    assert _gemm(w=GOOD16 + 8) == kq.KQ_EALIGN
+    # the workspace is optional, and 256-byte aligned when given
+    assert _gemm(ws=GOOD16 + 16, wsb=1 << 20, y=ODD) == kq.KQ_EALIGN
+    assert _gemm(ws=GOOD16 + 16, wsb=1 << 20) == kq.KQ_EALIGN
+
+
+def test_gemm_workspace_bytes():
+    # W_down at pp512 (160 tiles of 256 x 32) splits k; W_up (608 tiles) does not
+    assert kq.kq_gemm_workspace_bytes("q6_k", 2560, 9728, 512) > 0
+    assert kq.kq_gemm_workspace_bytes("q4_k", 9728, 2560, 512) == 0
+    # S = 3 partial slices of the m x n output
+    assert kq.kq_gemm_workspace_bytes("q4_k", 300, 2560, 130) == 3 * 130 * 300 * 4
+    assert kq.kq_gemm_workspace_bytes("q4_k", 300, 300, 130) == 0
+    assert kq.kq_gemm_workspace_bytes(9, 300, 2560, 130) == 0
 
 
 def test_gemm_k_bound():
-    f = kq.lib.kq_gemm
     kmax = (1 << 23) - 256
-    assert f(4, GOOD16, 16, kmax + 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EINVAL
+    assert _gemm(k=kmax + 256) == kq.KQ_EINVAL
     # the bound is the GEMM's: the GEMV takes the same k (fails later, on alignment)
     assert kq.lib.kq_gemv(4, GOOD16, 16, kmax + 256, GOOD16, GOOD16, GOOD16, 1, ODD, None) == kq.KQ_EALIGN
-    assert f(4, GOOD16, 16, kmax, GOOD16, GOOD16, GOOD16, 4, ODD, None) == kq.KQ_EALIGN
+    assert _gemm(k=kmax, y=ODD) == kq.KQ_EALIGN
 
 
 def test_tile_image_bytes_and_checks():

@@ -22,12 +22,15 @@ def test_graph_replays_match_eager(fmt):
     q1, qm = ops.q8k_buffers(t, k), ops.q8k_tile_buffers(m, k)
     y1 = torch.empty((t, n), device="cuda")
     ym = torch.empty((m, n), device="cuda")
+    # a grid this small splits k (GEMM + split-sum kernels in the graph)
+    ws = ops.gemm_workspace(fmt, n, k, m)
+    assert ws is not None
 
     def seq():
         kq.kq_quantize_q8k(x1, t, k, *q1)
         kq.kq_gemv(fmt, planes, n, k, *q1, t, y1)
         kq.kq_quantize_q8k_tiles(xm, m, k, *qm)
-        kq.kq_gemm(fmt, planes, n, k, *qm, m, ym)
+        kq.kq_gemm(fmt, planes, n, k, *qm, m, ym, ws)
 
     seq()
     torch.cuda.synchronize()

@@ -66,6 +66,14 @@ def check(case, y, P, M, rows=None):
     assert not bad.any(), f"{bad.sum()} outputs beyond tolerance, worst ratio {np.max(err / R):.3g}"
 
 
+def check_y(case, y, rows=None):
+    y_o, _, _, R = case.oracle_rows(rows)
+    y = host(y) if rows is None else host(y)[:, rows]
+    assert np.all(np.isfinite(y))
+    err = np.abs(y.astype(np.float64) - y_o)
+    assert np.all(err <= TOL * R), f"worst ratio {np.max(err / R):.3g}"
+
+
 # ------------------------------------------------------------ Q8_K ------
 @pytest.mark.parametrize("t,k", [(1, 256), (3, 2560), (8, 9728), (512, 2560), (129, 768)])
 def test_quantize_bit_exact(t, k):
@@ -168,8 +176,11 @@ def test_gemm_parity(fmt, m, n, k):
     c = Case(fmt, n, k, m, seed=m + n)
     y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
     check(c, y, P, M)
-    y2 = ops.gemm(fmt, c.planes, n, k, c.q8t)
+    # the production entry point, unsplit: the same body without the stores
+    y2 = ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=None)
     assert torch.equal(y, y2)
+    # with a workspace a grid this small is split along k: same tolerance
+    check_y(c, ops.gemm(fmt, c.planes, n, k, c.q8t))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -210,11 +221,11 @@ def test_gemm_pp512_full_size_sampled(fmt, n, k):
     c = Case(fmt, n, k, m, seed=4, x=x)
     for a, b in zip(q8, c.q8t):
         assert torch.equal(a, b)
-    y = ops.gemm(fmt, c.planes, n, k, q8)
+    y = ops.gemm(fmt, c.planes, n, k, q8)  # with a workspace: W_down splits k
     rows = sample_rows(n)[:24]
-    y_o, _, _, R = c.oracle_rows(rows)
-    err = np.abs(host(y)[:, rows].astype(np.float64) - y_o)
-    assert np.all(err <= TOL * R)
+    check_y(c, y, rows)
+    y1 = ops.gemm(fmt, c.planes, n, k, q8, workspace=None)
+    check_y(c, y1, rows)
 
 
 # ------------------------------------------ poison, guards, determinism --
@@ -242,6 +253,11 @@ def test_repeat_runs_are_bitwise_identical(kind):
     n, k = 2560, 9728
     t = 4 if kind == "gemv" else 256
     c = Case("q6_k", n, k, t, seed=12)
-    f, q8 = (ops.gemv, c.q8) if kind == "gemv" else (ops.gemm, c.q8t)
-    ys = [f("q6_k", c.planes, n, k, q8) for _ in range(3)]
+    if kind == "gemv":
+        ys = [ops.gemv("q6_k", c.planes, n, k, c.q8) for _ in range(3)]
+    else:
+        # one workspace reused: the split sums come out the same every call
+        ws = ops.gemm_workspace("q6_k", n, k, t)
+        assert ws is not None
+        ys = [ops.gemm("q6_k", c.planes, n, k, c.q8t, workspace=ws) for _ in range(3)]
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
