@@ -114,6 +114,18 @@ size_t kq_q8k_tiles_bytes(int64_t t, int64_t k);
 int kq_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq_tiles, float *xs, uint16_t *xbs_tiles,
                           void *stream);
 
+/* kq_quantize_q8k_tiles of gathered rows, for the grouped GEMM: image row
+ * i (0 <= i < m) is the Q8_K of activation row rows[i] of x[t][k]; an index
+ * outside [0, t) gives a zero row (codes 0, bsums 0, d8 = 0).  rows is a
+ * device int32[m]; xs has m rows; the tile buffers hold m rounded up to 32
+ * rows (kq_q8k_tiles_bytes(m, k)).  A mixture-of-experts layer lists the
+ * tokens routed to each expert one expert after another, each expert's
+ * list padded with -1 to a multiple of 32 rows (K-quant kernel arc page,
+ * "The pieces", kq v2 item: the MoE path fills one Q8_K image for gate and
+ * up). */
+int kq_quantize_q8k_tiles_gather(const float *x, int64_t t, int64_t k, const int32_t *rows, int64_t m,
+                                 int8_t *xq_tiles, float *xs, uint16_t *xbs_tiles, void *stream);
+
 /* Decode GEMV, batch t in 1..8: y[t][n] = W . a_t by the folds above,
  * streaming the packed planes once. */
 int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -138,7 +150,9 @@ size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
 
 /* Prefill GEMM, m >= 1 tokens: y[m][n], the folds of kq_gemv.  The codes
  * and bsums are the tile image of kq_quantize_q8k_tiles, xs row-major.
- * k <= 2^23 - 256 (KQ_EINVAL above).
+ * k <= 2^23 - 256 (KQ_EINVAL above).  m <= 127 runs a 32-token tile that
+ * unpacks each weight once per 32 tokens in registers, m >= 128 a
+ * 256-token tile that unpacks it once per 256 tokens into LDS.
  * workspace: NULL, or a 256-byte aligned device buffer of workspace_bytes
  * >= kq_gemm_workspace_bytes bytes (no initial contents needed).  With it, a
  * grid too small to fill the GPU is split along k: each split writes its
@@ -157,6 +171,19 @@ int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
 int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq,
                      const float *xs, const int16_t *xbs, int64_t t, float *y, int32_t *P,
                      int32_t *M, void *stream);
+
+/* Grouped GEMM of a mixture-of-experts layer, all experts in one launch:
+ * `experts` weight matrices of n x k in one format, expert e's planes at
+ * w_planes + e * w_stride bytes (w_stride >= kq_packed_bytes(fmt, n, k), a
+ * multiple of 16); a tile image of m rows (kq_quantize_q8k_tiles_gather)
+ * whose 32-row tile i belongs to expert tile_expert[i] (device
+ * int32[ceil(m/32)]).  y[m][n]: row i is row i of the image times that
+ * expert's matrix.  A tile whose expert id is outside [0, experts) is left
+ * unwritten.  Unsplit; each tile runs the kq_gemm 32-token tile body, so a
+ * tile's outputs equal kq_gemm's on the same rows bit for bit. */
+int kq_gemm_grouped(int fmt, const void *w_planes, int64_t w_stride, int64_t experts, const int32_t *tile_expert,
+                    int64_t n, int64_t k, const int8_t *xq_tiles, const float *xs, const uint16_t *xbs_tiles,
+                    int64_t m, float *y, void *stream);
 
 /* kq_gemm (unsplit, no workspace) that also stores the int32 partials, as
  * kq_gemv_partials. */

@@ -26,8 +26,9 @@ KQ_OK, KQ_EINVAL, KQ_EFORMAT, KQ_EALIGN, KQ_ELAUNCH = 0, -1, -2, -3, -4
 
 # every entry point of include/kq.h
 SYMBOLS = ("kq_record_bytes", "kq_packed_bytes", "kq_pack", "kq_unpack", "kq_quantize_q8k",
-           "kq_q8k_tiles_bytes", "kq_quantize_q8k_tiles", "kq_gemv", "kq_gemv_f32",
-           "kq_gemm_workspace_bytes", "kq_gemm", "kq_gemv_partials", "kq_gemm_partials", "kq_strerror")
+           "kq_q8k_tiles_bytes", "kq_quantize_q8k_tiles", "kq_quantize_q8k_tiles_gather", "kq_gemv",
+           "kq_gemv_f32", "kq_gemm_workspace_bytes", "kq_gemm", "kq_gemm_grouped", "kq_gemv_partials",
+           "kq_gemm_partials", "kq_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python quant_matmul_amd/build.py`")
@@ -44,6 +45,8 @@ lib.kq_quantize_q8k.argtypes = [_p, _i64, _i64, _p, _p, _p, _p]
 lib.kq_q8k_tiles_bytes.argtypes = [_i64, _i64]
 lib.kq_q8k_tiles_bytes.restype = ctypes.c_size_t
 lib.kq_quantize_q8k_tiles.argtypes = [_p, _i64, _i64, _p, _p, _p, _p]
+lib.kq_quantize_q8k_tiles_gather.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p, _p, _p]
+lib.kq_gemm_grouped.argtypes = [_int, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
 lib.kq_gemv.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
 lib.kq_gemm_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
 lib.kq_gemm_workspace_bytes.restype = ctypes.c_size_t
@@ -53,7 +56,8 @@ lib.kq_gemv_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p,
 lib.kq_gemm_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
 lib.kq_strerror.argtypes = [_int]
 lib.kq_strerror.restype = ctypes.c_char_p
-for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_quantize_q8k_tiles", "kq_gemv", "kq_gemv_f32", "kq_gemm",
+for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_quantize_q8k_tiles", "kq_quantize_q8k_tiles_gather",
+           "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemm_grouped",
            "kq_gemv_partials", "kq_gemm_partials"):
     getattr(lib, _f).restype = _int
 
@@ -121,6 +125,11 @@ def kq_quantize_q8k_tiles(x, t: int, k: int, xq_tiles, xs, xbs, stream=None):
         "kq_quantize_q8k_tiles")
 
 
+def kq_quantize_q8k_tiles_gather(x, t: int, k: int, rows, m: int, xq_tiles, xs, xbs, stream=None):
+    _ok(lib.kq_quantize_q8k_tiles_gather(_ptr(x), t, k, _ptr(rows), m, _ptr(xq_tiles), _ptr(xs), _ptr(xbs),
+                                         _stream(stream)), "kq_quantize_q8k_tiles_gather")
+
+
 def kq_gemv(fmt, w_planes, n: int, k: int, xq, xs, xbs, t: int, y, stream=None):
     _ok(lib.kq_gemv(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), t, _ptr(y),
                     _stream(stream)), "kq_gemv")
@@ -141,6 +150,12 @@ def kq_gemm(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, workspa
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _ok(lib.kq_gemm(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), m, _ptr(y),
                     _ptr(workspace), workspace_bytes, _stream(stream)), "kq_gemm")
+
+
+def kq_gemm_grouped(fmt, w_planes, w_stride: int, experts: int, tile_expert, n: int, k: int, xq_tiles, xs, xbs,
+                    m: int, y, stream=None):
+    _ok(lib.kq_gemm_grouped(_fmt(fmt), _ptr(w_planes), w_stride, experts, _ptr(tile_expert), n, k, _ptr(xq_tiles),
+                            _ptr(xs), _ptr(xbs), m, _ptr(y), _stream(stream)), "kq_gemm_grouped")
 
 
 def kq_gemv_partials(fmt, w_planes, n: int, k: int, xq, xs, xbs, t: int, y, P, M, stream=None):

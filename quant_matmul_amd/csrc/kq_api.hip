@@ -10,6 +10,17 @@ int launch_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float 
                         hipStream_t stream);
 int launch_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
                               hipStream_t stream);
+int launch_quantize_q8k_tiles_gather(const float *x, int64_t t, const int32_t *src, int64_t m, int64_t k,
+                                     int8_t *xq, float *xs, int16_t *xbs, hipStream_t stream);
+int launch_gemm_mid(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                    const void *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *ws, size_t ws_bytes,
+                    hipStream_t st);
+size_t gemm_mid_workspace_bytes(int64_t n, int64_t k, int64_t m);
+int launch_gemm_grouped(int fmt, const void *w, int64_t w_stride, int64_t experts, const int32_t *tile_expert,
+                        int64_t n, int64_t k, const int8_t *xq, const float *xs, const void *xbs, int64_t m,
+                        float *y, int32_t *P, int32_t *M, hipStream_t st);
+// token counts below this run the mid-size tile, the rest the prefill tile
+constexpr int64_t GEMM_MID_MAX = 127;
 int launch_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, hipStream_t stream);
 int launch_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, hipStream_t stream);
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -113,6 +124,17 @@ int kq_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq_tiles
     return kq::launch_quantize_q8k_tiles(x, t, k, xq_tiles, xs, (int16_t *)xbs_tiles, (hipStream_t)stream);
 }
 
+int kq_quantize_q8k_tiles_gather(const float *x, int64_t t, int64_t k, const int32_t *rows, int64_t m,
+                                 int8_t *xq_tiles, float *xs, uint16_t *xbs_tiles, void *stream)
+{
+    int rc = check_quantize(x, t, k, xq_tiles, xs, (const int16_t *)xbs_tiles);
+    if (rc) return rc;
+    if (!rows || m < 1 || m > INT_MAX || (m + 31) * (k / kq::QK) > ((int64_t)1 << 32)) return KQ_EINVAL;
+    if (!aligned(rows, 4)) return KQ_EALIGN;
+    return kq::launch_quantize_q8k_tiles_gather(x, t, rows, m, k, xq_tiles, xs, (int16_t *)xbs_tiles,
+                                                (hipStream_t)stream);
+}
+
 int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
             const int16_t *xbs, int64_t t, float *y, void *stream)
 {
@@ -150,7 +172,7 @@ int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
 size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m)
 {
     if (!known(fmt) || check_nk(n, k) || m < 1 || m > INT_MAX || k > kq::GEMM_KMAX) return 0;
-    return kq::gemm_workspace_bytes(n, k, m);
+    return m <= kq::GEMM_MID_MAX ? kq::gemm_mid_workspace_bytes(n, k, m) : kq::gemm_workspace_bytes(n, k, m);
 }
 
 int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -160,8 +182,25 @@ int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
                           false);
     if (rc) return rc;
     if (workspace && !aligned(workspace, 256)) return KQ_EALIGN;
+    if (m <= kq::GEMM_MID_MAX)
+        return kq::launch_gemm_mid(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, workspace,
+                                   workspace_bytes, (hipStream_t)stream);
     return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, workspace, workspace_bytes,
                            (hipStream_t)stream);
+}
+
+int kq_gemm_grouped(int fmt, const void *w_planes, int64_t w_stride, int64_t experts, const int32_t *tile_expert,
+                    int64_t n, int64_t k, const int8_t *xq_tiles, const float *xs, const uint16_t *xbs_tiles,
+                    int64_t m, float *y, void *stream)
+{
+    int rc = check_matmul(fmt, w_planes, n, k, xq_tiles, xs, (const int16_t *)xbs_tiles, m, INT_MAX, y, nullptr,
+                          nullptr, false);
+    if (rc) return rc;
+    if (!tile_expert || experts < 1 || experts > INT_MAX) return KQ_EINVAL;
+    if (w_stride < (int64_t)kq::planes_of(fmt, n, k / kq::QK).total) return KQ_EINVAL;
+    if (w_stride % 16 || !aligned(tile_expert, 4)) return KQ_EALIGN;
+    return kq::launch_gemm_grouped(fmt, w_planes, w_stride, experts, tile_expert, n, k, xq_tiles, xs, xbs_tiles, m, y,
+                                   nullptr, nullptr, (hipStream_t)stream);
 }
 
 int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -169,6 +208,8 @@ int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
 {
     int rc = check_matmul(fmt, w_planes, n, k, xq, xs, (const int16_t *)xbs, m, INT_MAX, y, P, M, true);
     if (rc) return rc;
+    if (m <= kq::GEMM_MID_MAX)
+        return kq::launch_gemm_mid(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, nullptr, 0, (hipStream_t)stream);
     return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, nullptr, 0, (hipStream_t)stream);
 }
 

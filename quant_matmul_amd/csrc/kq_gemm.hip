@@ -40,6 +40,7 @@
 // step of the codes is refilled with superblock s+1 as soon as its
 // low-digit MFMAs are issued.  One barrier per superblock.
 #include "kq_common.h"
+#include "kq_digits.h"
 
 namespace kq {
 
@@ -51,47 +52,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int LDS_STRIDE = 272;  // bytes per digit row: 256 + 16 pad
 
 namespace {
-
-// byte selectors of v_perm_b32 (bytes 0..3 = second operand, 4..7 = first)
-constexpr uint32_t SEL_EVEN = 0x0C020C00u;    // bytes 0, 2 -> 16-bit lanes
-constexpr uint32_t SEL_ODD = 0x0C030C01u;     // bytes 1, 3 -> 16-bit lanes
-constexpr uint32_t SEL_INTERLEAVE = 0x06020400u;  // low bytes of (e, o) lanes -> e0 o0 e1 o1
-
-// Digits of four 16-bit lane values (e = v0 | v2 << 16, o = v1 | v3 << 16,
-// each in [0, 16383]): low digits (bits 0..6) and high digits (bits 7..13)
-// packed as bytes v0 v1 v2 v3.  (e >> 7) keeps each lane's bits 7..14 in
-// that lane's low byte: the upper lane's bits move to bit 9 and up.
-__device__ inline void split_digits(uint32_t e, uint32_t o, uint32_t &hi, uint32_t &lo)
-{
-    lo = __builtin_amdgcn_perm(o, e, SEL_INTERLEAVE) & 0x7F7F7F7Fu;
-    hi = __builtin_amdgcn_perm(o >> 7, e >> 7, SEL_INTERLEAVE);
-}
-
-// Four unsigned quants (one per byte of q, each <= 31) times scale sc
-// (0..63): the digits of sc*q.
-__device__ inline void digits_q45(uint32_t q, int sc, uint32_t &hi, uint32_t &lo)
-{
-    // each 16-bit lane <= 31*63, and both factors fit 24 bits
-    const uint32_t e = (uint32_t)__umul24(__builtin_amdgcn_perm(0u, q, SEL_EVEN), (uint32_t)sc);
-    const uint32_t o = (uint32_t)__umul24(__builtin_amdgcn_perm(0u, q, SEL_ODD), (uint32_t)sc);
-    split_digits(e, o, hi, lo);
-}
-
-// Four Q6_K quants (bytes 0..63) with signed scale sc: the digits of
-// w' = sc*(q-32).  Each 16-bit lane is formed as w' + 4096 in [32, 8192]
-// (q*sc + 4096 - 32*sc); the integer sum of the two lanes is exact, so the
-// lanes never borrow.  The low digit of w' + 4096 is that of w' (4096 is a
-// multiple of 128), the high digit is 32 too large: it is taken back per
-// byte with a borrow-free byte subtraction, leaving a signed byte.
-__device__ inline void digits_q6(uint32_t q, int sc, uint32_t &hi, uint32_t &lo)
-{
-    const int bias = (4096 - 32 * sc) * 0x00010001;
-    const uint32_t e = (uint32_t)(__mul24((int)__builtin_amdgcn_perm(0u, q, SEL_EVEN), sc) + bias);
-    const uint32_t o = (uint32_t)(__mul24((int)__builtin_amdgcn_perm(0u, q, SEL_ODD), sc) + bias);
-    uint32_t hu;
-    split_digits(e, o, hu, lo);
-    hi = ((hu | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
-}
 
 // Half share: 32 weights of a superblock row, one unpack task.  Task
 // h = 2c + half of a Q4_K/Q5_K row covers quant bytes 32c + 16*half .. +15:
@@ -395,6 +355,11 @@ __global__ __launch_bounds__(256) void sum_splits(const float *__restrict__ p, i
     y[i] = acc;
 }
 
+void launch_sum_splits(const float *p, int S, int64_t count, float *y, hipStream_t st)
+{
+    hipLaunchKernelGGL(sum_splits, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, p, S, count, y);
+}
+
 // K splits for a grid of `tiles` workgroups: enough to give about two
 // workgroups per CU (the occupancy of this kernel), each split at least 3
 // superblocks deep, at most 8.  The splits' partial sums go to a workspace
@@ -455,11 +420,7 @@ int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
     if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
     else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
     else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
-    if (S > 1) {
-        const int64_t count = m * n;
-        hipLaunchKernelGGL(sum_splits, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, (const float *)ws, S,
-                           count, y);
-    }
+    if (S > 1) launch_sum_splits((const float *)ws, S, m * n, y, st);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 

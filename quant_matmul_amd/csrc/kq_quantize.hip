@@ -23,13 +23,19 @@
 // One operand is then one coalesced 1 KiB load with no conversion, where
 // row-major codes spread it over 32 partly used cache lines.  Tokens past t
 // up to the next multiple of 32 get zero codes and zero bsums.
+//
+// The gather form fills the tile image of a mixture-of-experts layer: image
+// row i is the Q8_K of activation row src[i] (the tokens routed to each
+// expert, each expert's rows padded to whole tiles), and an index outside
+// the activation rows gives a zero row.
 #include "kq_common.h"
 
 namespace kq {
 
-template <bool TILES>
-__global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restrict__ x, int64_t rows, int64_t t,
-                                                           int nsb, int8_t *__restrict__ xq,
+template <bool TILES, bool GATHER>
+__global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restrict__ x, int64_t t,
+                                                           const int32_t *__restrict__ src, int64_t m,
+                                                           int64_t rows, int nsb, int8_t *__restrict__ xq,
                                                            float *__restrict__ xs, int16_t *__restrict__ xbs)
 {
     const int lane = threadIdx.x & 63;
@@ -37,9 +43,15 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restri
     if (chunk >= rows * nsb) return;  // whole wave exits together
     const int64_t row = chunk / nsb;
     const int sb = (int)(chunk - row * nsb);
-    const bool real = row < t;  // uniform over the wave
+    // image row `row` (< m: a real row, else tile padding) quantises source
+    // row srow of x; a gather index outside [0, t) gives a zero row
+    const bool real = row < m;  // uniform over the wave
+    int64_t srow = row;
+    if constexpr (GATHER) srow = real ? (int64_t)src[row] : -1;
+    const bool data = real && srow >= 0 && srow < t;
 
-    const float4 v = real ? reinterpret_cast<const float4 *>(x + chunk * QK)[lane] : make_float4(0, 0, 0, 0);
+    const float4 v = data ? reinterpret_cast<const float4 *>(x + (srow * nsb + sb) * QK)[lane]
+                          : make_float4(0, 0, 0, 0);
     int qsum;
     float d8;
     const uint32_t packed = q8k_chunk(v, qsum, d8);
@@ -66,32 +78,35 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restri
     }
 }
 
-static int launch(bool tiles, const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
-                  hipStream_t stream)
+template <bool TILES, bool GATHER>
+static int launch(const float *x, int64_t t, const int32_t *src, int64_t m, int64_t k, int8_t *xq, float *xs,
+                  int16_t *xbs, hipStream_t stream)
 {
     const int nsb = (int)(k / QK);
-    const int64_t rows = tiles ? (t + 31) / 32 * 32 : t;
+    const int64_t rows = TILES ? (m + 31) / 32 * 32 : m;
     const int per_block = 4;  // waves (chunks) per 256-thread workgroup
     const int64_t blocks = (rows * nsb + per_block - 1) / per_block;
-    if (tiles)
-        hipLaunchKernelGGL(quantize_q8k_kernel<true>, dim3((unsigned)blocks), dim3(64 * per_block), 0, stream, x,
-                           rows, t, nsb, xq, xs, xbs);
-    else
-        hipLaunchKernelGGL(quantize_q8k_kernel<false>, dim3((unsigned)blocks), dim3(64 * per_block), 0, stream, x,
-                           rows, t, nsb, xq, xs, xbs);
+    hipLaunchKernelGGL((quantize_q8k_kernel<TILES, GATHER>), dim3((unsigned)blocks), dim3(64 * per_block), 0, stream,
+                       x, t, src, m, rows, nsb, xq, xs, xbs);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 
 int launch_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
                         hipStream_t stream)
 {
-    return launch(false, x, t, k, xq, xs, xbs, stream);
+    return launch<false, false>(x, t, nullptr, t, k, xq, xs, xbs, stream);
 }
 
 int launch_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
                               hipStream_t stream)
 {
-    return launch(true, x, t, k, xq, xs, xbs, stream);
+    return launch<true, false>(x, t, nullptr, t, k, xq, xs, xbs, stream);
+}
+
+int launch_quantize_q8k_tiles_gather(const float *x, int64_t t, const int32_t *src, int64_t m, int64_t k,
+                                     int8_t *xq, float *xs, int16_t *xbs, hipStream_t stream)
+{
+    return launch<true, true>(x, t, src, m, k, xq, xs, xbs, stream);
 }
 
 }  // namespace kq

@@ -8,8 +8,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (kq_gemm, kq_gemm_partials, kq_gemm_workspace_bytes, kq_gemv, kq_gemv_f32, kq_gemv_partials, kq_pack,
+from . import (kq_gemm, kq_gemm_grouped, kq_gemm_partials, kq_gemm_workspace_bytes, kq_gemv, kq_gemv_f32, kq_gemv_partials, kq_pack,
                kq_packed_bytes, kq_q8k_tiles_bytes, kq_quantize_q8k, kq_quantize_q8k_tiles,
+               kq_quantize_q8k_tiles_gather,
                kq_record_bytes, kq_unpack)
 
 QK = 256
@@ -59,6 +60,35 @@ def quantize_q8k_tiles(x: torch.Tensor, stream=None):
     xq, xs, xbs = q8k_tile_buffers(t, k, x.device)
     kq_quantize_q8k_tiles(x, t, k, xq, xs, xbs, stream)
     return xq, xs, xbs
+
+
+def quantize_q8k_tiles_gather(x: torch.Tensor, rows: torch.Tensor, stream=None):
+    """Tile image of the gathered rows x[rows[i]] (an index outside x's rows
+    gives a zero row), as kq_quantize_q8k_tiles_gather."""
+    t, k = x.shape
+    m = rows.shape[0]
+    xq, xs, xbs = q8k_tile_buffers(m, k, x.device)
+    kq_quantize_q8k_tiles_gather(x, t, k, rows, m, xq, xs, xbs, stream)
+    return xq, xs, xbs
+
+
+def pack_experts(fmt, recs_list, n: int, k: int, device="cuda"):
+    """Pack several n x k matrices into one buffer; returns (planes, stride)."""
+    stride = kq_packed_bytes(fmt, n, k)
+    buf = torch.empty(stride * len(recs_list), dtype=torch.uint8, device=device)
+    for e, recs in enumerate(recs_list):
+        kq_pack(fmt, upload_records(recs, device), n, k, buf[e * stride:(e + 1) * stride])
+    return buf, stride
+
+
+def gemm_grouped(fmt, planes, stride: int, experts: int, tile_expert: torch.Tensor, n: int, k: int, q8t,
+                 y=None, stream=None) -> torch.Tensor:
+    xq, xs, xbs = q8t
+    m = xs.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    kq_gemm_grouped(fmt, planes, stride, experts, tile_expert, n, k, xq, xs, xbs, m, y, stream)
+    return y
 
 
 def gemv(fmt, planes, n: int, k: int, q8, stream=None) -> torch.Tensor:

@@ -14,7 +14,8 @@ page):
   fields d (and dmin for Q4_K/Q5_K), which are |N(0, sigma=1e-3)| drawn in
   float64, rounded to float32 and then to float16 (round to nearest even);
 * activations: float32 N(0, 1);
-* the router for the MoE shape: float32 U(0, 1) logits.
+* the router for the MoE shape: float32 U(0, 1) logits, and the routing
+  tables (top-k experts per token, ties to the lower id) built from them.
 
 The bit generator is numpy's PCG64 with the given integer seed.
 """
@@ -68,3 +69,28 @@ def router_logits(tokens: int, experts: int, seed: int) -> np.ndarray:
     """float32 U(0, 1) router logits of shape (tokens, experts)."""
     return _rng(seed).random(size=(tokens, experts), dtype=np.float32)
 
+
+
+def moe_routes(logits: np.ndarray, top: int, tile: int = 32):
+    """Routing tables of a mixture-of-experts layer from router logits.
+
+    Each token goes to its `top` experts of highest logit (ties to the lower
+    expert id).  Returns (rows, tile_expert, starts, counts): `rows` lists,
+    expert after expert, the tokens routed to it in token order, each
+    expert's list padded with -1 to a multiple of `tile`; `tile_expert[i]`
+    is the expert of rows[i*tile:(i+1)*tile]; `starts[e]` / `counts[e]` are
+    the first row and the number of real rows of expert e.
+    """
+    tokens, experts = logits.shape
+    # a stable sort of the negated logits keeps the lower id first among ties
+    chosen = np.argsort(-logits, axis=1, kind="stable")[:, :top]
+    rows, tile_expert, starts, counts = [], [], [], []
+    for e in range(experts):
+        toks = np.nonzero((chosen == e).any(axis=1))[0]
+        starts.append(len(rows))
+        counts.append(len(toks))
+        padded = -(-len(toks) // tile) * tile
+        rows.extend(toks.tolist() + [-1] * (padded - len(toks)))
+        tile_expert.extend([e] * (padded // tile))
+    return (np.asarray(rows, dtype=np.int32), np.asarray(tile_expert, dtype=np.int32),
+            np.asarray(starts, dtype=np.int64), np.asarray(counts, dtype=np.int64))

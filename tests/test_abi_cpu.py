@@ -113,6 +113,26 @@ def test_tile_image_bytes_and_checks():
     assert q(GOOD16, (1 << 31) - 1, 1 << 16, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
 
 
+def test_gather_and_grouped_argument_checks():
+    g = kq.lib.kq_quantize_q8k_tiles_gather
+    assert g(GOOD16, 4, 256, None, 32, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert g(GOOD16, 4, 256, GOOD16, 0, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert g(GOOD16, 4, 300, GOOD16, 32, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EINVAL
+    assert g(GOOD16, 4, 256, GOOD16 + 2, 32, GOOD16, GOOD16, GOOD16, None) == kq.KQ_EALIGN
+    f = kq.lib.kq_gemm_grouped
+    stride = kq.kq_packed_bytes(4, 96, 512)
+
+    def call(fmt=4, stride=stride, experts=4, te=GOOD16, n=96, k=512, m=64):
+        return f(fmt, GOOD16, stride, experts, te, n, k, GOOD16, GOOD16, GOOD16, m, GOOD16, None)
+    assert call(fmt=2) == kq.KQ_EFORMAT
+    assert call(te=None) == kq.KQ_EINVAL
+    assert call(experts=0) == kq.KQ_EINVAL
+    assert call(stride=stride - 256) == kq.KQ_EINVAL  # smaller than one expert's planes
+    assert call(stride=stride + 8) == kq.KQ_EALIGN
+    assert call(te=GOOD16 + 2) == kq.KQ_EALIGN
+    assert call(m=0) == kq.KQ_EINVAL
+
+
 def test_partials_argument_checks():
     for f in (kq.lib.kq_gemv_partials, kq.lib.kq_gemm_partials):
         # P missing

@@ -171,7 +171,10 @@ def test_gemv_f32_fused_matches_two_step(fmt, t, n, k):
 # ------------------------------------------------------------ GEMM ------
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,n,k", [(128, 256, 2560), (129, 100, 768), (1, 64, 256), (300, 65, 512),
-                                   (256, 300, 1024)])
+                                   (256, 300, 1024),
+                                   # the 32-token tile (m <= 127): ragged tokens and rows
+                                   (9, 256, 2560), (32, 128, 512), (33, 300, 768), (100, 129, 1024),
+                                   (127, 40, 256)])
 def test_gemm_parity(fmt, m, n, k):
     c = Case(fmt, n, k, m, seed=m + n)
     y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
@@ -228,11 +231,21 @@ def test_gemm_pp512_full_size_sampled(fmt, n, k):
     check_y(c, y1, rows)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
+@pytest.mark.parametrize("m", [16, 96])
+def test_gemm_mid_full_size_sampled(fmt, n, k, m):
+    c = Case(fmt, n, k, m, seed=6)
+    y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
+    check(c, y, P, M, rows=sample_rows(n))
+    check_y(c, ops.gemm(fmt, c.planes, n, k, c.q8t), rows=sample_rows(n))  # K split with a workspace
+
+
 # ------------------------------------------ poison, guards, determinism --
-@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_mid"])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_outputs_fully_written_and_guards_intact(kind, fmt):
-    n, k, t = 70, 768, (3 if kind == "gemv" else 70)
+    n, k, t = 70, 768, {"gemv": 3, "gemm": 170, "gemm_mid": 70}[kind]
     c = Case(fmt, n, k, t, seed=9)
     g = 4096
     buf = torch.full((g + t * n + g,), float("nan"), dtype=torch.float32, device="cuda")
