@@ -28,6 +28,13 @@ int8 TOPS (2*M*N*K useful ops).  `roofline` / `roofline_gemm` divide the
 same algorithmic work by the average duration of back-to-back launches of
 the GEMV / GEMM kernel alone (a graph of repeated launches between one pair
 of HIP events on the launch stream, inside the timed region).
+
+Two further measurements run after the timed steps, each in its own graphs:
+`gemm_mid` (the 32-token tile: quantise 64 rows + kq_gemm on the same six
+matrices) and `moe` (a mixture-of-experts layer: 128 Q4_K experts of gate|up
+1536 x 2048 and down 2048 x 768, 512 tokens routed top-8 by seeded U(0,1)
+logits, gather-quantise + kq_gemm_grouped for each projection).  Both are
+bound by the weight bytes, so their rooflines are in GB/s of HBM.
 """
 from __future__ import annotations
 
@@ -43,6 +50,8 @@ MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POPS
 FMTS = ("q4_k", "q5_k", "q6_k")
 SHAPES = ((9728, 2560), (2560, 9728))  # (n, k): W_up, W_down
 GEMM_M = 512
+MID_M = 64
+MOE = {"experts": 128, "tokens": 512, "top": 8, "hidden": 2048, "ffn": 768, "fmt": "q4_k"}
 BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 
 
@@ -81,7 +90,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
-    ap.add_argument("--legs", default="gemv,gemm", help="which legs to run")
+    ap.add_argument("--legs", default="gemv,gemm,mid,moe", help="which legs to run")
+    ap.add_argument("--side-reps", type=int, default=20,
+                    help="replays of the gemm_mid / moe graphs (after the timed steps)")
     return ap.parse_args()
 
 
@@ -114,6 +125,130 @@ def cpu_baseline(seconds):
                       f"Q4_K/Q5_K/Q6_K W_up/W_down matrices (Q8_K quantise included), "
                       f"{t_used:.1f} s of single-thread CPU time",
             "seconds": t_used}
+
+
+def bench_mid(mats, copies, reps, stream, capture, ev):
+    """The 32-token tile: quantise MID_M rows to the tile image + kq_gemm,
+    per matrix, rotating the weight copies; HBM-bound at this size."""
+    import torch
+
+    import synth
+    import quant_matmul_amd as kq
+    from quant_matmul_amd import torch_ops as ops
+
+    res, kb_total, kus_total = {}, 0, 0.0
+    for j, (fmt, n, k, pl) in enumerate(mats):
+        x = torch.from_numpy(synth.activations(MID_M, k, synth.seed_for(3, 50 + j))).cuda()
+        q = ops.q8k_tile_buffers(MID_M, k)
+        y = torch.empty((MID_M, n), device="cuda")
+        ws = ops.gemm_workspace(fmt, n, k, MID_M)
+
+        def leg(c, kernel_only=False):
+            if not kernel_only:
+                kq.kq_quantize_q8k_tiles(x, MID_M, k, *q)
+            kq.kq_gemm(fmt, pl[c], n, k, *q, MID_M, y, ws)
+
+        kq.kq_quantize_q8k_tiles(x, MID_M, k, *q)
+        g_leg = [capture(leg, c) for c in range(copies)]
+        g_k = capture(lambda: [leg(r % copies, True) for r in range(copies)])
+        for g in g_leg:
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for r in range(reps):
+            g_leg[r % copies].replay()
+        b.record(stream)
+        c_, d_ = ev(), ev()
+        c_.record(stream)
+        for r in range(max(1, reps // copies)):
+            g_k.replay()
+        d_.record(stream)
+        torch.cuda.synchronize()
+        leg_us = a.elapsed_time(b) * 1e3 / reps
+        kus = c_.elapsed_time(d_) * 1e3 / (max(1, reps // copies) * copies)
+        wb = n * (k // 256) * BYTES[fmt]
+        byts = wb + MID_M * (k // 256) * 292 + 4 * MID_M * n
+        res[f"{fmt}_{n}x{k}"] = {"us": kus, "leg_us": leg_us, "GBps": byts / (kus * 1e-6) / 1e9,
+                                 "TOPS": 2 * MID_M * n * k / (kus * 1e-6) / 1e12, "split_k": ws is not None}
+        kb_total += byts
+        kus_total += kus
+    ach = kb_total / (kus_total * 1e-6) / 1e9
+    return {"tokens": MID_M, "per_matrix": res,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "kq::gemm_mid_kernel (kq_gemm, m <= 127)",
+                         "avg_launch_us": kus_total / len(mats)}}
+
+
+def bench_moe(reps, stream, capture, ev):
+    """A mixture-of-experts layer: gather-quantise the routed token rows,
+    grouped gate|up, gather-quantise the (synthetic) hidden rows, grouped
+    down -- all 128 experts per launch."""
+    import torch
+
+    import synth
+    import quant_matmul_amd as kq
+    from quant_matmul_amd import torch_ops as ops
+
+    E, T, top, H, F, fmt = (MOE[x] for x in ("experts", "tokens", "top", "hidden", "ffn", "fmt"))
+    rows, tile_expert, starts, counts = synth.moe_routes(synth.router_logits(T, E, synth.seed_for(4, 0)), top)
+    m = len(rows)
+    rows_d, te_d = torch.from_numpy(rows).cuda(), torch.from_numpy(tile_expert).cuda()
+    up, up_stride = ops.pack_experts(fmt, [synth.weights(fmt, 2 * F, H, synth.seed_for(4, 10 + e))
+                                           for e in range(E)], 2 * F, H)
+    dn, dn_stride = ops.pack_experts(fmt, [synth.weights(fmt, H, F, synth.seed_for(4, 300 + e))
+                                           for e in range(E)], H, F)
+    layer_bytes = E * (2 * F * (H // 256) + H * (F // 256)) * BYTES[fmt]
+    copies = max(2, -(-(1 << 30) // layer_bytes))  # > 1 GiB per rotation: past the 256 MB cache
+    ups, dns = [up] + [up.clone() for _ in range(copies - 1)], [dn] + [dn.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(synth.activations(T, H, synth.seed_for(4, 1))).cuda()
+    h = torch.from_numpy(synth.activations(T, F, synth.seed_for(4, 2))).cuda()
+    qx, qh = ops.q8k_tile_buffers(m, H), ops.q8k_tile_buffers(m, F)
+    y1, y2 = torch.empty((m, 2 * F), device="cuda"), torch.empty((m, H), device="cuda")
+
+    def layer(c):
+        kq.kq_quantize_q8k_tiles_gather(x, T, H, rows_d, m, *qx)
+        kq.kq_gemm_grouped(fmt, ups[c], up_stride, E, te_d, 2 * F, H, *qx, m, y1)
+        kq.kq_quantize_q8k_tiles_gather(h, T, F, rows_d, m, *qh)
+        kq.kq_gemm_grouped(fmt, dns[c], dn_stride, E, te_d, H, F, *qh, m, y2)
+
+    def grouped_only(c):
+        kq.kq_gemm_grouped(fmt, ups[c], up_stride, E, te_d, 2 * F, H, *qx, m, y1)
+        kq.kq_gemm_grouped(fmt, dns[c], dn_stride, E, te_d, H, F, *qh, m, y2)
+
+    gl = [capture(layer, c) for c in range(copies)]
+    gk = [capture(grouped_only, c) for c in range(copies)]
+    for g in gl:
+        g.replay()
+    torch.cuda.synchronize()
+    a, b, c_, d_ = ev(), ev(), ev(), ev()
+    a.record(stream)
+    for r in range(reps):
+        gl[r % copies].replay()
+    b.record(stream)
+    c_.record(stream)
+    for r in range(reps):
+        gk[r % copies].replay()
+    d_.record(stream)
+    torch.cuda.synchronize()
+    layer_us = a.elapsed_time(b) * 1e3 / reps
+    gemm_us = c_.elapsed_time(d_) * 1e3 / reps
+    routed = int(counts.sum())
+    useful = 2 * routed * (2 * F * H + H * F)
+    nsb_h, nsb_f = H // 256, F // 256
+    alg = layer_bytes + routed * (nsb_h + nsb_f) * 292 + 4 * routed * (2 * F + H)
+    ach = alg / (gemm_us * 1e-6) / 1e9
+    return {"config": {"experts": E, "tokens": T, "top": top, "hidden": H, "expert_ffn": F, "format": fmt,
+                       "gate_up_rows": 2 * F, "routed_rows": routed, "image_rows_padded": m,
+                       "weight_bytes": layer_bytes, "weight_copies": copies},
+            "layer_us": layer_us, "grouped_gemms_us": gemm_us,
+            "weight_GBps": layer_bytes / (gemm_us * 1e-6) / 1e9,
+            "useful_TOPS": useful / (gemm_us * 1e-6) / 1e12,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "kq::gemm_mid_kernel (kq_gemm_grouped), gate|up + down launches",
+                         "avg_launch_us": gemm_us / 2}}
 
 
 def main():
@@ -307,6 +442,10 @@ def main():
             per.setdefault(f"{f}_{n}x{k}", {})["gemm"] = {
                 "us": us, "TOPS": 2 * GEMM_M * n * k / (us * 1e-6) / 1e12}
     out["per_matrix"] = per
+    if "mid" in legs:
+        out["gemm_mid"] = bench_mid(mats, copies, args.side_reps, stream, capture, ev)
+    if "moe" in legs:
+        out["moe"] = bench_moe(args.side_reps, stream, capture, ev)
     if out["value"] is None and "gemm" in out:
         out["value"], out["unit"] = out["gemm"]["value"], "TOPS"
     if not args.no_cpu_baseline:

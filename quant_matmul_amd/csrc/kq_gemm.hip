@@ -263,11 +263,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     for (int ks = 0; ks < 8; ++ks) load_a(s0, ks);
     load_bs(s0);
     unpack_w(0);
-    if (s0 + 1 < s1) load_w(s0 + 1);
+    load_w(s0 + 1 < s1 ? s0 + 1 : s0);
     __syncthreads();
 
     for (int s = s0; s < s1; ++s) {
         const int b = (s - s0) & 1;
+        // the next superblocks' operands are fetched and unpacked
+        // unconditionally (clamped to the last one, in bounds, into the free
+        // buffer): a branch would split the MFMA loop into blocks the
+        // scheduler cannot interleave across
+        const int sn = s + 1 < s1 ? s + 1 : s1 - 1, sn2 = s + 2 < s1 ? s + 2 : s1 - 1;
         i32x16 acc[2];
         acc[0] = acc[1] = i32x16{};
         // high-digit pass
@@ -279,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                 acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
         }
         // the unpack of the next superblock overlaps these MFMAs
-        if (s + 1 < s1) unpack_w(b ^ 1);
+        unpack_w(b ^ 1);
         acc[0] = acc[0] * 128;
         acc[1] = acc[1] * 128;
         // low-digit pass; each 32-deep K step of the codes is dead after it
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
                 acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
-            if (s + 1 < s1) load_a(s + 1, ks);
+            load_a(sn, ks);
         }
         // the one float fold of superblock s; lane l holds row n0 + l%32 and
         // tokens 8*(r/4) + 4*(l/32) + r%4 of each 32-token group, r = 0..15
@@ -323,8 +328,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                 }
             }
         }
-        if (s + 1 < s1) load_bs(s + 1);
-        if (s + 2 < s1) load_w(s + 2);
+        load_bs(sn);
+        load_w(sn2);
         __syncthreads();  // panel s+1 complete; panel s free for s+2
     }
 

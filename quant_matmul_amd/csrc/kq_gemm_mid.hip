@@ -2,19 +2,23 @@
 // GEMV and the prefill tile (9..127 tokens), and the grouped form that runs
 // every expert of a mixture-of-experts layer in one launch.
 //
-// Same arithmetic as kq_gemm (K-quant kernel arc page, "The pieces", kq v2
-// item): sub-scale-folded int8 digit passes on v_mfma_i32_32x32x32_i8, the
-// min term on v_mfma_f32_32x32x16_f16, one float fold per superblock.  What
-// changes is where the weights are unpacked.  With 32 tokens per tile the
-// weight bytes, not the matrix cores, bound the kernel, and a shared LDS
-// panel would only add traffic and barriers: each lane unpacks its own half
-// superblock row (128 weights) straight into the MFMA B-operand registers.
+// Same integer partials and float fold as kq_gemm (K-quant kernel arc page,
+// "The pieces", kq v2 item), the min term on v_mfma_f32_32x32x16_f16.  What
+// changes is where and how the weights are unpacked.  With 32 tokens per
+// tile the unpack, not the matrix cores, bounds the kernel, and a shared
+// LDS panel would only add traffic and barriers: each lane unpacks its own
+// half superblock row (128 weights) straight into MFMA B-operand registers.
 // A wave owns 32 weight rows x 32 tokens; its lane l holds row l%32 and the
 // codes k = 32*ks + 16*(l/32) + 0..15 of each 32-deep K step ks, which is
-// exactly the B operand of the 32x32x32 MFMA.  The high- and low-digit
-// products of each K step go to two accumulators, so the unpack of step
-// ks+1 overlaps the MFMAs of step ks.  Waves share nothing but L2: no
-// barriers.  The page's mid-size lesson (the chain-regrain / nrsplit
+// exactly the B operand of v_mfma_i32_32x32x32_i8.
+//  * Q4_K/Q5_K: a 32-weight sub-block is one K step, so the raw quants go to
+//    the MFMA as they are and its output is dot_j; the sub-scale is one
+//    integer mad per output, P += sc_j * dot_j.  At 32 tokens that costs
+//    less than folding sc_j into two digit planes (the prefill tile's
+//    choice, which pays off when 256 tokens share each unpacked weight).
+//  * Q6_K: 16-weight sub-blocks do not match a K step, so it keeps the
+//    digit passes (kq_digits.h), high and low digit in two accumulators.
+// Waves share nothing but L2: no barriers.  The page's mid-size lesson (the chain-regrain / nrsplit
 // commits: splitting tokens re-ran the unpack per slice) is why a tile
 // covers its 32 tokens in one pass and the grid splits rows and, when the
 // grid is small, K -- never tokens.
@@ -89,7 +93,7 @@ __device__ inline void load_lane(Lane<KQ_Q6_K> &r, const uint8_t *__restrict__ w
 
 __device__ inline uint32_t word(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
-// digits (B operands) of K step ks of the lane's half row
+// Q6_K digits (B operands) of K step ks of the lane's half row
 template <int FMT>
 __device__ inline void digits_ks(const Lane<FMT> &r, int ks, int lh, i32x4 &bh, i32x4 &bl)
 {
@@ -190,40 +194,69 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     d8v = td < mtok ? xs_row[s0] : 0.0f;
 
     for (int s = s0; s < s1; ++s) {
+        // operands of the next superblock are fetched unconditionally (the
+        // last step re-reads its own, in bounds): a branch here would split
+        // the K loop into blocks the scheduler cannot interleave across
+        const int sn = s + 1 < s1 ? s + 1 : s;
         // stage the 32 d8s of superblock s for the fold (wave-private LDS:
         // the wave's own later reads see these writes in order)
         if (lh == 0) d8w[wv][lr] = d8v;
-        if (s + 1 < s1) {
-            load_lane(nxt, wb, pl, wrow + s + 1, lh);
-            d8v = td < mtok ? xs_row[s + 1] : 0.0f;
-        }
-        i32x16 acch = i32x16{}, accl = i32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            i32x4 bh, bl;
-            digits_ks<FMT>(raw, ks, lh, bh, bl);
-            acch = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bh, acch, 0, 0, 0);
-            accl = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bl, accl, 0, 0, 0);
-            if (s + 1 < s1) load_a(s + 1, ks);
-        }
-        const i32x16 P = (acch << 7) + accl;
-        // min term: B operand = m of the sub-block of bsums 8lh + 0..7
+        load_lane(nxt, wb, pl, wrow + sn, lh);
+        d8v = td < mtok ? xs_row[sn] : 0.0f;
         float dv, dm = 0.0f;
         f32x16 mf;
+        i32x16 P;
         if constexpr (FMT == KQ_Q6_K) {
+            // 16-weight sub-blocks: the scale is folded into the two digit
+            // passes (kq_digits.h)
+            i32x16 acch = i32x16{}, accl = i32x16{};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                i32x4 bh, bl;
+                digits_ks<FMT>(raw, ks, lh, bh, bl);
+                acch = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bh, acch, 0, 0, 0);
+                accl = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bl, accl, 0, 0, 0);
+                load_a(sn, ks);
+            }
+            P = (acch << 7) + accl;
             dv = rvalid ? f16_bits_to_float(raw.d) : 0.0f;
         } else {
+            // 32-weight sub-blocks = one 32-deep K step: the raw quants are
+            // the B operand, dot_j comes out of one MFMA and the sub-scale is
+            // applied with one 24-bit integer mad per output (|dot_j| <=
+            // 31*127*32 < 2^23, |P| < 2^26): P = sum_j sc_j * dot_j exactly
+            const uint32_t s0w = raw.h.y, s1w = raw.h.z, s2w = raw.h.w;
+            // the eight 6-bit scales and mins, four per word, as bytes
+            const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
+            const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
+            const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
+            const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
+            P = i32x16{};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                i32x4 bq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t qw = word(raw.q[ks >> 1], i);
+                    uint32_t q = (ks & 1) ? (qw >> 4) & 0x0F0F0F0Fu : qw & 0x0F0F0F0Fu;
+                    if constexpr (FMT == KQ_Q5_K) q |= ((word(raw.qh, i) >> ks) & 0x01010101u) << 4;
+                    bq[i] = (int)q;
+                }
+                const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bq, i32x16{}, 0, 0, 0);
+                const int sc = (int)byte_of(ks < 4 ? sc_lo : sc_hi, ks & 3);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) P[i] = __mul24(d[i], sc) + P[i];
+                load_a(sn, ks);
+            }
             dv = rvalid ? f16_bits_to_float(raw.h.x & 0xFFFFu) : 0.0f;
             dm = rvalid ? f16_bits_to_float(raw.h.x >> 16) : 0.0f;
+            // min term: B operand = m of the sub-block of bsums 8lh + 0..7
+            const uint32_t mw = lh ? m_hi : m_lo;
             f16x8 bm;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int sc, m;
-                scale_min_6bit(raw.h.y, raw.h.z, raw.h.w, 4 * lh + j, sc, m);
-                bm[2 * j] = bm[2 * j + 1] = (_Float16)m;
-            }
+            for (int j = 0; j < 4; ++j) bm[2 * j] = bm[2 * j + 1] = (_Float16)(int)byte_of(mw, j);
             mf = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab, bm, f32x16{}, 0, 0, 0);
-            if (s + 1 < s1) load_bs(s + 1);
+            load_bs(sn);
         }
         __builtin_amdgcn_wave_barrier();
         // lane holds tokens 8*(i/4) + 4*lh + i%4, i = 0..15, of row `row`
