@@ -55,20 +55,28 @@ MOE = {"experts": 128, "tokens": 512, "top": 8, "hidden": 2048, "ffn": 768, "fmt
 BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 
 
-# HBM traffic of kq_gemv per launch, averaged over the six matrices of a
-# step: FETCH_SIZE + WRITE_SIZE counter passes scaled by a plain-copy
-# reference (profiles/kq_gemv_hbm_traffic_qwen3_4b_ffn.md).  It holds only
-# for the GEMV sources it was measured on; with any other sources the
-# roofline reports traffic as null.
-GEMV_TRAFFIC = {"src_sha256_16": "c32ca253a2f82f95", "bytes_per_launch": 17422080}
+# HBM traffic per launch, averaged over the six matrices of a step:
+# FETCH_SIZE + WRITE_SIZE counter passes scaled by a plain-copy reference
+# (profiles/kq_gemv_hbm_traffic_qwen3_4b_ffn.md,
+# profiles/kq_gemm_hbm_traffic_qwen3_4b_ffn_pp512.md; the GEMM figure is one
+# kq_gemm call, split-sum pass included).  Each holds only for the sources
+# it was measured on; with any other sources the roofline reports null.
+GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "dbc622837506cdc1",
+                "bytes_per_launch": 17422042}
+GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "c93cf9ede3148534",
+                "bytes_per_launch": 79880411}
 
 
-def gemv_src_hash():
+def src_hash(files):
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(here, "quant_matmul_amd", "csrc")
-    data = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("kq_gemv.hip", "kq_common.h"))
+    data = b"".join(open(os.path.join(csrc, f), "rb").read() for f in files)
     return hashlib.sha256(data).hexdigest()[:16]
+
+
+def measured_traffic(rec):
+    return rec["bytes_per_launch"] if src_hash(rec["files"]) == rec["src_sha256_16"] else None
 
 
 def gemv_bytes(fmt, n, k, t=1, fused=True):
@@ -93,6 +101,12 @@ def parse():
     ap.add_argument("--legs", default="gemv,gemm,mid,moe", help="which legs to run")
     ap.add_argument("--side-reps", type=int, default=20,
                     help="replays of the gemm_mid / moe graphs (after the timed steps)")
+    ap.add_argument("--profile-one", metavar="KIND:FMT:N:K:T",
+                    help="instead of the benchmark, run one configuration --reps times (for "
+                         "rocprofv3 counter passes): KIND gemv|gemm|mid (T activation rows), "
+                         "moe (the MoE layer; FMT:N:K:T ignored), copy (a plain 64 MiB device "
+                         "copy, the counters' byte reference)")
+    ap.add_argument("--reps", type=int, default=10)
     return ap.parse_args()
 
 
@@ -251,6 +265,54 @@ def bench_moe(reps, stream, capture, ev):
                          "avg_launch_us": gemm_us / 2}}
 
 
+def profile_one(spec, reps):
+    """One kq configuration `reps` times on fixed seeded inputs, nothing else
+    timed: the workload of a rocprofv3 counter pass."""
+    import torch
+
+    import synth
+    import quant_matmul_amd as kq
+    from quant_matmul_amd import torch_ops as ops
+
+    kind, *rest = spec.split(":")
+    if kind == "copy":
+        src = torch.empty(16 << 20, dtype=torch.float32, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(reps):
+            dst.copy_(src)
+    elif kind == "moe":
+        # the bench's MoE layer, replayed
+        bench_moe(reps, torch.cuda.current_stream(), lambda fn, *a: _Eager(fn, *a),
+                  lambda: torch.cuda.Event(enable_timing=True))
+    else:
+        fmt, n, k, t = rest[0], int(rest[1]), int(rest[2]), int(rest[3])
+        planes = ops.pack(fmt, ops.upload_records(synth.weights(fmt, n, k, synth.seed_for(1, 0))), n, k)
+        x = torch.from_numpy(synth.activations(t, k, synth.seed_for(1, 50))).cuda()
+        y = torch.empty((t, n), device="cuda")
+        if kind == "gemv":
+            q = ops.quantize_q8k(x)
+            for _ in range(reps):
+                kq.kq_gemv(fmt, planes, n, k, *q, t, y)
+        else:
+            q = ops.quantize_q8k_tiles(x)
+            ws = ops.gemm_workspace(fmt, n, k, t)
+            for _ in range(reps):
+                kq.kq_gemm(fmt, planes, n, k, *q, t, y, ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_one": spec, "reps": reps}), flush=True)
+    return 0
+
+
+class _Eager:
+    """Stands in for a captured graph: replay() runs the function eagerly."""
+
+    def __init__(self, fn, *a):
+        self.fn, self.a = fn, a
+
+    def replay(self):
+        self.fn(*self.a)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -259,6 +321,8 @@ def main():
               file=sys.stderr)
         return 2
     legs = set(args.legs.split(","))
+    if args.profile_one:
+        return profile_one(args.profile_one, args.reps)
 
     import numpy as np
     import torch
@@ -416,8 +480,7 @@ def main():
         kb = sum(reps["gemv"] * gemv_bytes(f, n, k, fused=False) for f, n, k, _ in mats)
         kms = ms(krec["gemv"])
         ach = kb / (kms * 1e-3) / 1e9
-        traffic = (GEMV_TRAFFIC["bytes_per_launch"]
-                   if gemv_src_hash() == GEMV_TRAFFIC["src_sha256_16"] else None)
+        traffic = measured_traffic(GEMV_TRAFFIC)
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
                            "algorithmic_bytes_per_launch": kb / (reps["gemv"] * len(mats)),
@@ -434,8 +497,12 @@ def main():
         ach = reps["gemm"] * ops_step / (kms * 1e-3) / 1e12
         out["gemm"] = {"value": args.steps * ops_step / (leg_ms * 1e-3) / 1e12, "unit": "TOPS",
                        "leg_ms_per_step": leg_ms / args.steps}
+        gemm_alg = sum(n * (k // 256) * BYTES[f] + GEMM_M * (k + k // 64 + k // 8) + 4 * GEMM_M * n
+                       for f, n, k, _ in mats) / len(mats)
         out["roofline_gemm"] = {"bound": "mfma", "achieved": ach, "peak": MFMA_I8_PEAK_TOPS, "unit": "TOPS",
-                                "frac": ach / MFMA_I8_PEAK_TOPS, "traffic": None, "kernel": "kq::gemm_kernel",
+                                "frac": ach / MFMA_I8_PEAK_TOPS, "traffic": measured_traffic(GEMM_TRAFFIC),
+                                "algorithmic_bytes_per_launch": gemm_alg,
+                                "kernel": "kq::gemm_kernel (+ kq::sum_splits for W_down)",
                                 "avg_launch_us": kms * 1e3 / (reps["gemm"] * len(mats))}
         for j, (f, n, k, _) in enumerate(mats):
             us = krec["gemm"][j][0].elapsed_time(krec["gemm"][j][1]) * 1e3 / reps["gemm"]
