@@ -1,8 +1,10 @@
 // kq_digits.h -- the GEMMs' operand form of a K-quant weight: the
 // sub-scale-folded value w' = sc*q (Q4_K/Q5_K) or sc*(q-32) (Q6_K), split
-// into two int8 digits w' = 128*h + l, l in 0..127, four weights per dword.
-// The int8 MFMA then forms the per-sub-block integer fold P = sum sc*dot as
-// 128*(h . a) + (l . a) (K-quant kernel arc page, "The pieces", kq v2 item).
+// into two int8 digits, four weights per dword: w' = 128*h + l, l in 0..127
+// (Q5_K, Q6_K), or w' = 8*(u*q) + (v*q) with sc = 8u + v (Q4_K).  The int8
+// MFMA then forms the per-sub-block integer fold P = sum sc*dot as
+// 2^SHIFT*(h . a) + (l . a) (K-quant kernel arc page, "The pieces", kq v2
+// item).
 #pragma once
 
 #include "kq_common.h"
@@ -49,6 +51,20 @@ __device__ inline void digits_q6(uint32_t q, int sc, uint32_t &hi, uint32_t &lo)
     uint32_t hu;
     split_digits(e, o, hu, lo);
     hi = ((hu | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Q4_K's other split.  Its quants are 4-bit, so with the sub-scale written
+// as sc = 8*u + v (u, v in 0..7) both u*q and v*q are at most 105: they fit
+// a signed byte and four of them come out of one packed 16-bit multiply
+// with no carry between bytes.  Then sc*q = 8*(u*q) + (v*q), and the two
+// MFMA passes give P = 8*H + L.  Four quants (bytes of q, each <= 15):
+__device__ inline void digits_q4(uint32_t q, int u, int v, uint32_t &hi, uint32_t &lo)
+{
+    const u16x2 qq = __builtin_bit_cast(u16x2, q);
+    hi = __builtin_bit_cast(uint32_t, qq * u16x2{(unsigned short)u, (unsigned short)u});
+    lo = __builtin_bit_cast(uint32_t, qq * u16x2{(unsigned short)v, (unsigned short)v});
 }
 
 }  // namespace

@@ -9,15 +9,18 @@
 //    once per (group, token-block) and amortise it over the token block),
 //    each workgroup unpacks the superblock of its 32 weight rows into LDS
 //    once and reuses it for all 256 tokens.  What lands in LDS is not the
-//    raw quant but the sub-scale-folded weight w' = sc*q (Q4_K/Q5_K,
-//    0..1953) or sc*(q-32) (Q6_K, -4064..4096), split into two int8 digits
-//    w' = 128*h + l with l in 0..127: the MFMA cannot apply a per-row,
-//    per-sub-block scale, so folding it into the operand is what keeps the
-//    per-sub-block integer fold on the matrix cores.
+//    raw quant but the sub-scale-folded weight w' = sc*q (Q4_K/Q5_K) or
+//    sc*(q-32) (Q6_K, -4064..4096) as two int8 digits (kq_digits.h): the
+//    MFMA cannot apply a per-row, per-sub-block scale, so folding it into
+//    the operand is what keeps the per-sub-block integer fold on the matrix
+//    cores.  Q5_K/Q6_K use w' = 128*h + l; Q4_K, whose quants are 4-bit,
+//    splits the scale instead (sc = 8u + v, digits u*q and v*q), which one
+//    packed 16-bit multiply forms four at a time.
 //  * Dense contraction: v_mfma_i32_32x32x32_i8, a high-digit pass, a shift
-//    by 7, a low-digit pass into the same int32 accumulator -- which then
-//    holds P = sum_j sc_j * dot_j exactly (|P| < 2^27).  The 32x32x32 form
-//    sustains about twice the int8 rate of the 16x16x64 form on gfx950.
+//    by 7 (Q4_K: 3), a low-digit pass into the same int32 accumulator --
+//    which then holds P = sum_j sc_j * dot_j exactly (|P| < 2^27).  The
+//    32x32x32 form sustains about twice the int8 rate of the 16x16x64 form
+//    on gfx950.
 //  * Min term: M = sum_g m_{g/2} * bsum_g is a 16-deep contraction per
 //    superblock, one v_mfma_f32_32x32x16_f16 (bsums |.| <= 2032 and m <= 63
 //    are exact in f16, and |M| < 2^24 keeps the f32 sum exact).
@@ -36,9 +39,12 @@
 // the wave's codes sit in registers, the digit panel in one of two LDS
 // buffers; while the high-digit MFMAs of s run, the wave unpacks its share
 // of superblock s+1 (whose packed bytes were prefetched) into the other
-// buffer, so the VALU unpack overlaps the matrix pipe, and each 32-deep K
-// step of the codes is refilled with superblock s+1 as soon as its
-// low-digit MFMAs are issued.  One barrier per superblock.
+// buffer, so the VALU unpack overlaps the matrix pipe; the low-digit pass
+// runs tile by tile so that tile 0's float fold issues under tile 1's
+// MFMAs; each 32-deep K step of the codes is refilled with superblock s+1
+// as soon as it is dead.  The loop body is one basic block (no divergent
+// branch: validity is masked, every refill is unconditional), so the
+// scheduler can interleave all of it.  One barrier per superblock.
 #include "kq_common.h"
 #include "kq_digits.h"
 
@@ -48,6 +54,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int LDS_STRIDE = 272;  // bytes per digit row: 256 + 16 pad
 
@@ -109,7 +116,8 @@ __device__ inline void unpack_half(const Half<KQ_Q6_K> &rw, bool valid, int r, i
     const int c = h >> 1, half = h & 1, hh = c >> 1, u = c & 1;
     const uint32_t lw[4] = {rw.l.x, rw.l.y, rw.l.z, rw.l.w};
     const uint32_t hw[4] = {rw.hq.x, rw.hq.y, rw.hq.z, rw.hq.w};
-    const uint2 s8 = valid ? rw.s8 : make_uint2(0, 0);
+    const uint32_t vm = valid ? 0xFFFFFFFFu : 0u;
+    const uint2 s8 = make_uint2(rw.s8.x & vm, rw.s8.y & vm);
     const int slo = (int8_t)byte_of(s8.x, 2 * u + half), shi = (int8_t)byte_of(s8.y, 2 * u + half);
     uint32_t h0[4], l0[4], h1[4], l1[4];
 #pragma unroll
@@ -122,10 +130,9 @@ __device__ inline void unpack_half(const Half<KQ_Q6_K> &rw, bool valid, int r, i
     const int k0 = 128 * hh + 32 * u + 16 * half;
     store_half(wh, wl, r, k0, h0, l0);
     store_half(wh, wl, r, k0 + 64, h1, l1);
-    if (h == 0) {
-        dn[r] = valid ? f16_bits_to_float(rw.d) : 0.0f;
-        dmn[r] = 0.0f;
-    }
+    // every task of the row writes the same scale (no divergent branch)
+    dn[r] = valid ? f16_bits_to_float(rw.d) : 0.0f;
+    dmn[r] = 0.0f;
 }
 
 template <int FMT>
@@ -133,7 +140,9 @@ __device__ inline void unpack_half(const Half<FMT> &rw, bool valid, int r, int h
                                    _Float16 *mexp, float *dn, float *dmn)
 {
     const int c = h >> 1, half = h & 1;
-    const uint4 hd = valid ? rw.h : make_uint4(0, 0, 0, 0);
+    // rows past n: scales and mins masked to zero (an AND, not a branch)
+    const uint32_t vm = valid ? 0xFFFFFFFFu : 0u;
+    const uint4 hd = make_uint4(rw.h.x & vm, rw.h.y & vm, rw.h.z & vm, rw.h.w & vm);
     const uint32_t qw[4] = {rw.q.x, rw.q.y, rw.q.z, rw.q.w};
     int sc0, m0, sc1, m1;
     scale_min_6bit(hd.y, hd.z, hd.w, 2 * c, sc0, m0);
@@ -146,23 +155,23 @@ __device__ inline void unpack_half(const Half<FMT> &rw, bool valid, int r, int h
             const uint32_t hb = i == 0 ? rw.qh.x : i == 1 ? rw.qh.y : i == 2 ? rw.qh.z : rw.qh.w;
             lo |= ((hb >> (2 * c)) & 0x01010101u) << 4;
             hi |= ((hb >> (2 * c + 1)) & 0x01010101u) << 4;
+            digits_q45(lo, sc0, h0[i], l0[i]);
+            digits_q45(hi, sc1, h1[i], l1[i]);
+        } else {
+            digits_q4(lo, sc0 >> 3, sc0 & 7, h0[i], l0[i]);
+            digits_q4(hi, sc1 >> 3, sc1 & 7, h1[i], l1[i]);
         }
-        digits_q45(lo, sc0, h0[i], l0[i]);
-        digits_q45(hi, sc1, h1[i], l1[i]);
     }
     const int k0 = 64 * c + 16 * half;
     store_half(wh, wl, r, k0, h0, l0);
     store_half(wh, wl, r, k0 + 32, h1, l1);
-    if (half == 0) {
-        // min of sub-block j pairs with bsums 2j and 2j+1
-        _Float16 *me = mexp + r * 16 + 4 * c;
-        me[0] = me[1] = (_Float16)m0;
-        me[2] = me[3] = (_Float16)m1;
-    }
-    if (h == 0) {
-        dn[r] = f16_bits_to_float(hd.x & 0xFFFFu);
-        dmn[r] = f16_bits_to_float(hd.x >> 16);
-    }
+    // min of sub-block j pairs with bsums 2j and 2j+1: the half-0 task
+    // writes sub-block 2c's pair, the half-1 task 2c+1's; every task of the
+    // row writes the same d, dmin (no divergent branch)
+    const _Float16 mv = (_Float16)(half ? m1 : m0);
+    *reinterpret_cast<f16x2 *>(mexp + r * 16 + 4 * c + 2 * half) = f16x2{mv, mv};
+    dn[r] = f16_bits_to_float(hd.x & 0xFFFFu);
+    dmn[r] = f16_bits_to_float(hd.x >> 16);
 }
 
 // Workgroup index -> work item, grouping consecutive items on one XCD
@@ -182,7 +191,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                                                       const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                       const _Float16 *__restrict__ xbs, int64_t mtok,
                                                       float *__restrict__ y, int32_t *__restrict__ Pout,
-                                                      int32_t *__restrict__ Mout, int mtiles, int S)
+                                                      int32_t *__restrict__ Mout, int mtiles, int full, int TS,
+                                                      float *__restrict__ ws)
 {
     constexpr int BM = 256, BN = 32;
     static_assert(BN * 8 == 256, "one 32-weight unpack task per thread");
@@ -192,9 +202,19 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     __shared__ float dn[2][BN], dmn[2][BN];
     __shared__ __align__(16) float d8s[2][BM];
 
-    // item = (tile, K split); split j of S covers superblocks [s0, s1)
-    const int item = item_of(blockIdx.x, gridDim.x);
-    const int tile = item / S, split = item - tile * S;
+    // Workgroups 0..full-1 each run one whole tile and write y; the rest run
+    // the remaining tiles split along K in TS parts (split j covers
+    // superblocks [s0, s1)) and write partial tiles to ws.  The whole tiles
+    // come first in dispatch order, so the split ones fill the tail.
+    int tile, split = 0, S = 1;
+    if ((int)blockIdx.x < full) {
+        tile = item_of(blockIdx.x, full);
+    } else {
+        const int r = item_of(blockIdx.x - full, gridDim.x - full);
+        tile = full + r / TS;
+        split = r - (r / TS) * TS;
+        S = TS;
+    }
     const int nt = tile / mtiles, mt = tile - nt * mtiles;
     const int s0 = (int)((int64_t)nsb * split / S), s1 = (int)((int64_t)nsb * (split + 1) / S);
     const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
@@ -214,7 +234,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     float d8n = 0.0f;
     auto load_w = [&](int s) {
         load_half(raw, w, pl, wrow + s, tid & 7);
-        d8n = t_d8 < mtok ? xs_row[s] : 0.0f;
+        // unconditional load (xs_row is clamped in bounds), then select
+        const float d8v = xs_row[s];
+        d8n = t_d8 < mtok ? d8v : 0.0f;
     };
     auto unpack_w = [&](int b) {
         unpack_half(raw, wvalid, tid >> 3, tid & 7, wh[b], wl[b], mexp[b], dn[b], dmn[b]);
@@ -245,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
             A[mi][ks] = __builtin_bit_cast(
-                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[mi] + (s * 8 + ks) * 1024, 0, 0));
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[mi], (s * 8 + ks) * 1024, 0));
     };
     auto load_bs = [&](int s) {
         if constexpr (FMT != KQ_Q6_K) {
@@ -274,68 +296,87 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
         // scheduler cannot interleave across
         const int sn = s + 1 < s1 ? s + 1 : s1 - 1, sn2 = s + 2 < s1 ? s + 2 : s1 - 1;
         i32x16 acc[2];
-        acc[0] = acc[1] = i32x16{};
-        // high-digit pass
+        // high-digit pass (the first K step starts from the zero operand)
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const i32x4 B = *reinterpret_cast<const i32x4 *>(wh[b] + l32 * LDS_STRIDE + 32 * ks + 16 * lh);
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
-                acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
+                acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, ks == 0 ? i32x16{} : acc[mi], 0, 0, 0);
         }
         // the unpack of the next superblock overlaps these MFMAs
         unpack_w(b ^ 1);
-        acc[0] = acc[0] * 128;
-        acc[1] = acc[1] * 128;
-        // low-digit pass; each 32-deep K step of the codes is dead after it
-        // and is refilled with superblock s+1 at once
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + l32 * LDS_STRIDE + 32 * ks + 16 * lh);
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
-            load_a(sn, ks);
-        }
-        // the one float fold of superblock s; lane l holds row n0 + l%32 and
-        // tokens 8*(r/4) + 4*(l/32) + r%4 of each 32-token group, r = 0..15
+        // weight of the high digit: 8 for Q4_K's sc = 8u + v split, else 128
+        constexpr int SHIFT = FMT == KQ_Q4_K ? 3 : 7;
         const float dv = dn[b][l32], dm = dmn[b][l32];
         const int64_t col = n0 + l32;
         f16x8 Bm;
         if constexpr (FMT != KQ_Q6_K) Bm = *reinterpret_cast<const f16x8 *>(mexp[b] + l32 * 16 + 8 * lh);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-            f32x16 mf;
-            if constexpr (FMT != KQ_Q6_K) mf = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab[mi], Bm, f32x16{}, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int tl = wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                const float Pf = (float)acc[mi][r];
-                float u;
-                if constexpr (FMT == KQ_Q6_K) u = dv * Pf;
-                else u = fmaf(dv, Pf, -(dm * mf[r]));
-                accf[mi][r] = fmaf(d8s[b][tl], u, accf[mi][r]);
-                if (PART) {
-                    const int64_t t = m0 + tl;
-                    if (t < mtok && col < n) {
-                        const int64_t o = (t * n + col) * nsb + s;
-                        Pout[o] = acc[mi][r];
-                        if (Mout) {
-                            if constexpr (FMT == KQ_Q6_K) Mout[o] = 0;
-                            else Mout[o] = (int)mf[r];
-                        }
+        f32x16 mf0, mf1;
+        if constexpr (FMT != KQ_Q6_K) mf0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab[0], Bm, f32x16{}, 0, 0, 0);
+        // one float fold of superblock s for element r of tile mi; lane l
+        // holds row n0 + l%32 and tokens 8*(r/4) + 4*(l/32) + r%4 of each
+        // 32-token group
+        auto fold = [&](int mi, int r, const f32x16 &mf) {
+            const int tl = wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const float Pf = (float)acc[mi][r];
+            float u;
+            if constexpr (FMT == KQ_Q6_K) u = dv * Pf;
+            else u = fmaf(dv, Pf, -(dm * mf[r]));
+            accf[mi][r] = fmaf(d8s[b][tl], u, accf[mi][r]);
+            if (PART) {
+                const int64_t t = m0 + tl;
+                if (t < mtok && col < n) {
+                    const int64_t o = (t * n + col) * nsb + s;
+                    Pout[o] = acc[mi][r];
+                    if (Mout) {
+                        if constexpr (FMT == KQ_Q6_K) Mout[o] = 0;
+                        else Mout[o] = (int)mf[r];
                     }
                 }
             }
+        };
+        // low-digit pass of tile 0; each 32-deep K step of its codes is
+        // refilled with superblock s+1 as soon as it is dead
+        acc[0] = acc[0] << SHIFT;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + l32 * LDS_STRIDE + 32 * ks + 16 * lh);
+            acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0][ks], B, acc[0], 0, 0, 0);
+            A[0][ks] = __builtin_bit_cast(
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[0], (sn * 8 + ks) * 1024, 0));
         }
+        // keep tile 1's MFMAs after tile 0's, so tile 0's fold can run under them
+        __builtin_amdgcn_sched_barrier(0);
+        // low-digit pass of tile 1, with tile 0's fold under its MFMAs
+        acc[1] = acc[1] << SHIFT;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + l32 * LDS_STRIDE + 32 * ks + 16 * lh);
+            acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[1][ks], B, acc[1], 0, 0, 0);
+            A[1][ks] = __builtin_bit_cast(
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[1], (sn * 8 + ks) * 1024, 0));
+            fold(0, 2 * ks, mf0);
+            fold(0, 2 * ks + 1, mf0);
+        }
+        if constexpr (FMT != KQ_Q6_K) mf1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab[1], Bm, f32x16{}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) fold(1, r, mf1);
         load_bs(sn);
         load_w(sn2);
         __syncthreads();  // panel s+1 complete; panel s free for s+2
     }
 
-    // K split j of S writes its partial sums to slice j of y (y then
-    // points at the workspace), reduced in split order by sum_splits
-    float *yo = y + (int64_t)split * mtok * n;
+    if (S > 1) {
+        // partial tile (lane-major: element r of tile mi of wave wm at
+        // ((wm*32 + mi*16 + r) * 64 + lane)), summed by sum_tile_splits
+        float *part = ws + ((int64_t)(tile - full) * S + split) * (BM * BN);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part[((wm * 32 + mi * 16 + r) << 6) + lane] = accf[mi][r];
+        return;
+    }
     const int64_t col = n0 + l32;
     if (col < n) {
 #pragma unroll
@@ -343,13 +384,34 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t t = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (t < mtok) yo[t * n + col] = accf[mi][r];
+                if (t < mtok) y[t * n + col] = accf[mi][r];
             }
     }
 }
 
-// y = ((p_0 + p_1) + p_2) + ... over the S partial slices, in split order,
-// one float per thread (y is only 4-byte aligned)
+// The split tiles' outputs: y = ((p_0 + p_1) + p_2) + ... over the TS
+// partial tiles, in split order; one thread per output of a split tile.
+__global__ __launch_bounds__(256) void sum_tile_splits(const float *__restrict__ ws, int TS, int full, int ntail,
+                                                       int mtiles, int64_t n, int64_t mtok, float *__restrict__ y)
+{
+    constexpr int E = 256 * 32;  // outputs per tile
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)ntail * E) return;
+    const int st = (int)(gid / E), e = (int)(gid - (int64_t)st * E);
+    const float *p = ws + (int64_t)st * TS * E + e;
+    float acc = p[0];
+    for (int j = 1; j < TS; ++j) acc += p[(int64_t)j * E];
+    const int lane = e & 63, idx = e >> 6;  // idx = wm*32 + mi*16 + r
+    const int wm = idx >> 5, mi = (idx >> 4) & 1, r = idx & 15;
+    const int tile = full + st, nt = tile / mtiles, mt = tile - nt * mtiles;
+    const int64_t t = (int64_t)mt * 256 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    const int64_t col = (int64_t)nt * 32 + (lane & 31);
+    if (t < mtok && col < n) y[t * n + col] = acc;
+}
+
+// y = ((p_0 + p_1) + p_2) + ... over S whole-output partial slices p_j of
+// m*n floats, in split order, one float per thread (y is only 4-byte
+// aligned); the K-split form of the 32-token tile (kq_gemm_mid.hip)
 __global__ __launch_bounds__(256) void sum_splits(const float *__restrict__ p, int S, int64_t count,
                                                   float *__restrict__ y)
 {
@@ -365,13 +427,22 @@ void launch_sum_splits(const float *p, int S, int64_t count, float *y, hipStream
     hipLaunchKernelGGL(sum_splits, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, p, S, count, y);
 }
 
-// K splits for a grid of `tiles` workgroups: enough to give about two
-// workgroups per CU (the occupancy of this kernel), each split at least 3
-// superblocks deep, at most 8.  The splits' partial sums go to a workspace
-// and a second kernel adds them in split order: a deterministic sum, and no
-// cross-workgroup signalling (on MI355X a device-scope fence writes back and
-// invalidates the whole L2 of the XCD, which costs more than the pass).
-static int pick_splits(int64_t tiles, int nsb)
+// Grid plan.  `slots` = workgroups resident at once (two per CU at this
+// kernel's occupancy).  A grid of at least `slots` tiles runs unsplit.  A
+// smaller one (W_down at pp512: 160 tiles) is split along K into up to 8
+// parts of at least 3 superblocks.  The split tiles' partial sums go to the
+// caller's workspace and sum_tile_splits adds them in split order:
+// deterministic, and with no cross-workgroup signalling (on MI355X a
+// device-scope fence writes back and invalidates the whole L2 of the XCD,
+// which costs more than the pass).  The kernel also takes a grid whose
+// whole rounds run unsplit and only the last partial round is split, but
+// measured on the pp512 W_up grid (608 tiles) that was no faster, so the
+// plan does not use it.
+struct Plan {
+    int full, tail, TS;
+};
+
+static Plan plan_of(int64_t n, int64_t m, int nsb)
 {
     static int cus = 0;
     if (!cus) {
@@ -381,33 +452,36 @@ static int pick_splits(int64_t tiles, int nsb)
             cus = 256;
     }
     const int64_t slots = 2 * (int64_t)cus;
-    int S = (int)(slots / tiles);
-    S = S < nsb / 3 ? S : nsb / 3;
-    S = S < 8 ? S : 8;
-    return S > 1 ? S : 1;
+    const int64_t tiles = ((n + 31) / 32) * ((m + 255) / 256);
+    const int64_t tail = tiles < slots ? tiles : 0;
+    Plan p{(int)tiles, 0, 1};
+    if (tail == 0) return p;
+    int TS = (int)(slots / tail);
+    TS = TS < nsb / 3 ? TS : nsb / 3;
+    TS = TS < 8 ? TS : 8;
+    if (TS < 2) return p;
+    return Plan{(int)(tiles - tail), (int)tail, TS};
 }
-
-static int64_t tiles_of(int64_t n, int64_t m) { return ((n + 31) / 32) * ((m + 255) / 256); }
 
 size_t gemm_workspace_bytes(int64_t n, int64_t k, int64_t m)
 {
-    const int S = pick_splits(tiles_of(n, m), (int)(k / QK));
-    return S == 1 ? 0 : (size_t)S * (size_t)m * (size_t)n * 4;
+    const Plan p = plan_of(n, m, (int)(k / QK));
+    return (size_t)p.tail * p.TS * 256 * 32 * 4;
 }
 
 template <int FMT>
 static void launch_fmt(bool part, int64_t n, int nsb, const uint8_t *w, const int8_t *xq, const float *xs,
-                       const _Float16 *xbs, int64_t m, float *y, int32_t *P, int32_t *M, int S, hipStream_t st)
+                       const _Float16 *xbs, int64_t m, float *y, int32_t *P, int32_t *M, const Plan &pl, float *ws,
+                       hipStream_t st)
 {
-    constexpr int BM = 256, BN = 32;
-    const int64_t ntiles = (n + BN - 1) / BN, mtiles = (m + BM - 1) / BM;
-    const dim3 g((unsigned)(ntiles * mtiles * S)), b(256);
+    const int64_t mtiles = (m + 255) / 256;
+    const dim3 g((unsigned)(pl.full + (int64_t)pl.tail * pl.TS)), b(256);
     if (part)
         hipLaunchKernelGGL((gemm_kernel<FMT, true>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles,
-                           S);
+                           pl.full, pl.TS, ws);
     else
         hipLaunchKernelGGL((gemm_kernel<FMT, false>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles,
-                           S);
+                           pl.full, pl.TS, ws);
 }
 
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -418,14 +492,18 @@ int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
     const uint8_t *wb = (const uint8_t *)w;
     const _Float16 *bt = (const _Float16 *)xbs;
     const bool part = P != nullptr;
-    // split K only with a workspace large enough (and never for the partials)
-    int S = 1;
-    if (!part && ws && ws_bytes >= gemm_workspace_bytes(n, k, m)) S = pick_splits(tiles_of(n, m), nsb);
-    float *dst = S > 1 ? (float *)ws : y;
-    if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
-    else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
-    else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, bt, m, dst, P, M, S, st);
-    if (S > 1) launch_sum_splits((const float *)ws, S, m * n, y, st);
+    // split only with a workspace large enough (and never for the partials)
+    Plan pl = plan_of(n, m, nsb);
+    if (part || !ws || ws_bytes < gemm_workspace_bytes(n, k, m) || pl.tail == 0) pl = Plan{pl.full + pl.tail, 0, 1};
+    float *wsf = (float *)ws;
+    if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, wsf, st);
+    else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, wsf, st);
+    else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, wsf, st);
+    if (pl.tail > 0) {
+        const int64_t cnt = (int64_t)pl.tail * 256 * 32;
+        hipLaunchKernelGGL(sum_tile_splits, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, (const float *)wsf,
+                           pl.TS, pl.full, pl.tail, (int)((m + 255) / 256), n, m, y);
+    }
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 

@@ -81,11 +81,15 @@ def test_gemm_argument_checks():
 
 
 def test_gemm_workspace_bytes():
-    # W_down at pp512 (160 tiles of 256 x 32) splits k; W_up (608 tiles) does not
-    assert kq.kq_gemm_workspace_bytes("q6_k", 2560, 9728, 512) > 0
+    # on 256 CUs (2 x 256 workgroup slots; a host without a GPU assumes 256):
+    # W_down at pp512 (160 tiles of 256 x 32) splits all its tiles in 3,
+    # W_up (608 tiles, more than one round) runs unsplit
+    tile = 256 * 32 * 4
+    assert kq.kq_gemm_workspace_bytes("q6_k", 2560, 9728, 512) == 160 * 3 * tile
     assert kq.kq_gemm_workspace_bytes("q4_k", 9728, 2560, 512) == 0
-    # S = 3 partial slices of the m x n output
-    assert kq.kq_gemm_workspace_bytes("q4_k", 300, 2560, 130) == 3 * 130 * 300 * 4
+    assert kq.kq_gemm_workspace_bytes("q4_k", 8192, 2560, 512) == 0  # exactly one round
+    # the 32-token tile (m <= 127): S = 3 partial slices of the m x n output
+    assert kq.kq_gemm_workspace_bytes("q4_k", 300, 2560, 100) > 0
     assert kq.kq_gemm_workspace_bytes("q4_k", 300, 300, 130) == 0
     assert kq.kq_gemm_workspace_bytes(9, 300, 2560, 130) == 0
 
