@@ -3,25 +3,26 @@
 // every expert of a mixture-of-experts layer in one launch.
 //
 // Same integer partials and float fold as kq_gemm (K-quant kernel arc page,
-// "The pieces", kq v2 item), the min term on v_mfma_f32_32x32x16_f16.  What
-// changes is where and how the weights are unpacked.  With 32 tokens per
-// tile the unpack, not the matrix cores, bounds the kernel, and a shared
-// LDS panel would only add traffic and barriers: each lane unpacks its own
-// half superblock row (128 weights) straight into MFMA B-operand registers.
-// A wave owns 32 weight rows x 32 tokens; its lane l holds row l%32 and the
-// codes k = 32*ks + 16*(l/32) + 0..15 of each 32-deep K step ks, which is
-// exactly the B operand of v_mfma_i32_32x32x32_i8.
-//  * Q4_K/Q5_K: a 32-weight sub-block is one K step, so the raw quants go to
-//    the MFMA as they are and its output is dot_j; the sub-scale is one
-//    integer mad per output, P += sc_j * dot_j.  At 32 tokens that costs
-//    less than folding sc_j into two digit planes (the prefill tile's
-//    choice, which pays off when 256 tokens share each unpacked weight).
-//  * Q6_K: 16-weight sub-blocks do not match a K step, so it keeps the
-//    digit passes (kq_digits.h), high and low digit in two accumulators.
-// Waves share nothing but L2: no barriers.  The page's mid-size lesson (the chain-regrain / nrsplit
-// commits: splitting tokens re-ran the unpack per slice) is why a tile
-// covers its 32 tokens in one pass and the grid splits rows and, when the
-// grid is small, K -- never tokens.
+// "The pieces", kq v2 item), the min term on v_mfma_f32_32x32x16_f16.  A
+// workgroup is 4 waves over 128 weight rows x one 32-token tile (a wave: 32
+// rows x 32 tokens, one v_mfma_i32_32x32x32_i8 tile), so each unpacked
+// weight serves 32 tokens; what changes from the 256-token tile is how the
+// weights are unpacked.
+//  * Q4_K/Q5_K: a 32-weight sub-block is one K step, so the MFMA takes the
+//    raw quants as its B operand, yields dot_j, and P += sc_j * dot_j is one
+//    integer mad per output (cheaper at 32 tokens than folding sc_j into
+//    two digit planes).  The workgroup fetches its 128 rows of a superblock
+//    cooperatively (eight lanes per 128-byte row: whole cache lines) into a
+//    double-buffered LDS panel of one byte per quant.
+//  * Q6_K: 16-weight sub-blocks do not match a K step; each lane unpacks
+//    its own half row into digit registers (kq_digits.h), no LDS panel.
+// Measured on 128 experts x 32-row tiles the HBM traffic is at the
+// algorithmic bytes; the per-output mads and folds keep the SIMDs, not HBM,
+// the limit at this token count.
+// The page's mid-size lesson (the nrsplit / regrain commits: splitting
+// tokens re-ran the unpack per slice) is why a tile covers its 32 tokens in
+// one pass and the grid splits rows and, when the grid is small, K -- never
+// tokens.
 //
 // Grouped form: the activation rows are gathered per expert into one tile
 // image, each expert's rows padded to whole 32-row tiles, and tile_expert
@@ -40,47 +41,17 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
-// Raw bytes of one lane's half superblock row (lane half lh takes the codes
-// k = 32*ks + 16*lh + e of every K step ks):
-//  Q4_K/Q5_K: weights 64c + 16lh + e and 64c + 32 + 16lh + e are the low
-//    and high nibbles of quant byte 32c + 16lh + e; Q5_K's fifth bit of
-//    sub-block j is bit j of high-bit byte 16lh + e.
-//  Q6_K: weight 128h + 32u + 16lh + e takes nibble u/2 of low byte
-//    64h + 32(u%2) + 16lh + e and bits 2u, 2u+1 of high byte 32h + 16lh + e;
-//    its scale is that of 16-weight sub-block 8h + 2u + lh.
-template <int FMT>
-struct Lane;
-template <>
-struct Lane<KQ_Q4_K> {
-    uint4 h, q[4];
-};
-template <>
-struct Lane<KQ_Q5_K> {
-    uint4 h, q[4], qh;
-};
-template <>
-struct Lane<KQ_Q6_K> {
+// Q6_K raw bytes of one lane's half superblock row: lane half lh takes the
+// codes k = 32*ks + 16*lh + e of every K step ks; weight 128h + 32u + 16lh
+// + e is nibble u/2 of low byte 64h + 32(u%2) + 16lh + e with bits 2u, 2u+1
+// of high byte 32h + 16lh + e, and its scale is that of 16-weight sub-block
+// 8h + 2u + lh.
+struct Lane6 {
     uint4 l[4], hq[2], sc;
     uint32_t d;
 };
 
-__device__ inline void load_lane(Lane<KQ_Q4_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb,
-                                 int lh)
-{
-    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 128 + 32 * c + 16 * lh);
-}
-__device__ inline void load_lane(Lane<KQ_Q5_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb,
-                                 int lh)
-{
-    r.h = *reinterpret_cast<const uint4 *>(w + pl.off[0] + sb * 16);
-    r.qh = *reinterpret_cast<const uint4 *>(w + pl.off[1] + sb * 32 + 16 * lh);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint4 *>(w + pl.off[2] + sb * 128 + 32 * c + 16 * lh);
-}
-__device__ inline void load_lane(Lane<KQ_Q6_K> &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb,
-                                 int lh)
+__device__ inline void load_lane(Lane6 &r, const uint8_t *__restrict__ w, const Planes &pl, int64_t sb, int lh)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -94,31 +65,17 @@ __device__ inline void load_lane(Lane<KQ_Q6_K> &r, const uint8_t *__restrict__ w
 __device__ inline uint32_t word(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 // Q6_K digits (B operands) of K step ks of the lane's half row
-template <int FMT>
-__device__ inline void digits_ks(const Lane<FMT> &r, int ks, int lh, i32x4 &bh, i32x4 &bl)
+__device__ inline void digits_ks(const Lane6 &r, int ks, int lh, i32x4 &bh, i32x4 &bl)
 {
     uint32_t h[4], l[4];
-    if constexpr (FMT == KQ_Q6_K) {
-        const int hh = ks >> 2, u = ks & 3;
-        const int sc = (int8_t)byte_of(word(r.sc, (2 * ks + lh) >> 2), (2 * ks + lh) & 3);
+    const int hh = ks >> 2, u = ks & 3;
+    const int sc = (int8_t)byte_of(word(r.sc, (2 * ks + lh) >> 2), (2 * ks + lh) & 3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lw = word(r.l[2 * hh + (u & 1)], i);
-            const uint32_t nib = (u >> 1) ? (lw >> 4) & 0x0F0F0F0Fu : lw & 0x0F0F0F0Fu;
-            const uint32_t q = nib | (((word(r.hq[hh], i) >> (2 * u)) & 0x03030303u) << 4);
-            digits_q6(q, sc, h[i], l[i]);
-        }
-    } else {
-        const int c = ks >> 1;
-        int sc, m;
-        scale_min_6bit(r.h.y, r.h.z, r.h.w, ks, sc, m);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t qw = word(r.q[c], i);
-            uint32_t q = (ks & 1) ? (qw >> 4) & 0x0F0F0F0Fu : qw & 0x0F0F0F0Fu;
-            if constexpr (FMT == KQ_Q5_K) q |= ((word(r.qh, i) >> ks) & 0x01010101u) << 4;
-            digits_q45(q, sc, h[i], l[i]);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lw = word(r.l[2 * hh + (u & 1)], i);
+        const uint32_t nib = (u >> 1) ? (lw >> 4) & 0x0F0F0F0Fu : lw & 0x0F0F0F0Fu;
+        const uint32_t q = nib | (((word(r.hq[hh], i) >> (2 * u)) & 0x03030303u) << 4);
+        digits_q6(q, sc, h[i], l[i]);
     }
     bh = i32x4{(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
     bl = i32x4{(int)l[0], (int)l[1], (int)l[2], (int)l[3]};
@@ -132,19 +89,35 @@ __device__ inline int item_of_mid(int b, int G)
 
 }  // namespace
 
+// Q6_K form: each lane unpacks its own half superblock row straight into
+// MFMA B-operand registers (no LDS panel, no barriers); its 16-weight
+// sub-blocks do not match a K step, so the signed sub-scale is folded into
+// two digit passes (kq_digits.h), high and low digit in two accumulators.
 template <int FMT, bool GROUPED, bool PART>
 __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     const uint8_t *__restrict__ w, int64_t w_stride, const int32_t *__restrict__ tile_expert, int experts, int64_t n,
     int nsb, const int8_t *__restrict__ xq, const float *__restrict__ xs, const _Float16 *__restrict__ xbs,
     int64_t mtok, float *__restrict__ y, int32_t *__restrict__ Pout, int32_t *__restrict__ Mout, int mtiles, int S)
 {
+    static_assert(FMT == KQ_Q6_K, "Q4_K/Q5_K use the LDS-panel form");
     __shared__ __align__(16) float d8w[4][32];
 
     // item = (128-row panel, 32-token tile, K split): the token tiles of a
     // panel run on one XCD and share its L2 copy of the panel's planes
     const int item = item_of_mid(blockIdx.x, gridDim.x);
     const int tile = item / S, split = item - tile * S;
-    const int nt = tile / mtiles, mt = tile - nt * mtiles;
+    // grouped: the 128-row panels of one 32-token tile (one expert) run
+    // together, so they share that tile's codes and the expert's planes in
+    // L2; otherwise the token tiles of one panel run together and share it
+    int nt, mt;
+    if constexpr (GROUPED) {
+        const int ntiles = (int)((n + 127) / 128);
+        mt = tile / ntiles;
+        nt = tile - mt * ntiles;
+    } else {
+        nt = tile / mtiles;
+        mt = tile - nt * mtiles;
+    }
     const int s0 = (int)((int64_t)nsb * split / S), s1 = (int)((int64_t)nsb * (split + 1) / S);
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
     const int64_t row0 = (int64_t)nt * 128 + wv * 32;
@@ -162,35 +135,27 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     const Planes pl = planes_of(FMT, n, nsb);
     const int64_t wrow = (rvalid ? row : n - 1) * nsb;
 
-    // the tile's 32 tokens of codes and f16 bsums (tile image) and d8s
+    // the tile's 32 tokens of codes (tile image) and d8s; Q6_K has no min
+    // term, so the bsums are not read
+    (void)xbs;
     const int64_t mpad = (mtok + 31) & ~(int64_t)31;
     const uint64_t a_bytes = (uint64_t)(mpad - m0) * (uint64_t)K;
-    const uint64_t b_bytes = (uint64_t)(mpad - m0) * (uint64_t)nsb * 32;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(xq + m0 * K), 0, (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(xbs + m0 * nsb * 16), 0, (int)(uint32_t)(b_bytes < 0xFFFFFFFFu ? b_bytes : 0xFFFFFFFFu),
-        0x00020000);
     const int64_t td = m0 + lr;  // token whose d8 this lane stages
     const float *xs_row = xs + (td < mtok ? td : mtok - 1) * nsb;
 
     i32x4 A[8];
-    f16x8 Ab;
-    Lane<FMT> raw, nxt;
+    Lane6 raw, nxt;
     float d8v;
     auto load_a = [&](int s, int ks) {
-        A[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, (s * 8 + ks) * 1024 + 16 * lane, 0, 0));
-    };
-    auto load_bs = [&](int s) {
-        if constexpr (FMT != KQ_Q6_K)
-            Ab = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, s * 1024 + 16 * lane, 0, 0));
+        A[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, 16 * lane, (s * 8 + ks) * 1024, 0));
     };
 
     f32x16 accf = f32x16{};
     load_lane(raw, wb, pl, wrow + s0, lh);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) load_a(s0, ks);
-    load_bs(s0);
     d8v = td < mtok ? xs_row[s0] : 0.0f;
 
     for (int s = s0; s < s1; ++s) {
@@ -203,80 +168,31 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
         if (lh == 0) d8w[wv][lr] = d8v;
         load_lane(nxt, wb, pl, wrow + sn, lh);
         d8v = td < mtok ? xs_row[sn] : 0.0f;
-        float dv, dm = 0.0f;
-        f32x16 mf;
-        i32x16 P;
-        if constexpr (FMT == KQ_Q6_K) {
-            // 16-weight sub-blocks: the scale is folded into the two digit
-            // passes (kq_digits.h)
-            i32x16 acch = i32x16{}, accl = i32x16{};
+        // 16-weight sub-blocks: the scale is folded into the two digit
+        // passes (kq_digits.h)
+        i32x16 acch = i32x16{}, accl = i32x16{};
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                i32x4 bh, bl;
-                digits_ks<FMT>(raw, ks, lh, bh, bl);
-                acch = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bh, acch, 0, 0, 0);
-                accl = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bl, accl, 0, 0, 0);
-                load_a(sn, ks);
-            }
-            P = (acch << 7) + accl;
-            dv = rvalid ? f16_bits_to_float(raw.d) : 0.0f;
-        } else {
-            // 32-weight sub-blocks = one 32-deep K step: the raw quants are
-            // the B operand, dot_j comes out of one MFMA and the sub-scale is
-            // applied with one 24-bit integer mad per output (|dot_j| <=
-            // 31*127*32 < 2^23, |P| < 2^26): P = sum_j sc_j * dot_j exactly
-            const uint32_t s0w = raw.h.y, s1w = raw.h.z, s2w = raw.h.w;
-            // the eight 6-bit scales and mins, four per word, as bytes
-            const uint32_t sc_lo = s0w & 0x3F3F3F3Fu;
-            const uint32_t sc_hi = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
-            const uint32_t m_lo = s1w & 0x3F3F3F3Fu;
-            const uint32_t m_hi = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
-            P = i32x16{};
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                i32x4 bq;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t qw = word(raw.q[ks >> 1], i);
-                    uint32_t q = (ks & 1) ? (qw >> 4) & 0x0F0F0F0Fu : qw & 0x0F0F0F0Fu;
-                    if constexpr (FMT == KQ_Q5_K) q |= ((word(raw.qh, i) >> ks) & 0x01010101u) << 4;
-                    bq[i] = (int)q;
-                }
-                const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bq, i32x16{}, 0, 0, 0);
-                const int sc = (int)byte_of(ks < 4 ? sc_lo : sc_hi, ks & 3);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) P[i] = __mul24(d[i], sc) + P[i];
-                load_a(sn, ks);
-            }
-            dv = rvalid ? f16_bits_to_float(raw.h.x & 0xFFFFu) : 0.0f;
-            dm = rvalid ? f16_bits_to_float(raw.h.x >> 16) : 0.0f;
-            // min term: B operand = m of the sub-block of bsums 8lh + 0..7
-            const uint32_t mw = lh ? m_hi : m_lo;
-            f16x8 bm;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bm[2 * j] = bm[2 * j + 1] = (_Float16)(int)byte_of(mw, j);
-            mf = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab, bm, f32x16{}, 0, 0, 0);
-            load_bs(sn);
+        for (int ks = 0; ks < 8; ++ks) {
+            i32x4 bh, bl;
+            digits_ks(raw, ks, lh, bh, bl);
+            acch = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bh, acch, 0, 0, 0);
+            accl = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bl, accl, 0, 0, 0);
+            load_a(sn, ks);
         }
+        const i32x16 P = (acch << 7) + accl;
+        const float dv = rvalid ? f16_bits_to_float(raw.d) : 0.0f;
         __builtin_amdgcn_wave_barrier();
         // lane holds tokens 8*(i/4) + 4*lh + i%4, i = 0..15, of row `row`
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int tl = 8 * (i >> 2) + 4 * lh + (i & 3);
-            const float Pf = (float)P[i];
-            float u;
-            if constexpr (FMT == KQ_Q6_K) u = dv * Pf;
-            else u = fmaf(dv, Pf, -(dm * mf[i]));
-            accf[i] = fmaf(d8w[wv][tl], u, accf[i]);
+            accf[i] = fmaf(d8w[wv][tl], dv * (float)P[i], accf[i]);
             if (PART) {
                 const int64_t t = m0 + tl;
                 if (t < mtok && rvalid) {
                     const int64_t o = (t * n + row) * nsb + s;
                     Pout[o] = P[i];
-                    if (Mout) {
-                        if constexpr (FMT == KQ_Q6_K) Mout[o] = 0;
-                        else Mout[o] = (int)mf[i];
-                    }
+                    if (Mout) Mout[o] = 0;
                 }
             }
         }
@@ -286,6 +202,212 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
 
     // K split j of S writes slice j of y (y then points at the workspace)
     if (!rvalid) return;
+    float *yo = y + (int64_t)split * mtok * n;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t t = m0 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (t < mtok) yo[t * n + row] = accf[i];
+    }
+}
+
+// Q4_K/Q5_K form with an LDS weight panel.  The workgroup's 128 rows x one
+// superblock are fetched cooperatively, eight lanes per row (16 bytes each,
+// so every load instruction covers eight whole 128-byte lines), expanded to
+// one byte per quant into an LDS panel (row stride 272 bytes: the B-operand
+// reads of 32 rows hit distinct banks) with the decoded scales, mins and
+// d/dmin beside it, double-buffered with one barrier per superblock.  Each
+// wave then reads its 32 rows' B operands from LDS; the sub-scale is the
+// per-output integer mad of the register form.
+constexpr int MID_STRIDE = 272;
+
+template <int FMT, bool GROUPED, bool PART>
+__global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
+    const uint8_t *__restrict__ w, int64_t w_stride, const int32_t *__restrict__ tile_expert, int experts, int64_t n,
+    int nsb, const int8_t *__restrict__ xq, const float *__restrict__ xs, const _Float16 *__restrict__ xbs,
+    int64_t mtok, float *__restrict__ y, int32_t *__restrict__ Pout, int32_t *__restrict__ Mout, int mtiles, int S)
+{
+    static_assert(FMT != KQ_Q6_K, "Q6_K uses the register form");
+    __shared__ __align__(16) int8_t qp[2][128 * MID_STRIDE];
+    __shared__ __align__(16) uint32_t scw[2][128][2];  // 8 sub-scales per row, as bytes
+    __shared__ __align__(16) uint32_t mnw[2][128][2];  // 8 mins per row, as bytes
+    __shared__ float dd[2][128], dmm[2][128];
+    __shared__ __align__(16) float d8s[2][32];
+
+    const int item = item_of_mid(blockIdx.x, gridDim.x);
+    const int tile = item / S, split = item - tile * S;
+    // grouped: the 128-row panels of one 32-token tile (one expert) run
+    // together, so they share that tile's codes and the expert's planes in
+    // L2; otherwise the token tiles of one panel run together and share it
+    int nt, mt;
+    if constexpr (GROUPED) {
+        const int ntiles = (int)((n + 127) / 128);
+        mt = tile / ntiles;
+        nt = tile - mt * ntiles;
+    } else {
+        nt = tile / mtiles;
+        mt = tile - nt * mtiles;
+    }
+    const int s0 = (int)((int64_t)nsb * split / S), s1 = (int)((int64_t)nsb * (split + 1) / S);
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+    const int64_t n0 = (int64_t)nt * 128, m0 = (int64_t)mt * 32;
+    const uint8_t *wb = w;
+    if constexpr (GROUPED) {
+        const int e = tile_expert[mt];  // uniform over the workgroup
+        if (e < 0 || e >= experts) return;
+        wb += (int64_t)e * w_stride;
+    }
+    const int64_t K = (int64_t)nsb * QK;
+    const Planes pl = planes_of(FMT, n, nsb);
+
+    // panel fetch: thread covers 16 bytes (chunk tid%8) of the quant rows
+    // 32j + tid/8, j = 0..3; threads 0..127 also take row tid's header
+    const int chunk = tid & 7, rsub = tid >> 3;
+    int64_t qrow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t r = n0 + 32 * j + rsub;
+        qrow[j] = (r < n ? r : n - 1) * nsb;
+    }
+    const int64_t hr = n0 + (tid & 127);
+    const bool hvalid = hr < n;
+    const int64_t hrow = (hvalid ? hr : n - 1) * nsb;
+    uint4 rq[4], rqh[4], rh;
+    auto fetch = [&](int s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            rq[j] = *reinterpret_cast<const uint4 *>(wb + pl.off[FMT == KQ_Q5_K ? 2 : 1] + (qrow[j] + s) * 128 + 16 * chunk);
+            if constexpr (FMT == KQ_Q5_K)
+                rqh[j] = *reinterpret_cast<const uint4 *>(wb + pl.off[1] + (qrow[j] + s) * 32 + 16 * (chunk & 1));
+        }
+        rh = *reinterpret_cast<const uint4 *>(wb + pl.off[0] + (hrow + s) * 16);
+    };
+    const int64_t td = m0 + (tid & 31);
+    const float *xs_row = xs + (td < mtok ? td : mtok - 1) * nsb;
+    float d8v = 0.0f;
+    // expand the fetched bytes into panel buffer b: quant byte 32c + b of a
+    // row holds weight 64c + b (low nibble) and 64c + 32 + b (high nibble)
+    auto stage = [&](int b) {
+        const int c = chunk >> 1, b0 = 16 * (chunk & 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t q[4] = {rq[j].x, rq[j].y, rq[j].z, rq[j].w};
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo[i] = q[i] & 0x0F0F0F0Fu;
+                hi[i] = (q[i] >> 4) & 0x0F0F0F0Fu;
+                if constexpr (FMT == KQ_Q5_K) {
+                    const uint32_t hb = i == 0 ? rqh[j].x : i == 1 ? rqh[j].y : i == 2 ? rqh[j].z : rqh[j].w;
+                    lo[i] |= ((hb >> (2 * c)) & 0x01010101u) << 4;
+                    hi[i] |= ((hb >> (2 * c + 1)) & 0x01010101u) << 4;
+                }
+            }
+            int8_t *row = qp[b] + (32 * j + rsub) * MID_STRIDE + 64 * c + b0;
+            *reinterpret_cast<uint4 *>(row) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint4 *>(row + 32) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        }
+        if (tid < 128) {
+            // rows past n: scales, mins and d masked to zero
+            const uint32_t vm = hvalid ? 0xFFFFFFFFu : 0u;
+            const uint32_t s0w = rh.y & vm, s1w = rh.z & vm, s2w = rh.w & vm;
+            scw[b][tid][0] = s0w & 0x3F3F3F3Fu;
+            scw[b][tid][1] = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
+            mnw[b][tid][0] = s1w & 0x3F3F3F3Fu;
+            mnw[b][tid][1] = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
+            dd[b][tid] = f16_bits_to_float(rh.x & vm & 0xFFFFu);
+            dmm[b][tid] = f16_bits_to_float((rh.x & vm) >> 16);
+        }
+        if (tid < 32) d8s[b][tid] = td < mtok ? d8v : 0.0f;
+    };
+
+    // the tile's 32 tokens of codes and f16 bsums (tile image)
+    const int64_t mpad = (mtok + 31) & ~(int64_t)31;
+    const uint64_t a_bytes = (uint64_t)(mpad - m0) * (uint64_t)K;
+    const uint64_t b_bytes = (uint64_t)(mpad - m0) * (uint64_t)nsb * 32;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xq + m0 * K), 0, (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xbs + m0 * nsb * 16), 0, (int)(uint32_t)(b_bytes < 0xFFFFFFFFu ? b_bytes : 0xFFFFFFFFu),
+        0x00020000);
+    i32x4 A[8];
+    f16x8 Ab;
+    auto load_a = [&](int s, int ks) {
+        A[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, 16 * lane, (s * 8 + ks) * 1024, 0));
+    };
+    auto load_bs = [&](int s) {
+        Ab = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, 16 * lane, s * 1024, 0));
+    };
+
+    fetch(s0);
+    d8v = xs_row[s0];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) load_a(s0, ks);
+    load_bs(s0);
+    stage(0);
+    {
+        const int sn = s0 + 1 < s1 ? s0 + 1 : s0;
+        fetch(sn);
+        d8v = xs_row[sn];
+    }
+    __syncthreads();
+
+    const int rl = 32 * wv + lr;  // this lane's panel row
+    const int64_t row = n0 + rl;
+    f32x16 accf = f32x16{};
+    for (int s = s0; s < s1; ++s) {
+        const int b = (s - s0) & 1;
+        const int sn = s + 1 < s1 ? s + 1 : s1 - 1, sn2 = s + 2 < s1 ? s + 2 : s1 - 1;
+        const uint2 scv = *reinterpret_cast<const uint2 *>(scw[b][rl]);
+        i32x16 P = i32x16{};
+        const int8_t *brow = qp[b] + rl * MID_STRIDE + 16 * lh;
+        i32x4 Bc = *reinterpret_cast<const i32x4 *>(brow);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            // the next K step's B operand is read before this step's mads
+            i32x4 Bn = Bc;
+            if (ks + 1 < 8) Bn = *reinterpret_cast<const i32x4 *>(brow + 32 * (ks + 1));
+            const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], Bc, i32x16{}, 0, 0, 0);
+            const int sc = (int)byte_of(ks < 4 ? scv.x : scv.y, ks & 3);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) P[i] = __mul24(d[i], sc) + P[i];
+            load_a(sn, ks);
+            // keep the K steps in order (MFMA, its mads, then the next
+            // step): left to itself the compiler issues all eight MFMAs
+            // first and holds their 8 x 16 results live
+            asm volatile("" : "+v"(P), "+v"(Bn)::"memory");
+            Bc = Bn;
+        }
+        // min term: B operand = m of the sub-block of bsums 8lh + 0..7
+        const uint32_t mw = *reinterpret_cast<const uint32_t *>(&mnw[b][rl][lh]);
+        f16x8 bm;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bm[2 * j] = bm[2 * j + 1] = (_Float16)(int)byte_of(mw, j);
+        const f32x16 mf = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab, bm, f32x16{}, 0, 0, 0);
+        load_bs(sn);
+        const float dv = dd[b][rl], dm = dmm[b][rl];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int tl = 8 * (i >> 2) + 4 * lh + (i & 3);
+            const float u = fmaf(dv, (float)P[i], -(dm * mf[i]));
+            accf[i] = fmaf(d8s[b][tl], u, accf[i]);
+            if (PART) {
+                const int64_t t = m0 + tl;
+                if (t < mtok && row < n) {
+                    const int64_t o = (t * n + row) * nsb + s;
+                    Pout[o] = P[i];
+                    if (Mout) Mout[o] = (int)mf[i];
+                }
+            }
+        }
+        // superblock s+1 into the other buffer (its last readers passed the
+        // previous barrier), then fetch s+2
+        stage(b ^ 1);
+        fetch(sn2);
+        d8v = xs_row[sn2];
+        __syncthreads();
+    }
+
+    if (row >= n) return;
     float *yo = y + (int64_t)split * mtok * n;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -321,12 +443,21 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
 {
     const int64_t ntiles = (n + 127) / 128, mtiles = (m + 31) / 32;
     const dim3 g((unsigned)(ntiles * mtiles * S)), b(256);
-    if (part)
-        hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, true>), g, b, 0, st, w, w_stride, tile_expert, experts, n,
-                           nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
-    else
-        hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, false>), g, b, 0, st, w, w_stride, tile_expert, experts, n,
-                           nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+    if constexpr (FMT == KQ_Q6_K) {
+        if (part)
+            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, true>), g, b, 0, st, w, w_stride, tile_expert, experts, n,
+                               nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+        else
+            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, false>), g, b, 0, st, w, w_stride, tile_expert, experts,
+                               n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+    } else {
+        if (part)
+            hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, true>), g, b, 0, st, w, w_stride, tile_expert,
+                               experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+        else
+            hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, false>), g, b, 0, st, w, w_stride, tile_expert,
+                               experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+    }
 }
 
 template <bool GROUPED>
