@@ -63,8 +63,8 @@ BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 # it was measured on; with any other sources the roofline reports null.
 GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "dbc622837506cdc1",
                 "bytes_per_launch": 17422042}
-GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "c93cf9ede3148534",
-                "bytes_per_launch": 79880411}
+GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "37bc4ac9c4805fe4",
+                "bytes_per_launch": 78662833}
 
 
 def src_hash(files):
@@ -191,7 +191,7 @@ def bench_mid(mats, copies, reps, stream, capture, ev):
     return {"tokens": MID_M, "per_matrix": res,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBPS, "traffic": None,
-                         "kernel": "kq::gemm_mid_kernel (kq_gemm, m <= 127)",
+                         "kernel": "kq::gemm_mid_lds_kernel (Q4_K, Q5_K) / kq::gemm_mid_kernel (Q6_K) (kq_gemm, m <= 127)",
                          "avg_launch_us": kus_total / len(mats)}}
 
 
@@ -261,7 +261,7 @@ def bench_moe(reps, stream, capture, ev):
             "useful_TOPS": useful / (gemm_us * 1e-6) / 1e12,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBPS, "traffic": None,
-                         "kernel": "kq::gemm_mid_kernel (kq_gemm_grouped), gate|up + down launches",
+                         "kernel": "kq::gemm_mid_lds_kernel (kq_gemm_grouped), gate|up + down launches",
                          "avg_launch_us": gemm_us / 2}}
 
 
@@ -502,7 +502,7 @@ def main():
         out["roofline_gemm"] = {"bound": "mfma", "achieved": ach, "peak": MFMA_I8_PEAK_TOPS, "unit": "TOPS",
                                 "frac": ach / MFMA_I8_PEAK_TOPS, "traffic": measured_traffic(GEMM_TRAFFIC),
                                 "algorithmic_bytes_per_launch": gemm_alg,
-                                "kernel": "kq::gemm_kernel (+ kq::sum_splits for W_down)",
+                                "kernel": "kq::gemm_kernel (+ kq::sum_tile_splits for W_down)",
                                 "avg_launch_us": kms * 1e3 / (reps["gemm"] * len(mats))}
         for j, (f, n, k, _) in enumerate(mats):
             us = krec["gemm"][j][0].elapsed_time(krec["gemm"][j][1]) * 1e3 / reps["gemm"]
