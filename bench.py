@@ -61,10 +61,10 @@ BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 # profiles/kq_gemm_hbm_traffic_qwen3_4b_ffn_pp512.md; the GEMM figure is one
 # kq_gemm call, split-sum pass included).  Each holds only for the sources
 # it was measured on; with any other sources the roofline reports null.
-GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "dbc622837506cdc1",
-                "bytes_per_launch": 17422042}
-GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "37bc4ac9c4805fe4",
-                "bytes_per_launch": 78662833}
+GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "bcf1079a9e69f449",
+                "bytes_per_launch": 17425486}
+GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "f3269408910c538a",
+                "bytes_per_launch": 74726499}
 
 
 def src_hash(files):
@@ -502,7 +502,7 @@ def main():
         out["roofline_gemm"] = {"bound": "mfma", "achieved": ach, "peak": MFMA_I8_PEAK_TOPS, "unit": "TOPS",
                                 "frac": ach / MFMA_I8_PEAK_TOPS, "traffic": measured_traffic(GEMM_TRAFFIC),
                                 "algorithmic_bytes_per_launch": gemm_alg,
-                                "kernel": "kq::gemm_kernel (+ kq::sum_tile_splits for W_down)",
+                                "kernel": "kq::gemm_kernel (W_down split along k, parts added in-kernel)",
                                 "avg_launch_us": kms * 1e3 / (reps["gemm"] * len(mats))}
         for j, (f, n, k, _) in enumerate(mats):
             us = krec["gemm"][j][0].elapsed_time(krec["gemm"][j][1]) * 1e3 / reps["gemm"]

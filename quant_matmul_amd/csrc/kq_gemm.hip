@@ -45,6 +45,8 @@
 // as soon as it is dead.  The loop body is one basic block (no divergent
 // branch: validity is masked, every refill is unconditional), so the
 // scheduler can interleave all of it.  One barrier per superblock.
+#include <atomic>
+
 #include "kq_common.h"
 #include "kq_digits.h"
 
@@ -192,7 +194,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                                                       const _Float16 *__restrict__ xbs, int64_t mtok,
                                                       float *__restrict__ y, int32_t *__restrict__ Pout,
                                                       int32_t *__restrict__ Mout, int mtiles, int full, int TS,
-                                                      float *__restrict__ ws)
+                                                      float *__restrict__ ws, unsigned long long *__restrict__ cnt,
+                                                      unsigned long long seq)
 {
     constexpr int BM = 256, BN = 32;
     static_assert(BN * 8 == 256, "one 32-weight unpack task per thread");
@@ -204,8 +207,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
 
     // Workgroups 0..full-1 each run one whole tile and write y; the rest run
     // the remaining tiles split along K in TS parts (split j covers
-    // superblocks [s0, s1)) and write partial tiles to ws.  The whole tiles
-    // come first in dispatch order, so the split ones fill the tail.
+    // superblocks [s0, s1)) and write partial tiles to ws; the last part of
+    // a tile to finish adds them up.  The whole tiles come first in dispatch
+    // order, so split ones would fill the tail (the plan splits only grids
+    // smaller than one round, so full is 0 whenever TS > 1).
     int tile, split = 0, S = 1;
     if ((int)blockIdx.x < full) {
         tile = item_of(blockIdx.x, full);
@@ -368,14 +373,56 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
     }
 
     if (S > 1) {
-        // partial tile (lane-major: element r of tile mi of wave wm at
-        // ((wm*32 + mi*16 + r) * 64 + lane)), summed by sum_tile_splits
-        float *part = ws + ((int64_t)(tile - full) * S + split) * (BM * BN);
+        // Split tile: publish this part (lane-major: element r of tile mi of
+        // wave wm at ((wm*32 + mi*16 + r) * 64 + lane)) with agent-scope
+        // stores, which write through to memory all XCDs see, wait for them,
+        // then count the part in.  The counter word holds (seq << 16 | parts
+        // in); a word of another call (any other seq, or garbage) counts as
+        // zero, and the last part resets it to (seq, 0) for graph replays of
+        // the same call.  No part waits for another: the last to arrive
+        // (whichever it is) reads the others back, again at agent scope, so
+        // it sees memory rather than a stale line of its own L2, and adds
+        // all parts in split order -- deterministic.
+        float *part = ws + (int64_t)(tile - full) * S * (BM * BN);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) part[((wm * 32 + mi * 16 + r) << 6) + lane] = accf[mi][r];
-        return;
+            for (int r = 0; r < 16; ++r)
+                __hip_atomic_store(part + split * (BM * BN) + ((wm * 32 + mi * 16 + r) << 6) + lane, accf[mi][r],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        __shared__ int last_part;
+        if (tid == 0) {
+            unsigned long long *c = cnt + (tile - full);
+            const unsigned long long tag = seq & 0xFFFFFFFFFFFFull;
+            unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), nv;
+            do {  // at most S-1 retries: each failure is another part's success
+                const unsigned long long in = (old >> 16) == tag ? (old & 0xFFFF) : 0;
+                nv = (tag << 16) | (in + 1);
+            } while (!__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT));
+            const bool last = (int)(nv & 0xFFFF) == S;
+            if (last) __hip_atomic_store(c, tag << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_part = last;
+        }
+        __syncthreads();
+        if (!last_part) return;
+        f32x16 sum[2];
+        for (int j = 0; j < S; ++j) {
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float v = j == split ? accf[mi][r]
+                                               : __hip_atomic_load(part + j * (BM * BN) +
+                                                                       ((wm * 32 + mi * 16 + r) << 6) + lane,
+                                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    sum[mi][r] = j == 0 ? v : sum[mi][r] + v;
+                }
+        }
+        accf[0] = sum[0];
+        accf[1] = sum[1];
     }
     const int64_t col = n0 + l32;
     if (col < n) {
@@ -387,26 +434,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                 if (t < mtok) y[t * n + col] = accf[mi][r];
             }
     }
-}
-
-// The split tiles' outputs: y = ((p_0 + p_1) + p_2) + ... over the TS
-// partial tiles, in split order; one thread per output of a split tile.
-__global__ __launch_bounds__(256) void sum_tile_splits(const float *__restrict__ ws, int TS, int full, int ntail,
-                                                       int mtiles, int64_t n, int64_t mtok, float *__restrict__ y)
-{
-    constexpr int E = 256 * 32;  // outputs per tile
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (int64_t)ntail * E) return;
-    const int st = (int)(gid / E), e = (int)(gid - (int64_t)st * E);
-    const float *p = ws + (int64_t)st * TS * E + e;
-    float acc = p[0];
-    for (int j = 1; j < TS; ++j) acc += p[(int64_t)j * E];
-    const int lane = e & 63, idx = e >> 6;  // idx = wm*32 + mi*16 + r
-    const int wm = idx >> 5, mi = (idx >> 4) & 1, r = idx & 15;
-    const int tile = full + st, nt = tile / mtiles, mt = tile - nt * mtiles;
-    const int64_t t = (int64_t)mt * 256 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    const int64_t col = (int64_t)nt * 32 + (lane & 31);
-    if (t < mtok && col < n) y[t * n + col] = acc;
 }
 
 // y = ((p_0 + p_1) + p_2) + ... over S whole-output partial slices p_j of
@@ -430,14 +457,15 @@ void launch_sum_splits(const float *p, int S, int64_t count, float *y, hipStream
 // Grid plan.  `slots` = workgroups resident at once (two per CU at this
 // kernel's occupancy).  A grid of at least `slots` tiles runs unsplit.  A
 // smaller one (W_down at pp512: 160 tiles) is split along K into up to 8
-// parts of at least 3 superblocks.  The split tiles' partial sums go to the
-// caller's workspace and sum_tile_splits adds them in split order:
-// deterministic, and with no cross-workgroup signalling (on MI355X a
-// device-scope fence writes back and invalidates the whole L2 of the XCD,
-// which costs more than the pass).  The kernel also takes a grid whose
-// whole rounds run unsplit and only the last partial round is split, but
-// measured on the pp512 W_up grid (608 tiles) that was no faster, so the
-// plan does not use it.
+// parts of at least 3 superblocks so that it fills the chip.  The parts meet
+// through the caller's workspace: a small array of counter words, then the
+// partial tiles.  A separate summing pass cost more (it re-reads every
+// partial from memory in a second launch), and a device-scope fence writes
+// back and invalidates the whole L2 of the XCD, so only the partial tiles
+// and the counters use coherent (agent-scope) accesses.  Splitting just the
+// last, partial round of a larger grid (W_up: 608 tiles on 512 slots) was
+// measured too: the parts' fill and hand-over cost what the shorter tail
+// saved, so such grids stay unsplit.
 struct Plan {
     int full, tail, TS;
 };
@@ -463,25 +491,30 @@ static Plan plan_of(int64_t n, int64_t m, int nsb)
     return Plan{(int)(tiles - tail), (int)tail, TS};
 }
 
+// counter words (one per split tile, 256-byte rounded), then the partials
+static size_t counter_bytes(const Plan &p) { return ((size_t)p.tail * 8 + 255) / 256 * 256; }
+
 size_t gemm_workspace_bytes(int64_t n, int64_t k, int64_t m)
 {
     const Plan p = plan_of(n, m, (int)(k / QK));
-    return (size_t)p.tail * p.TS * 256 * 32 * 4;
+    return p.tail == 0 ? 0 : counter_bytes(p) + (size_t)p.tail * p.TS * 256 * 32 * 4;
 }
 
 template <int FMT>
 static void launch_fmt(bool part, int64_t n, int nsb, const uint8_t *w, const int8_t *xq, const float *xs,
-                       const _Float16 *xbs, int64_t m, float *y, int32_t *P, int32_t *M, const Plan &pl, float *ws,
-                       hipStream_t st)
+                       const _Float16 *xbs, int64_t m, float *y, int32_t *P, int32_t *M, const Plan &pl, void *ws,
+                       unsigned long long seq, hipStream_t st)
 {
+    unsigned long long *cnt = (unsigned long long *)ws;
+    float *parts = pl.tail ? (float *)((char *)ws + counter_bytes(pl)) : nullptr;
     const int64_t mtiles = (m + 255) / 256;
     const dim3 g((unsigned)(pl.full + (int64_t)pl.tail * pl.TS)), b(256);
     if (part)
         hipLaunchKernelGGL((gemm_kernel<FMT, true>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles,
-                           pl.full, pl.TS, ws);
+                           pl.full, pl.TS, parts, cnt, seq);
     else
         hipLaunchKernelGGL((gemm_kernel<FMT, false>), g, b, 0, st, w, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles,
-                           pl.full, pl.TS, ws);
+                           pl.full, pl.TS, parts, cnt, seq);
 }
 
 int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -495,15 +528,12 @@ int launch_gemm(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
     // split only with a workspace large enough (and never for the partials)
     Plan pl = plan_of(n, m, nsb);
     if (part || !ws || ws_bytes < gemm_workspace_bytes(n, k, m) || pl.tail == 0) pl = Plan{pl.full + pl.tail, 0, 1};
-    float *wsf = (float *)ws;
-    if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, wsf, st);
-    else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, wsf, st);
-    else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, wsf, st);
-    if (pl.tail > 0) {
-        const int64_t cnt = (int64_t)pl.tail * 256 * 32;
-        hipLaunchKernelGGL(sum_tile_splits, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, (const float *)wsf,
-                           pl.TS, pl.full, pl.tail, (int)((m + 255) / 256), n, m, y);
-    }
+    // a fresh tag per call for the split counters (48 bits used)
+    static std::atomic<unsigned long long> calls{1};
+    const unsigned long long seq = pl.tail ? calls.fetch_add(1, std::memory_order_relaxed) : 0;
+    if (fmt == KQ_Q4_K) launch_fmt<KQ_Q4_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, ws, seq, st);
+    else if (fmt == KQ_Q5_K) launch_fmt<KQ_Q5_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, ws, seq, st);
+    else launch_fmt<KQ_Q6_K>(part, n, nsb, wb, xq, xs, bt, m, y, P, M, pl, ws, seq, st);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 

@@ -156,13 +156,15 @@ __device__ inline float dpp_f(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// One workgroup = 16/SL rows x all superblocks.  A wave step covers SL
-// adjacent superblocks of each of its 16/SL rows (quad q = sig + SL*rho of
-// the wave: superblock slot sig, row rho), so small-n matrices still spread
-// over many workgroups; the waves of a workgroup take contiguous runs of
-// `per_wave` steps, U steps at a time with every weight load of the U issued
-// before the first is consumed.  The SL slot sums of a row meet by DPP
-// mirrors, the waves' sums in LDS.
+// One workgroup = RGS row groups of 16/SL rows x all superblocks.  A wave
+// step covers SL adjacent superblocks of each of its group's 16/SL rows
+// (quad q = sig + SL*rho of the wave: superblock slot sig, row rho), so
+// small-n matrices still spread over many waves; the kw waves of a row
+// group take contiguous runs of `per_wave` steps, U steps at a time with
+// every weight load of the U issued before the first is consumed.  The SL
+// slot sums of a row meet by DPP mirrors, the kw waves' sums in LDS.  The
+// activation image is staged (or, fused, quantised) once per workgroup, so
+// a workgroup of several row groups pays for it once.
 //
 // FUSE (batch <= 2): the workgroup quantises the f32 activation x itself
 // into its LDS stage (the same per-chunk arithmetic as kq_quantize_q8k, so
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
                                                     const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                     const int16_t *__restrict__ xbs, float *__restrict__ y,
                                                     int32_t *__restrict__ Pout, int32_t *__restrict__ Mout,
-                                                    int per_wave, const float *__restrict__ x,
+                                                    int per_wave, int kw, const float *__restrict__ x,
                                                     int8_t *__restrict__ oq, float *__restrict__ os,
                                                     int16_t *__restrict__ obs)
 {
@@ -185,7 +187,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
     const int nw = blockDim.x >> 6;
     const int c = lane & 3, quad = lane >> 2;
     const int sig = quad % SL, rho = quad / SL;
-    const int64_t row = (int64_t)blockIdx.x * RPW + rho;
+    // several row groups per workgroup only when fused (the plain GEMV runs
+    // one, and keeps its first weight loads free of the division)
+    const int rgs = FUSE ? nw / kw : 1, rgi = FUSE ? wave / kw : 0, kwi = FUSE ? wave - rgi * kw : wave;
+    const int64_t row = ((int64_t)blockIdx.x * rgs + rgi) * RPW + rho;
     const bool valid = row < n;
     const int64_t K = (int64_t)nsb * QK, KB = K / 16;
     const Planes pl = planes_of(FMT, n, nsb);
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
     for (int t = 0; t < T; ++t) acc[t] = 0.0f;
 
     const int nsteps = (nsb + SL - 1) / SL;
-    const int j_begin = wave * per_wave;
+    const int j_begin = kwi * per_wave;
     const int j_end = min(nsteps, j_begin + per_wave);
     // this lane's superblock at step j, clamped in bounds (out-of-range
     // slots re-read a valid superblock and contribute nothing)
@@ -342,12 +347,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
         for (int t = 0; t < T; ++t) red[wave][t][rho] = acc[t];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < RPW * T; i += blockDim.x) {
-        const int t = i / RPW, r = i % RPW;
-        const int64_t rr = (int64_t)blockIdx.x * RPW + r;
+    const int rows_wg = rgs * RPW;
+    for (int i = threadIdx.x; i < rows_wg * T; i += blockDim.x) {
+        const int t = i / rows_wg, rl = i - t * rows_wg;
+        const int rg = rl / RPW, r = rl - rg * RPW;
+        const int64_t rr = (int64_t)blockIdx.x * rows_wg + rl;
         if (rr < n) {
+            // the kw partial sums in wave order, whatever the group count
             float v = 0.0f;
-            for (int wv = 0; wv < nw; ++wv) v += red[wv][t][r];
+            for (int kk = 0; kk < kw; ++kk) v += red[rg * kw + kk][t][r];
             y[t * n + rr] = v;
         }
     }
@@ -362,7 +370,7 @@ struct GemvArgs {
     const int16_t *xbs;
     float *y;
     int32_t *P, *M;
-    int per_wave;
+    int per_wave, kw;
     const float *x;  // fused: f32 activations, and the optional image out
     int8_t *oq;
     float *os;
@@ -378,12 +386,12 @@ static void launch_one(dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
         if (a.x) {
             lds += (size_t)T * a.nsb * sizeof(float);
             hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, true>), g, b, lds, st, a.w, a.n, a.nsb, a.xq,
-                               a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.x, a.oq, a.os, a.obs);
+                               a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
             return;
         }
     }
     hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false>), g, b, lds, st, a.w, a.n, a.nsb, a.xq, a.xs,
-                       a.xbs, a.y, a.P, a.M, a.per_wave, a.x, a.oq, a.os, a.obs);
+                       a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
 }
 
 template <int FMT, int T>
@@ -423,11 +431,18 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
                 const float *x, int8_t *oq, float *os, int16_t *obs)
 {
     const int64_t nsb = k / QK;
+    // the fused kernel runs exactly when launch_one picks it
+    const bool fused = x != nullptr && t <= 2 && P == nullptr;
     // 16 rows per workgroup when that gives two or more workgroups per CU,
     // else 4 rows x 4 adjacent superblocks per wave step
     // (the fused path keeps the same shape, so its y is bit-identical to
     // quantise-then-GEMV)
     const int sl = t <= 2 ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
+    // Row groups per workgroup (below).  Staging a read-only image costs a
+    // workgroup little, so the plain GEMV keeps one group per workgroup (the
+    // finest grain); the fused GEMV quantises the whole activation in every
+    // workgroup, so it groups rows down to about two workgroups per CU.
+    const int64_t min_wg = fused ? 512 : 0;
     const int64_t groups = (n + 16 / sl - 1) / (16 / sl);
     const int64_t nsteps = (nsb + sl - 1) / sl;
     // about 16 waves per CU in flight, at most 16 waves per workgroup, and
@@ -436,11 +451,17 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
     nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
     nw = nw > nsteps ? nsteps : nw;
     const int64_t per_wave = (nsteps + nw - 1) / nw;
-    nw = (nsteps + per_wave - 1) / per_wave;
+    const int64_t kw = (nsteps + per_wave - 1) / per_wave;
+    // Row groups per workgroup: doubled while the workgroup stays within 16
+    // waves and the grid keeps at least min_wg workgroups.  Each row's sum
+    // order depends only on kw and per_wave, so y does not change with the
+    // grouping.
+    int64_t rgs = 1;
+    while (min_wg > 0 && 2 * rgs * kw <= 16 && (groups + 2 * rgs - 1) / (2 * rgs) >= min_wg) rgs *= 2;
     const int umax = sl == 4 ? 2 : 4;
     const int u = per_wave >= umax ? umax : (int)per_wave;
-    GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave, x, oq, os, obs};
-    const dim3 g((unsigned)groups), b((unsigned)(64 * nw));
+    GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave, (int)kw, x, oq, os, obs};
+    const dim3 g((unsigned)((groups + rgs - 1) / rgs)), b((unsigned)(64 * kw * rgs));
     const bool part = P != nullptr;
     if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, sl, u, part, g, b, st, a);
     else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, sl, u, part, g, b, st, a);

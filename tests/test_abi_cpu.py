@@ -83,9 +83,11 @@ def test_gemm_argument_checks():
 def test_gemm_workspace_bytes():
     # on 256 CUs (2 x 256 workgroup slots; a host without a GPU assumes 256):
     # W_down at pp512 (160 tiles of 256 x 32) splits all its tiles in 3,
-    # W_up (608 tiles, more than one round) runs unsplit
+    # W_up (608 tiles, more than one round) runs unsplit; the workspace is one
+    # 8-byte counter per split tile (rounded up to 256 bytes), then the
+    # partial tiles
     tile = 256 * 32 * 4
-    assert kq.kq_gemm_workspace_bytes("q6_k", 2560, 9728, 512) == 160 * 3 * tile
+    assert kq.kq_gemm_workspace_bytes("q6_k", 2560, 9728, 512) == 1280 + 160 * 3 * tile
     assert kq.kq_gemm_workspace_bytes("q4_k", 9728, 2560, 512) == 0
     assert kq.kq_gemm_workspace_bytes("q4_k", 8192, 2560, 512) == 0  # exactly one round
     # the 32-token tile (m <= 127): S = 3 partial slices of the m x n output

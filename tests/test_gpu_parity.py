@@ -232,6 +232,34 @@ def test_gemm_pp512_full_size_sampled(fmt, n, k):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k,m", [(640, 2560, 300), (96, 2560, 512)])
+def test_gemm_split_parts_meet_through_any_workspace(fmt, n, k, m):
+    # (640, 2560, 300): 40 tiles; (96, 2560, 512): 6 tiles, whose parts run
+    # on different XCDs (the XCD-blocked order has runs of one part there).
+    # Every tile is split along k in 3 parts; the last part of each tile to
+    # finish adds the others; the
+    # counters are tagged per call, so a workspace holding garbage or another
+    # call's counters and parts gives the same bits as a zeroed one.
+    c = Case(fmt, n, k, m, seed=14)
+    nbytes = kq.kq_gemm_workspace_bytes(fmt, n, k, m)
+    nbytes2 = kq.kq_gemm_workspace_bytes(fmt, 200, 2560, 256)
+    assert nbytes > 0 and nbytes2 > 0
+    ws = torch.zeros(max(nbytes, nbytes2) + 65536, dtype=torch.uint8, device="cuda")
+    y0 = ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=ws)
+    check_y(c, y0, sample_rows(n) if n > 2048 else None)
+    ws.random_(0, 256)
+    assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
+    for _ in range(2):
+        assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
+    # another split call in the same workspace, then this one again
+    c2 = Case(fmt, 200, 2560, 256, seed=15)
+    check_y(c2, ops.gemm(fmt, c2.planes, 200, 2560, c2.q8t, workspace=ws))
+    assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
+    # unsplit: the same outputs within the fold's float tolerance
+    check_y(c, ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=None), sample_rows(n) if n > 2048 else None)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
 @pytest.mark.parametrize("m", [16, 96])
 def test_gemm_mid_full_size_sampled(fmt, n, k, m):
