@@ -35,6 +35,12 @@ matrices) and `moe` (a mixture-of-experts layer: 128 Q4_K experts of gate|up
 1536 x 2048 and down 2048 x 768, 512 tokens routed top-8 by seeded U(0,1)
 logits, gather-quantise + kq_gemm_grouped for each projection).  Both are
 bound by the weight bytes, so their rooflines are in GB/s of HBM.
+`layers` runs every matmul of one decode token and of one 512-token prefill
+through a 36-layer Qwen3-4B-shaped set (q, k, v, o, gate, up, down; 2.3 GB
+of weights), and `probes` measures this machine's achievable ceilings -- a
+plain streaming read of the same plane buffers and a plain int8 MFMA loop --
+which `roofline.achievable` / `roofline_gemm.achievable` set beside the
+datasheet peaks.
 """
 from __future__ import annotations
 
@@ -61,8 +67,8 @@ BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 # profiles/kq_gemm_hbm_traffic_qwen3_4b_ffn_pp512.md; the GEMM figure is one
 # kq_gemm call, split-sum pass included).  Each holds only for the sources
 # it was measured on; with any other sources the roofline reports null.
-GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "bcf1079a9e69f449",
-                "bytes_per_launch": 17425486}
+GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "c34040b09438b960",
+                "bytes_per_launch": 17417286}
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "f3269408910c538a",
                 "bytes_per_launch": 74726499}
 
@@ -98,7 +104,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
-    ap.add_argument("--legs", default="gemv,gemm,mid,moe", help="which legs to run")
+    ap.add_argument("--legs", default="gemv,gemm,mid,moe,probes,layers", help="which legs to run")
     ap.add_argument("--side-reps", type=int, default=20,
                     help="replays of the gemm_mid / moe graphs (after the timed steps)")
     ap.add_argument("--profile-one", metavar="KIND:FMT:N:K:T",
@@ -139,6 +145,55 @@ def cpu_baseline(seconds):
                       f"Q4_K/Q5_K/Q6_K W_up/W_down matrices (Q8_K quantise included), "
                       f"{t_used:.1f} s of single-thread CPU time",
             "seconds": t_used}
+
+
+def bench_probes(mats, copies, stream, capture, ev):
+    """Achievable ceilings on this machine (include/kq_probe.h): a plain
+    streaming read of each matrix's plane buffers, rotated over the same
+    weight copies the GEMV reads, and a plain int8 32x32x32 MFMA loop."""
+    import torch
+    import quant_matmul_amd as kq
+    sink = torch.zeros(65536 * 256, dtype=torch.int32, device="cuda")
+    reps = 8 * copies
+    read = []
+    for fmt, n, k, pl in mats:
+        nbytes = pl[0].numel()
+        best = None
+        for grid in (1024, 2048, 4096, 8192):
+            def run(grid=grid):
+                for r in range(reps):
+                    kq.kq_probe_read(pl[r % copies], nbytes, sink, grid)
+            g = capture(run)
+            g.replay()
+            a, b = ev(), ev()
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            if best is None or us < best[0]:
+                best = (us, grid)
+        read.append({"matrix": f"{fmt}_{n}x{k}", "bytes": nbytes, "us": best[0], "grid": best[1],
+                     "GBps": nbytes / (best[0] * 1e-6) / 1e9})
+    read_gbps = sum(r["bytes"] for r in read) / (sum(r["us"] for r in read) * 1e-6) / 1e9
+    mfma = []
+    iters = 2048
+    for grid in (512, 1024, 2048):
+        def run(grid=grid):
+            for _ in range(4):
+                kq.kq_probe_mfma_i8(iters, grid, sink)
+        g = capture(run)
+        g.replay()
+        a, b = ev(), ev()
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / 4
+        ops = grid * 4 * iters * 4 * 65536
+        mfma.append({"grid": grid, "waves_per_simd": grid // 256, "us": us, "TOPS": ops / (us * 1e-6) / 1e12})
+    return {"read_GBps": read_gbps, "read_per_matrix": read,
+            "mfma_i8_TOPS": max(m["TOPS"] for m in mfma), "mfma_i8_runs": mfma}
 
 
 def bench_mid(mats, copies, reps, stream, capture, ev):
@@ -263,6 +318,86 @@ def bench_moe(reps, stream, capture, ev):
                          "frac": ach / HBM_PEAK_GBPS, "traffic": None,
                          "kernel": "kq::gemm_mid_lds_kernel (kq_gemm_grouped), gate|up + down launches",
                          "avg_launch_us": gemm_us / 2}}
+
+
+# The Qwen3-4B-shaped layer set: (name, format, n, k, input), 36 layers.
+# Matrices with the same input read one shared Q8_K image, as a model does.
+LAYER_SET = [("q", "q4_k", 4096, 2560, "attn"), ("k", "q4_k", 1024, 2560, "attn"),
+             ("v", "q6_k", 1024, 2560, "attn"), ("o", "q4_k", 2560, 4096, "o"),
+             ("gate", "q4_k", 9728, 2560, "ffn"), ("up", "q4_k", 9728, 2560, "ffn"),
+             ("down", "q6_k", 2560, 9728, "down")]
+LAYER_INPUTS = {"attn": 2560, "o": 4096, "ffn": 2560, "down": 9728}
+N_LAYERS = 36
+
+
+def bench_layers(reps, stream, capture, ev):
+    """Every matmul of one decode token (batch 1) and of one 512-token
+    prefill through the 36-layer Qwen3-4B-shaped set, in order on one stream:
+    per layer four quantisations (attention input, o input, FFN input, down
+    input) and seven GEMVs / GEMMs.  Only the matmuls run -- no attention,
+    norms or activation functions; the inputs are fixed seeded rows.  One
+    seeded layer is packed and copied to 36 distinct buffers (2.3 GB), so
+    the weights stream from HBM as in a real model."""
+    import torch
+
+    import synth
+    import quant_matmul_amd as kq
+    from quant_matmul_amd import torch_ops as ops
+
+    layer = []
+    for i, (name, fmt, n, k, inp) in enumerate(LAYER_SET):
+        planes = ops.pack(fmt, ops.upload_records(synth.weights(fmt, n, k, synth.seed_for(3, i))), n, k)
+        layer.append((name, fmt, n, k, inp, [planes] + [planes.clone() for _ in range(N_LAYERS - 1)]))
+    torch.cuda.synchronize()
+    x1 = {inp: torch.from_numpy(synth.activations(1, k, synth.seed_for(3, 100 + j))).cuda()
+          for j, (inp, k) in enumerate(LAYER_INPUTS.items())}
+    xm = {inp: torch.from_numpy(synth.activations(GEMM_M, k, synth.seed_for(3, 110 + j))).cuda()
+          for j, (inp, k) in enumerate(LAYER_INPUTS.items())}
+    q1 = {inp: ops.q8k_buffers(1, k) for inp, k in LAYER_INPUTS.items()}
+    qm = {inp: ops.q8k_tile_buffers(GEMM_M, k) for inp, k in LAYER_INPUTS.items()}
+    y1 = [torch.empty((1, n), device="cuda") for _, _, n, _, _, _ in layer]
+    ym = [torch.empty((GEMM_M, n), device="cuda") for _, _, n, _, _, _ in layer]
+    wss = [ops.gemm_workspace(fmt, n, k, GEMM_M) for _, fmt, n, k, _, _ in layer]
+
+    def decode():
+        for L in range(N_LAYERS):
+            for j, (name, fmt, n, k, inp, pl) in enumerate(layer):
+                if j == 0 or inp != layer[j - 1][4]:
+                    kq.kq_quantize_q8k(x1[inp], 1, k, *q1[inp])
+                kq.kq_gemv(fmt, pl[L], n, k, *q1[inp], 1, y1[j])
+
+    def prefill():
+        for L in range(N_LAYERS):
+            for j, (name, fmt, n, k, inp, pl) in enumerate(layer):
+                if j == 0 or inp != layer[j - 1][4]:
+                    kq.kq_quantize_q8k_tiles(xm[inp], GEMM_M, k, *qm[inp])
+                kq.kq_gemm(fmt, pl[L], n, k, *qm[inp], GEMM_M, ym[j], wss[j])
+
+    res = {}
+    for kind, fn, nrep in (("decode", decode, reps), ("prefill", prefill, max(2, reps // 4))):
+        g = capture(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(nrep):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[kind] = a.elapsed_time(b) * 1e3 / nrep  # us per pass
+    wbytes = N_LAYERS * sum(n * (k // 256) * BYTES[fmt] for _, fmt, n, k, _, _ in layer)
+    ops_prefill = N_LAYERS * sum(2 * GEMM_M * n * k for _, _, n, k, _, _ in layer)
+    dec_alg = wbytes + N_LAYERS * (sum(292 * k // 256 for k in LAYER_INPUTS.values())
+                                   + 4 * sum(n for _, _, n, _, _, _ in layer))
+    return {"config": {"layers": N_LAYERS, "matrices": [[nm, f, n, k] for nm, f, n, k, _, _ in layer],
+                       "weight_bytes": wbytes, "prefill_tokens": GEMM_M},
+            "decode_us_per_token": res["decode"],
+            "decode_GBps": dec_alg / (res["decode"] * 1e-6) / 1e9,
+            "decode_frac_hbm": dec_alg / (res["decode"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "decode_launches_per_token": N_LAYERS * (len(layer) + len(LAYER_INPUTS)),
+            "prefill_us": res["prefill"],
+            "prefill_TOPS": ops_prefill / (res["prefill"] * 1e-6) / 1e12,
+            "prefill_frac_mfma": ops_prefill / (res["prefill"] * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS}
 
 
 def profile_one(spec, reps):
@@ -509,6 +644,21 @@ def main():
             per.setdefault(f"{f}_{n}x{k}", {})["gemm"] = {
                 "us": us, "TOPS": 2 * GEMM_M * n * k / (us * 1e-6) / 1e12}
     out["per_matrix"] = per
+    if "probes" in legs:
+        pr = bench_probes(mats, copies, stream, capture, ev)
+        out["probes"] = pr
+        if "roofline" in out:
+            out["roofline"]["achievable"] = {
+                "value": pr["read_GBps"], "unit": "GB/s", "frac": out["roofline"]["achieved"] / pr["read_GBps"],
+                "probe": "kq_probe_read: plain 16-byte streaming read of the same plane buffers"}
+        if "roofline_gemm" in out:
+            t = pr["mfma_i8_TOPS"]
+            out["roofline_gemm"]["achievable"] = {
+                "value": t, "unit": "TOPS", "frac": out["roofline_gemm"]["achieved"] / t,
+                "useful_ceiling_two_digit_passes": t / 2,
+                "probe": "kq_probe_mfma_i8: independent v_mfma_i32_32x32x32_i8 chains"}
+    if "layers" in legs:
+        out["layers"] = bench_layers(args.side_reps, stream, capture, ev)
     if "mid" in legs:
         out["gemm_mid"] = bench_mid(mats, copies, args.side_reps, stream, capture, ev)
     if "moe" in legs:

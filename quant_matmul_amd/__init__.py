@@ -24,11 +24,11 @@ KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 4, 5, 6
 FORMATS = {"q4_k": KQ_Q4_K, "q5_k": KQ_Q5_K, "q6_k": KQ_Q6_K}
 KQ_OK, KQ_EINVAL, KQ_EFORMAT, KQ_EALIGN, KQ_ELAUNCH = 0, -1, -2, -3, -4
 
-# every entry point of include/kq.h
+# every entry point of include/kq.h and include/kq_probe.h
 SYMBOLS = ("kq_record_bytes", "kq_packed_bytes", "kq_pack", "kq_unpack", "kq_quantize_q8k",
            "kq_q8k_tiles_bytes", "kq_quantize_q8k_tiles", "kq_quantize_q8k_tiles_gather", "kq_gemv",
            "kq_gemv_f32", "kq_gemm_workspace_bytes", "kq_gemm", "kq_gemm_grouped", "kq_gemv_partials",
-           "kq_gemm_partials", "kq_strerror")
+           "kq_gemm_partials", "kq_strerror", "kq_probe_read", "kq_probe_mfma_i8")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python quant_matmul_amd/build.py`")
@@ -54,11 +54,13 @@ lib.kq_gemm.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, ctypes.c
 lib.kq_gemv_f32.argtypes = [_int, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
 lib.kq_gemv_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
 lib.kq_gemm_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
+lib.kq_probe_read.argtypes = [_p, ctypes.c_size_t, _p, _int, _p]
+lib.kq_probe_mfma_i8.argtypes = [_i64, _int, _p, _p]
 lib.kq_strerror.argtypes = [_int]
 lib.kq_strerror.restype = ctypes.c_char_p
 for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_quantize_q8k_tiles", "kq_quantize_q8k_tiles_gather",
            "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemm_grouped",
-           "kq_gemv_partials", "kq_gemm_partials"):
+           "kq_gemv_partials", "kq_gemm_partials", "kq_probe_read", "kq_probe_mfma_i8"):
     getattr(lib, _f).restype = _int
 
 
@@ -170,3 +172,13 @@ def kq_gemm_partials(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y
 
 def kq_strerror(code: int) -> str:
     return lib.kq_strerror(code).decode()
+
+
+def kq_probe_read(buf, nbytes: int, sink, grid: int, stream=None):
+    """Streaming-read probe (include/kq_probe.h): reads nbytes at buf once."""
+    _ok(lib.kq_probe_read(_ptr(buf), nbytes, _ptr(sink), grid, _stream(stream)), "kq_probe_read")
+
+
+def kq_probe_mfma_i8(iters: int, grid: int, sink, stream=None):
+    """Matrix-core probe (include/kq_probe.h): grid*4*iters*4 int8 32x32x32 MFMAs."""
+    _ok(lib.kq_probe_mfma_i8(iters, grid, _ptr(sink), _stream(stream)), "kq_probe_mfma_i8")

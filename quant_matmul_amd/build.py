@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
-SOURCES = ["kq_api.hip", "kq_quantize.hip", "kq_pack.hip", "kq_gemv.hip", "kq_gemm.hip", "kq_gemm_mid.hip"]
+SOURCES = ["kq_api.hip", "kq_quantize.hip", "kq_pack.hip", "kq_gemv.hip", "kq_gemm.hip", "kq_gemm_mid.hip",
+           "kq_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,5 +1,5 @@
-"""CPU tier: libkq.so loads, exports every entry point include/kq.h
-declares, and rejects bad arguments with the documented status code before
+"""CPU tier: libkq.so loads, exports every entry point include/kq.h and
+include/kq_probe.h declare, and rejects bad arguments with the documented status code before
 any HIP call (so these run on a host without a GPU; no call here reaches a
 kernel launch)."""
 import os
@@ -10,7 +10,7 @@ import pytest
 import quant_matmul_amd as kq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kq.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("kq.h", "kq_probe.h")]
 
 GOOD16 = 0x10000   # fake but 16-byte aligned "device pointers": never dereferenced,
 GOOD16B = 0x20000  # every call below fails validation first
@@ -18,7 +18,7 @@ ODD = 0x10001
 
 
 def header_symbols():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", text)))
 
 
@@ -187,3 +187,15 @@ def test_strerror_and_python_error():
     with pytest.raises(kq.KqError) as e:
         kq.kq_gemv(9, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 1, GOOD16, stream=0)
     assert e.value.code == kq.KQ_EFORMAT
+
+
+def test_probe_arg_checks():
+    lib = kq.lib
+    assert lib.kq_probe_read(None, 1024, GOOD16, 256, None) == kq.KQ_EINVAL
+    assert lib.kq_probe_read(GOOD16, 1000, GOOD16, 256, None) == kq.KQ_EINVAL  # not a multiple of 16
+    assert lib.kq_probe_read(GOOD16, 1024, GOOD16, 0, None) == kq.KQ_EINVAL
+    assert lib.kq_probe_read(ODD, 1024, GOOD16, 256, None) == kq.KQ_EALIGN
+    assert lib.kq_probe_mfma_i8(0, 256, GOOD16, None) == kq.KQ_EINVAL
+    assert lib.kq_probe_mfma_i8(1 << 25, 256, GOOD16, None) == kq.KQ_EINVAL
+    assert lib.kq_probe_mfma_i8(10, 70000, GOOD16, None) == kq.KQ_EINVAL
+    assert lib.kq_probe_mfma_i8(10, 256, ODD, None) == kq.KQ_EALIGN
