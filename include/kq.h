@@ -28,8 +28,9 @@
  * Conventions shared by every entry point:
  *  - Buffers.  Every pointer argument except the host side of a copy is a
  *    DEVICE pointer on the current HIP device, owned by the caller.  The
- *    library allocates nothing and keeps no mutable global state; calls are
- *    reentrant.
+ *    library allocates nothing.  Its only global state is on the host: the
+ *    CU count, read once, and an atomic call counter that tags kq_gemm's
+ *    split counters; calls are reentrant and thread-safe.
  *  - Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  Every call only enqueues work and returns; nothing
  *    synchronises.  Outputs are fully overwritten.

@@ -472,12 +472,15 @@ struct Plan {
 
 static Plan plan_of(int64_t n, int64_t m, int nsb)
 {
-    static int cus = 0;
+    // the CU count, read once (an atomic, so concurrent first calls are safe)
+    static std::atomic<int> cus_once{0};
+    int cus = cus_once.load(std::memory_order_relaxed);
     if (!cus) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             cus = 256;
+        cus_once.store(cus, std::memory_order_relaxed);
     }
     const int64_t slots = 2 * (int64_t)cus;
     const int64_t tiles = ((n + 31) / 32) * ((m + 255) / 256);

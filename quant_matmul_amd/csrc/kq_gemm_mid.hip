@@ -29,6 +29,8 @@
 // names the expert of every 32-row tile; its weights are the planes at
 // w_planes + expert * w_stride.  The page's MoE path fills one Q8_K image
 // for the gate and up projections ("The pieces", kq v2 item).
+#include <atomic>
+
 #include "kq_common.h"
 #include "kq_digits.h"
 
@@ -422,12 +424,15 @@ namespace {
 
 int pick_splits_mid(int64_t waves, int nsb)
 {
-    static int cus = 0;
+    // the CU count, read once (an atomic, so concurrent first calls are safe)
+    static std::atomic<int> cus_once{0};
+    int cus = cus_once.load(std::memory_order_relaxed);
     if (!cus) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             cus = 256;
+        cus_once.store(cus, std::memory_order_relaxed);
     }
     // about 8 resident waves per CU
     int S = (int)((8 * (int64_t)cus) / waves);

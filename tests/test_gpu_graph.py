@@ -22,7 +22,8 @@ def test_graph_replays_match_eager(fmt):
     q1, qm = ops.q8k_buffers(t, k), ops.q8k_tile_buffers(m, k)
     y1 = torch.empty((t, n), device="cuda")
     ym = torch.empty((m, n), device="cuda")
-    # a grid this small splits k (GEMM + split-sum kernels in the graph)
+    # a grid this small splits k: the parts meet through counter words in the
+    # workspace, tagged per call -- a replay reuses its captured tag
     ws = ops.gemm_workspace(fmt, n, k, m)
     assert ws is not None
 
@@ -47,6 +48,10 @@ def test_graph_replays_match_eager(fmt):
     for rep in range(4):
         for a in (*q1, *qm, y1, ym):
             a.zero_()  # eager work between replays
+        if rep == 2:
+            # an eager call (a new tag) on the same workspace between replays
+            kq.kq_gemm(fmt, planes, n, k, *qm, m, ym, ws)
+            ym.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
