@@ -138,8 +138,10 @@ int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
  * (commit message of that name) quantises inside the consuming chain at
  * whole-superblock granules -- here inside the GEMV, which saves the
  * separate quantiser launch and the image's round trip.  For t <= 2 this
- * is one kernel: every workgroup quantises x into LDS; xq/xs/xbs may then
- * be NULL (all three), or receive the Q8_K image.  For t > 2 the image
+ * is one kernel: every workgroup quantises x into LDS (a workgroup covers
+ * several row groups, down to about two workgroups per CU, so fewer of them
+ * repeat it); xq/xs/xbs may then be NULL (all three), or receive the Q8_K
+ * image.  y is bit-identical to kq_quantize_q8k then kq_gemv.  For t > 2 the image
  * buffers are required and the call runs kq_quantize_q8k then kq_gemv.
  * x must be 16-byte aligned and finite. */
 int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float *x, int64_t t,
@@ -160,10 +162,9 @@ size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
  * a grid too small to fill the GPU is split along k: for m >= 128 each
  * tile's parts write partial sums to the workspace and the last part of the
  * tile to finish adds them into y (one launch); for m <= 127 whole-output
- * slices that a second kernel adds.  Both add in
- * split order, so results are the same from call to call (they may differ
- * from the unsplit sum in the last bits, within the fold's float
- * tolerance).  The m >= 128 parts count in through counter words at the
+ * slices that a second kernel adds.  Both add in split order, so results
+ * are the same from call to call (they may differ from the unsplit sum in
+ * the last bits, within the fold's float tolerance).  The m >= 128 parts count in through counter words at the
  * start of the workspace that every call tags as its own, so stale contents
  * are ignored and graph replays may reuse the workspace.  Calls sharing one
  * workspace must be ordered on one stream.  A NULL or too small workspace
