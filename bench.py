@@ -71,6 +71,10 @@ GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "c3404
                 "bytes_per_launch": 17417286}
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "3444c4aae5ae0be1",
                 "bytes_per_launch": 74832664}
+MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
+               "src_sha256_16": "7007199ba676257e", "bytes_per_launch": 37279684}
+MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
+               "src_sha256_16": "bedb59a9a468eaa5", "bytes_per_launch": 229705304}
 
 
 def src_hash(files):
@@ -245,7 +249,8 @@ def bench_mid(mats, copies, reps, stream, capture, ev):
     ach = kb_total / (kus_total * 1e-6) / 1e9
     return {"tokens": MID_M, "per_matrix": res,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic(MID_TRAFFIC),
+                         "algorithmic_bytes_per_launch": kb_total / len(mats),
                          "kernel": "kq::gemm_mid_lds_kernel (Q4_K, Q5_K) / kq::gemm_mid_kernel (Q6_K) (kq_gemm, m <= 127)",
                          "avg_launch_us": kus_total / len(mats)}}
 
@@ -315,7 +320,8 @@ def bench_moe(reps, stream, capture, ev):
             "weight_GBps": layer_bytes / (gemm_us * 1e-6) / 1e9,
             "useful_TOPS": useful / (gemm_us * 1e-6) / 1e12,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic(MOE_TRAFFIC),
+                         "algorithmic_bytes_per_launch": alg / 2,
                          "kernel": "kq::gemm_mid_lds_kernel (kq_gemm_grouped), gate|up + down launches",
                          "avg_launch_us": gemm_us / 2}}
 
