@@ -19,9 +19,14 @@ def test_graph_replays_match_eager(fmt):
     planes = ops.pack(fmt, ops.upload_records(synth.weights(fmt, n, k, 21)), n, k)
     x1 = torch.from_numpy(synth.activations(t, k, 22)).cuda()
     xm = torch.from_numpy(synth.activations(m, k, 23)).cuda()
-    q1, qm = ops.q8k_buffers(t, k), ops.q8k_tile_buffers(m, k)
+    ms = 40  # the 32-token tile, also split along k
+    xs_ = torch.from_numpy(synth.activations(ms, k, 24)).cuda()
+    q1, qm, qs = ops.q8k_buffers(t, k), ops.q8k_tile_buffers(m, k), ops.q8k_tile_buffers(ms, k)
     y1 = torch.empty((t, n), device="cuda")
     ym = torch.empty((m, n), device="cuda")
+    ys = torch.empty((ms, n), device="cuda")
+    wss = ops.gemm_workspace(fmt, n, k, ms)
+    assert wss is not None
     # a grid this small splits k: the parts meet through counter words in the
     # workspace, tagged per call -- a replay reuses its captured tag
     ws = ops.gemm_workspace(fmt, n, k, m)
@@ -32,10 +37,12 @@ def test_graph_replays_match_eager(fmt):
         kq.kq_gemv(fmt, planes, n, k, *q1, t, y1)
         kq.kq_quantize_q8k_tiles(xm, m, k, *qm)
         kq.kq_gemm(fmt, planes, n, k, *qm, m, ym, ws)
+        kq.kq_quantize_q8k_tiles(xs_, ms, k, *qs)
+        kq.kq_gemm(fmt, planes, n, k, *qs, ms, ys, wss)
 
     seq()
     torch.cuda.synchronize()
-    ref = [a.clone() for a in (*q1, *qm, y1, ym)]
+    ref = [a.clone() for a in (*q1, *qm, y1, ym, ys)]
 
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -46,7 +53,7 @@ def test_graph_replays_match_eager(fmt):
     with torch.cuda.graph(g):
         seq()
     for rep in range(4):
-        for a in (*q1, *qm, y1, ym):
+        for a in (*q1, *qm, y1, ym, ys):
             a.zero_()  # eager work between replays
         if rep == 2:
             # an eager call (a new tag) on the same workspace between replays
@@ -55,5 +62,5 @@ def test_graph_replays_match_eager(fmt):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip((*q1, *qm, y1, ym), ref):
+        for a, b in zip((*q1, *qm, y1, ym, ys), ref):
             assert torch.equal(a, b), f"replay {rep} differs from eager"

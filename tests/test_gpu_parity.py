@@ -232,14 +232,17 @@ def test_gemm_pp512_full_size_sampled(fmt, n, k):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("n,k,m", [(640, 2560, 300), (96, 2560, 512)])
+@pytest.mark.parametrize("n,k,m", [(640, 2560, 300), (96, 2560, 512), (640, 2560, 64), (300, 2560, 40)])
 def test_gemm_split_parts_meet_through_any_workspace(fmt, n, k, m):
-    # (640, 2560, 300): 40 tiles; (96, 2560, 512): 6 tiles, whose parts run
-    # on different XCDs (the XCD-blocked order has runs of one part there).
-    # Every tile is split along k in 3 parts; the last part of each tile to
-    # finish adds the others; the
-    # counters are tagged per call, so a workspace holding garbage or another
-    # call's counters and parts gives the same bits as a zeroed one.
+    # 256-token tile: (640, 2560, 300): 40 tiles; (96, 2560, 512): 6 tiles,
+    # whose parts run on different XCDs (the XCD-blocked order has runs of
+    # one part there); every tile split along k in 3 parts, the last part of
+    # each tile to finish adds the others.  32-token tile: (640, 2560, 64)
+    # and (300, 2560, 40, ragged rows and tokens) split along k in 5
+    # whole-output slices that a second kernel adds.  The 256-token tile's
+    # counters are tagged per call, so for either tile a workspace holding
+    # garbage or another call's counters and parts gives the same bits as a
+    # zeroed one.
     c = Case(fmt, n, k, m, seed=14)
     nbytes = kq.kq_gemm_workspace_bytes(fmt, n, k, m)
     nbytes2 = kq.kq_gemm_workspace_bytes(fmt, 200, 2560, 256)
