@@ -305,3 +305,16 @@ def test_repeat_runs_are_bitwise_identical(kind):
         assert ws is not None
         ys = [ops.gemm("q6_k", c.planes, n, k, c.q8t, workspace=ws) for _ in range(3)]
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+
+
+# ------------------------------------------------------- long rows ------
+@pytest.mark.parametrize("fmt", FMTS)
+def test_long_k_all_kernels(fmt):
+    # k = 65536 (256 superblocks per row): the large offsets of every path --
+    # GEMV (batch 1 and 5), the 32-token tile (40 tokens, k split) and the
+    # 256-token tile (130 tokens, k split in 8)
+    n, k = 40, 65536
+    for t, kind in ((1, "gemv"), (5, "gemv"), (40, "gemm"), (130, "gemm")):
+        c = Case(fmt, n, k, t, seed=90 + t)
+        y = ops.gemv(fmt, c.planes, n, k, c.q8) if kind == "gemv" else ops.gemm(fmt, c.planes, n, k, c.q8t)
+        check_y(c, y)
