@@ -40,7 +40,10 @@ through a 36-layer Qwen3-4B-shaped set (q, k, v, o, gate, up, down; 2.3 GB
 of weights), and `probes` measures this machine's achievable ceilings -- a
 plain streaming read of the same plane buffers and a plain int8 MFMA loop --
 which `roofline.achievable` / `roofline_gemm.achievable` set beside the
-datasheet peaks.
+datasheet peaks.  `dense` runs the large dense projections (17408 x 5120 and
+its transpose, Q4_K and Q6_K, 50-73 MB each) through the GEMV at batch 1 and
+the GEMM at 512 tokens, beside a plain streaming read of the same buffers:
+the same kernels at a size where a launch's fixed cost weighs less.
 """
 from __future__ import annotations
 
@@ -58,6 +61,8 @@ SHAPES = ((9728, 2560), (2560, 9728))  # (n, k): W_up, W_down
 GEMM_M = 512
 MID_M = 64
 MOE = {"experts": 128, "tokens": 512, "top": 8, "hidden": 2048, "ffn": 768, "fmt": "q4_k"}
+# the large dense projections (17408 x 5120 and its transpose) in Q4_K and Q6_K
+DENSE = (("q4_k", 17408, 5120), ("q4_k", 5120, 17408), ("q6_k", 17408, 5120), ("q6_k", 5120, 17408))
 BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 
 
@@ -108,7 +113,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
-    ap.add_argument("--legs", default="gemv,gemm,mid,moe,probes,layers", help="which legs to run")
+    ap.add_argument("--legs", default="gemv,gemm,mid,moe,probes,layers,dense", help="which legs to run")
     ap.add_argument("--side-reps", type=int, default=20,
                     help="replays of the gemm_mid / moe graphs (after the timed steps)")
     ap.add_argument("--profile-one", metavar="KIND:FMT:N:K:T",
@@ -253,6 +258,81 @@ def bench_mid(mats, copies, reps, stream, capture, ev):
                          "algorithmic_bytes_per_launch": kb_total / len(mats),
                          "kernel": "kq::gemm_mid_lds_kernel (Q4_K, Q5_K) / kq::gemm_mid_kernel (Q6_K) (kq_gemm, m <= 127)",
                          "avg_launch_us": kus_total / len(mats)}}
+
+
+def bench_dense(pool_gib, reps, stream, capture, ev):
+    """The large dense projections at decode batch 1 (GEMV) and 512-token
+    prefill (GEMM), each matrix in enough copies that a rotation reads more
+    than the 256 MB last-level cache holds, beside a plain streaming read of
+    the same plane buffers.  At 50-73 MB per matrix the fixed cost of a
+    launch weighs far less than on the 14-20 MB FFN matrices."""
+    import torch
+
+    import synth
+    import quant_matmul_amd as kq
+    from quant_matmul_amd import torch_ops as ops
+
+    sink = torch.zeros(65536 * 256, dtype=torch.int32, device="cuda")
+    res = {}
+    tot = {"gemv_bytes": 0, "gemv_us": 0.0, "read_us": 0.0, "gemm_ops": 0, "gemm_us": 0.0}
+    for j, (fmt, n, k) in enumerate(DENSE):
+        planes = ops.pack(fmt, ops.upload_records(synth.weights(fmt, n, k, synth.seed_for(4, j))), n, k)
+        wb = n * (k // 256) * BYTES[fmt]
+        copies = max(2, -(-int(pool_gib * (1 << 30)) // wb))
+        pl = [planes] + [planes.clone() for _ in range(copies - 1)]
+        x1 = torch.from_numpy(synth.activations(1, k, synth.seed_for(4, 50 + j))).cuda()
+        xm = torch.from_numpy(synth.activations(GEMM_M, k, synth.seed_for(4, 60 + j))).cuda()
+        q1, qm = ops.quantize_q8k(x1), ops.quantize_q8k_tiles(xm)
+        y1 = torch.empty((1, n), device="cuda")
+        ym = torch.empty((GEMM_M, n), device="cuda")
+        ws = ops.gemm_workspace(fmt, n, k, GEMM_M)
+        nbytes = pl[0].numel()
+
+        def gemv_run():
+            for r in range(copies):
+                kq.kq_gemv(fmt, pl[r], n, k, *q1, 1, y1)
+
+        def read_run():
+            for r in range(copies):
+                kq.kq_probe_read(pl[r], nbytes, sink, 4096)
+
+        def gemm_run():
+            for r in range(copies):
+                kq.kq_gemm(fmt, pl[r], n, k, *qm, GEMM_M, ym, ws)
+
+        out = {}
+        for name, fn in (("gemv", gemv_run), ("read", read_run), ("gemm", gemm_run)):
+            g = capture(fn)
+            g.replay()
+            a, b = ev(), ev()
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            out[name] = a.elapsed_time(b) * 1e3 / (reps * copies)
+        gbytes = wb + (k // 256) * 292 + 4 * n
+        ops_ = 2 * GEMM_M * n * k
+        res[f"{fmt}_{n}x{k}"] = {"gemv_us": out["gemv"], "gemv_GBps": gbytes / (out["gemv"] * 1e-6) / 1e9,
+                                 "read_us": out["read"], "read_GBps": nbytes / (out["read"] * 1e-6) / 1e9,
+                                 "gemm_us": out["gemm"], "gemm_TOPS": ops_ / (out["gemm"] * 1e-6) / 1e12,
+                                 "weight_copies": copies}
+        tot["gemv_bytes"] += gbytes
+        tot["gemv_us"] += out["gemv"]
+        tot["read_us"] += out["read"]
+        tot["gemm_ops"] += ops_
+        tot["gemm_us"] += out["gemm"]
+        del pl, planes
+        torch.cuda.empty_cache()
+    ach = tot["gemv_bytes"] / (tot["gemv_us"] * 1e-6) / 1e9
+    gem = tot["gemm_ops"] / (tot["gemm_us"] * 1e-6) / 1e12
+    return {"per_matrix": res,
+            "gemv_roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": ach / HBM_PEAK_GBPS, "kernel": "kq::gemv_kernel (kq_gemv, batch 1)",
+                              "avg_launch_us": tot["gemv_us"] / len(DENSE)},
+            "gemm_roofline": {"bound": "mfma", "achieved": gem, "peak": MFMA_I8_PEAK_TOPS, "unit": "TOPS",
+                              "frac": gem / MFMA_I8_PEAK_TOPS, "kernel": "kq::gemm_kernel (kq_gemm, 512 tokens)",
+                              "avg_launch_us": tot["gemm_us"] / len(DENSE)}}
 
 
 def bench_moe(reps, stream, capture, ev):
@@ -708,6 +788,8 @@ def main():
         out["gemm_mid"] = bench_mid(mats, copies, args.side_reps, stream, capture, ev)
     if "moe" in legs:
         out["moe"] = bench_moe(args.side_reps, stream, capture, ev)
+    if "dense" in legs:
+        out["dense"] = bench_dense(args.pool_gib, max(2, args.side_reps // 4), stream, capture, ev)
     if out["value"] is None and "gemm" in out:
         out["value"], out["unit"] = out["gemm"]["value"], "TOPS"
     if not args.no_cpu_baseline:
