@@ -141,8 +141,10 @@ int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
  * is one kernel: every workgroup quantises x into LDS (a workgroup covers
  * several row groups, down to about two workgroups per CU, so fewer of them
  * repeat it); xq/xs/xbs may then be NULL (all three), or receive the Q8_K
- * image.  y is bit-identical to kq_quantize_q8k then kq_gemv.  For t > 2 the image
- * buffers are required and the call runs kq_quantize_q8k then kq_gemv.
+ * image.  With the image buffers given and k > 4096, where that repeated
+ * quantisation costs more than a launch, the call runs kq_quantize_q8k then
+ * kq_gemv instead.  y is bit-identical to kq_quantize_q8k then kq_gemv.  For
+ * t > 2 the image buffers are required and the call runs the two launches.
  * x must be 16-byte aligned and finite. */
 int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float *x, int64_t t,
                 float *y, int8_t *xq, float *xs, int16_t *xbs, void *stream);

@@ -153,7 +153,13 @@ int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float
     if (t > 2 && !image) return KQ_EINVAL;              // batches past 2 need the image buffers
     if (!aligned(w_planes, 16) || !aligned(x, 16) || !aligned(y, 4)) return KQ_EALIGN;
     if (image && (!aligned(xq, 16) || !aligned(xbs, 16) || !aligned(xs, 4))) return KQ_EALIGN;
-    if (t <= 2)
+    // The one-kernel form re-quantises x in every workgroup.  Past 16
+    // superblocks that repeated work costs more than the quantiser launch it
+    // saves (k = 9728, batch 1: 11.4 us fused against 8.5 us for quantise +
+    // GEMV), so when the caller gives the image buffers such a call runs the
+    // two launches instead; y is the same bits either way.
+    constexpr int64_t FUSE_KMAX = 16 * 256;
+    if (t <= 2 && (!image || k <= FUSE_KMAX))
         return kq::launch_gemv(fmt, w_planes, n, k, nullptr, nullptr, nullptr, t, y, nullptr, nullptr,
                                (hipStream_t)stream, x, xq, xs, xbs);
     int rc = kq::launch_quantize_q8k(x, t, k, xq, xs, xbs, (hipStream_t)stream);
