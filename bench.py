@@ -74,10 +74,10 @@ BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 # it was measured on; with any other sources the roofline reports null.
 GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "c34040b09438b960",
                 "bytes_per_launch": 17417286}
-GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "3444c4aae5ae0be1",
-                "bytes_per_launch": 74832664}
+GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "11609855197ded27",
+                "bytes_per_launch": 74635230}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "7007199ba676257e", "bytes_per_launch": 37279684}
+               "src_sha256_16": "695a77e1d0e5c96b", "bytes_per_launch": 37280782}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
                "src_sha256_16": "bedb59a9a468eaa5", "bytes_per_launch": 229705304}
 

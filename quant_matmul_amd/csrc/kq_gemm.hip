@@ -39,10 +39,12 @@
 // the wave's codes sit in registers, the digit panel in one of two LDS
 // buffers; while the high-digit MFMAs of s run, the wave unpacks its share
 // of superblock s+1 (whose packed bytes were prefetched) into the other
-// buffer, so the VALU unpack overlaps the matrix pipe; the low-digit pass
-// runs tile by tile so that tile 0's float fold issues under tile 1's
-// MFMAs; each 32-deep K step of the codes is refilled with superblock s+1
-// as soon as it is dead.  The loop body is one basic block (no divergent
+// buffer, so the VALU unpack overlaps the matrix pipe; the low-digit passes
+// of the two tiles are interleaved, so two independent MFMA chains are in
+// flight there too (run tile by tile, each a single dependent chain, the
+// pass was 4-6% slower over the whole kernel even with tile 0's fold under
+// tile 1's MFMAs); each 32-deep K step of the codes is refilled with
+// superblock s+1 as soon as it is dead.  The loop body is one basic block (no divergent
 // branch: validity is masked, every refill is unconditional), so the
 // scheduler can interleave all of it.  One barrier per superblock.
 #include <atomic>
@@ -341,30 +343,23 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict_
                 }
             }
         };
-        // low-digit pass of tile 0; each 32-deep K step of its codes is
-        // refilled with superblock s+1 as soon as it is dead
+        // low-digit passes of both tiles interleaved (two independent MFMA
+        // chains), each K step's codes refilled with superblock s+1 once dead
         acc[0] = acc[0] << SHIFT;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + l32 * LDS_STRIDE + 32 * ks + 16 * lh);
-            acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0][ks], B, acc[0], 0, 0, 0);
-            A[0][ks] = __builtin_bit_cast(
-                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[0], (sn * 8 + ks) * 1024, 0));
-        }
-        // keep tile 1's MFMAs after tile 0's, so tile 0's fold can run under them
-        __builtin_amdgcn_sched_barrier(0);
-        // low-digit pass of tile 1, with tile 0's fold under its MFMAs
         acc[1] = acc[1] << SHIFT;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const i32x4 B = *reinterpret_cast<const i32x4 *>(wl[b] + l32 * LDS_STRIDE + 32 * ks + 16 * lh);
-            acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[1][ks], B, acc[1], 0, 0, 0);
-            A[1][ks] = __builtin_bit_cast(
-                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[1], (sn * 8 + ks) * 1024, 0));
-            fold(0, 2 * ks, mf0);
-            fold(0, 2 * ks + 1, mf0);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mi][ks], B, acc[mi], 0, 0, 0);
+                A[mi][ks] = __builtin_bit_cast(
+                    i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff[mi], (sn * 8 + ks) * 1024, 0));
+            }
         }
         if constexpr (FMT != KQ_Q6_K) mf1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab[1], Bm, f32x16{}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) fold(0, r, mf0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) fold(1, r, mf1);
         load_bs(sn);
