@@ -44,6 +44,8 @@ datasheet peaks.  `dense` runs the large dense projections (17408 x 5120 and
 its transpose, Q4_K and Q6_K, 50-73 MB each) through the GEMV at batch 1 and
 the GEMM at 512 tokens, beside a plain streaming read of the same buffers:
 the same kernels at a size where a launch's fixed cost weighs less.
+`gemv_batch` times the decode GEMV alone at batch 4 and 8 on the six FFN
+matrices, with its own rooflines.
 """
 from __future__ import annotations
 
@@ -72,8 +74,8 @@ BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 # profiles/kq_gemm_hbm_traffic_qwen3_4b_ffn_pp512.md; the GEMM figure is one
 # kq_gemm call, split-sum pass included).  Each holds only for the sources
 # it was measured on; with any other sources the roofline reports null.
-GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "c34040b09438b960",
-                "bytes_per_launch": 17417286}
+GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "73d65b37e9c630ee",
+                "bytes_per_launch": 17412658}
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "11609855197ded27",
                 "bytes_per_launch": 74635230}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
@@ -113,7 +115,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
-    ap.add_argument("--legs", default="gemv,gemm,mid,moe,probes,layers,dense", help="which legs to run")
+    ap.add_argument("--legs", default="gemv,gemm,mid,moe,probes,layers,dense,batch", help="which legs to run")
     ap.add_argument("--side-reps", type=int, default=20,
                     help="replays of the gemm_mid / moe graphs (after the timed steps)")
     ap.add_argument("--profile-one", metavar="KIND:FMT:N:K:T",
@@ -258,6 +260,49 @@ def bench_mid(mats, copies, reps, stream, capture, ev):
                          "algorithmic_bytes_per_launch": kb_total / len(mats),
                          "kernel": "kq::gemm_mid_lds_kernel (Q4_K, Q5_K) / kq::gemm_mid_kernel (Q6_K) (kq_gemm, m <= 127)",
                          "avg_launch_us": kus_total / len(mats)}}
+
+
+def bench_batch(mats, copies, reps, stream, capture, ev, batches=(4, 8)):
+    """The decode GEMV at batch 4 and 8 on the six FFN matrices (kq_gemv,
+    the Q8_K image quantised once beforehand), back-to-back launches over the
+    rotating weight copies: the kernel alone, as `roofline` times batch 1."""
+    import torch
+
+    import synth
+    import quant_matmul_amd as kq
+    from quant_matmul_amd import torch_ops as ops
+
+    res = {}
+    for t in batches:
+        per, tb, tus = {}, 0, 0.0
+        for j, (fmt, n, k, pl) in enumerate(mats):
+            x = torch.from_numpy(synth.activations(t, k, synth.seed_for(5, 10 * t + j))).cuda()
+            q = ops.quantize_q8k(x)
+            y = torch.empty((t, n), device="cuda")
+
+            def run():
+                for r in range(copies):
+                    kq.kq_gemv(fmt, pl[r], n, k, *q, t, y)
+
+            g = capture(run)
+            g.replay()
+            a, b = ev(), ev()
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / (reps * copies)
+            byts = gemv_bytes(fmt, n, k, t, fused=False)
+            per[f"{fmt}_{n}x{k}"] = {"us": us, "GBps": byts / (us * 1e-6) / 1e9}
+            tb += byts
+            tus += us
+        ach = tb / (tus * 1e-6) / 1e9
+        res[f"t{t}"] = {"per_matrix": per,
+                        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                     "frac": ach / HBM_PEAK_GBPS, "kernel": f"kq::gemv_kernel (kq_gemv, batch {t})",
+                                     "avg_launch_us": tus / len(mats)}}
+    return res
 
 
 def bench_dense(pool_gib, reps, stream, capture, ev):
@@ -788,6 +833,8 @@ def main():
         out["gemm_mid"] = bench_mid(mats, copies, args.side_reps, stream, capture, ev)
     if "moe" in legs:
         out["moe"] = bench_moe(args.side_reps, stream, capture, ev)
+    if "batch" in legs:
+        out["gemv_batch"] = bench_batch(mats, copies, max(2, args.side_reps // 4), stream, capture, ev)
     if "dense" in legs:
         out["dense"] = bench_dense(args.pool_gib, max(2, args.side_reps // 4), stream, capture, ev)
     if out["value"] is None and "gemm" in out:

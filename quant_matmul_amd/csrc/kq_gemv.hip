@@ -170,7 +170,7 @@ __device__ inline float dpp_f(float v)
 // into its LDS stage (the same per-chunk arithmetic as kq_quantize_q8k, so
 // the image is bit-identical) instead of reading a Q8_K image; workgroup 0
 // also writes that image out when oq is non-null.
-template <int FMT, int T, int U, int SL, bool PART, bool FUSE>
+template <int FMT, int T, int U, int SL, bool PART, bool FUSE, bool STG>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                     const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                     const int16_t *__restrict__ xbs, float *__restrict__ y,
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
                                                     int8_t *__restrict__ oq, float *__restrict__ os,
                                                     int16_t *__restrict__ obs)
 {
-    static_assert(!FUSE || T <= 2, "the fused quantiser stages the image in LDS");
+    static_assert(!FUSE || (T <= 2 && STG), "the fused quantiser stages the image in LDS");
     constexpr int RPW = 16 / SL;
     __shared__ float red[16][T][RPW];
     const int lane = threadIdx.x & 63;
@@ -208,15 +208,17 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
     // slots re-read a valid superblock and contribute nothing)
     auto sb_at = [&](int j) { return min(min(j, j_end - 1) * SL + sig, nsb - 1); };
 
-    // Small batches stage the whole Q8_K image (codes + bsums, T*K*9/8
-    // bytes) in LDS with coalesced 16-byte loads, so no lane waits on an L2
-    // round trip for its codes after its weights land; larger batches read
-    // the codes straight from L2.  Memory counters retire in issue order, so
-    // the staging loads go out before the weight loads: writing them to LDS
-    // then waits only for themselves, and their L2 latency hides under the
-    // HBM fetch of the weights.
-    constexpr bool LDSA = T <= 2;
-    constexpr int SMAX = 2;  // staged 16-byte chunks held per thread
+    // STG: the whole Q8_K image (codes + bsums, T*K*9/8 bytes) is staged in
+    // LDS with coalesced 16-byte loads, so no lane waits on an L2 round trip
+    // for its codes after its weights land (batches 1-2 always; larger
+    // batches while the image is small enough that several workgroups still
+    // fit on a CU).  Otherwise the codes are read straight from L2 inside
+    // the loop.  Memory counters retire in issue order, so the staging
+    // loads go out before the weight loads: writing them to LDS then waits
+    // only for themselves, and their L2 latency hides under the HBM fetch of
+    // the weights.
+    constexpr bool LDSA = STG;
+    constexpr int SMAX = T <= 2 ? 2 : 8;  // staged 16-byte chunks held per thread
     extern __shared__ __align__(16) uint8_t stage[];
     const int64_t nq = T * K / 16, nst = nq + T * K / 128;  // chunks: codes, then bsums
     auto src_chunk = [&](int64_t i) {
@@ -377,21 +379,40 @@ struct GemvArgs {
     int16_t *obs;
 };
 
+// Largest Q8_K image a batch of 3-8 stages in LDS (three such workgroups
+// still fit on a CU); past it those batches read the codes from L2.
+// Measured at batch 4 on the Qwen3-4B FFN matrices: reading from L2 took
+// 11.7-16.5 us per call against 4.9-6.9 us at batch 1 with the image staged.
+constexpr size_t STAGE_MAX = (size_t)48 << 10;
+
 template <int FMT, int T, int U, int SL, bool PART>
 static void launch_one(dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
     // staged Q8_K image (codes + bsums), plus the scales when fused
-    size_t lds = T <= 2 ? (size_t)T * a.nsb * QK * 9 / 8 : 0;
-    if constexpr (T <= 2 && !PART) {
-        if (a.x) {
-            lds += (size_t)T * a.nsb * sizeof(float);
-            hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, true>), g, b, lds, st, a.w, a.n, a.nsb, a.xq,
-                               a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
-            return;
+    const size_t img = (size_t)T * a.nsb * QK * 9 / 8;
+    if constexpr (T <= 2) {
+        if constexpr (!PART) {
+            if (a.x) {
+                hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, true, true>), g, b,
+                                   img + (size_t)T * a.nsb * sizeof(float), st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs,
+                                   a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
+                return;
+            }
         }
+        hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, true>), g, b, img, st, a.w, a.n, a.nsb, a.xq,
+                           a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
+    } else {
+        // the partials (a test path) keep reading from L2
+        if constexpr (!PART) {
+            if (img <= STAGE_MAX) {
+                hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, false, true>), g, b, img, st, a.w, a.n, a.nsb,
+                                   a.xq, a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, false>), g, b, 0, st, a.w, a.n, a.nsb, a.xq,
+                           a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
     }
-    hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false>), g, b, lds, st, a.w, a.n, a.nsb, a.xq, a.xs,
-                       a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
 }
 
 template <int FMT, int T>
@@ -433,11 +454,16 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
     const int64_t nsb = k / QK;
     // the fused kernel runs exactly when launch_one picks it
     const bool fused = x != nullptr && t <= 2 && P == nullptr;
-    // 16 rows per workgroup when that gives two or more workgroups per CU,
-    // else 4 rows x 4 adjacent superblocks per wave step
-    // (the fused path keeps the same shape, so its y is bit-identical to
-    // quantise-then-GEMV)
-    const int sl = t <= 2 ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
+    // 4 rows x 4 adjacent superblocks per wave step whenever the image is
+    // staged in LDS (the fused path keeps the same shape, so its y is
+    // bit-identical to quantise-then-GEMV).  A batch that reads its codes
+    // from L2 takes 16 rows x one superblock when that gives two or more
+    // workgroups per CU, so that the wave's 16 rows share one superblock's
+    // codes.  Measured with the image staged, 4 x 4 against 16 x 1 on W_up
+    // (9728 x 2560): batch 4 8.2-9.5 us against 10.7-13.6 us.  The choice
+    // depends on t, k and n only, so the partials entry point (which reads
+    // from L2) sums in the same order.
+    const int sl = (t <= 2 || (size_t)t * k * 9 / 8 <= STAGE_MAX) ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
     // Row groups per workgroup (below).  Staging a read-only image costs a
     // workgroup little, so the plain GEMV keeps one group per workgroup (the
     // finest grain); the fused GEMV quantises the whole activation in every
