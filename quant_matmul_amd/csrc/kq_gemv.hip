@@ -475,8 +475,12 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
     // every wave of a workgroup with the same share of steps; a row of at
     // most 4 steps gives each wave one step (measured: W_up 9728 x 2560 at
     // batch 1, 3 steps, runs 0.2-0.4 us faster with 3 waves of one step than
-    // with 2 of up to two, while W_down's 10 steps prefer two per wave)
-    int64_t nw = nsteps <= 4 ? nsteps : (4096 + groups - 1) / groups;
+    // with 2 of up to two, while W_down's 10 steps prefer two per wave).  A
+    // staged batch of 3-8 gives each wave one step up to 16 steps (W_down at
+    // batch 4: 59.7 against 62.3 us over the six matrices); like sl, this
+    // depends on t, k and n only.
+    const bool staged3 = t > 2 && (size_t)t * k * 9 / 8 <= STAGE_MAX;
+    int64_t nw = (nsteps <= 4 || (staged3 && nsteps <= 16)) ? nsteps : (4096 + groups - 1) / groups;
     nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
     nw = nw > nsteps ? nsteps : nw;
     const int64_t per_wave = (nsteps + nw - 1) / nw;
