@@ -447,9 +447,9 @@ static void launch_t(int t, int sl, int u, bool part, dim3 g, dim3 b, hipStream_
     }
 }
 
-int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
-                const float *x, int8_t *oq, float *os, int16_t *obs)
+static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                           const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
+                           const float *x, int8_t *oq, float *os, int16_t *obs)
 {
     const int64_t nsb = k / QK;
     // the fused kernel runs exactly when launch_one picks it
@@ -500,6 +500,32 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, 
     else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, sl, u, part, g, b, st, a);
     else launch_t<KQ_Q6_K>((int)t, sl, u, part, g, b, st, a);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
+}
+
+// A batch of 3-8 whose Q8_K image is too large to stage runs as chunks of
+// the most tokens (at least 3) whose image does stage, one launch each; the
+// weights are read once per chunk, but the L2 path is slower still (W_down,
+// k = 9728, at batch 8: 22-36 us from L2 against two staged launches of
+// batch 4).  The chunking depends on t and k only, so the partials entry
+// point sums every token in the same order.  Where no chunk of 3 stages
+// (k above 14336), the batch reads its codes from L2.
+int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
+                const float *x, int8_t *oq, float *os, int16_t *obs)
+{
+    int64_t tc = t;
+    while (tc > 2 && (size_t)tc * k * 9 / 8 > STAGE_MAX) --tc;
+    if (t <= 2 || tc == t || tc < 3)
+        return launch_gemv_one(fmt, w, n, k, xq, xs, xbs, t, y, P, M, st, x, oq, os, obs);
+    const int64_t nsb = k / QK;
+    for (int64_t t0 = 0; t0 < t; t0 += tc) {
+        const int64_t tn = t - t0 < tc ? t - t0 : tc;
+        const int rc = launch_gemv_one(fmt, w, n, k, xq + t0 * k, xs + t0 * nsb, xbs + t0 * (k / 16), tn, y + t0 * n,
+                                       P ? P + t0 * n * nsb : nullptr, M ? M + t0 * n * nsb : nullptr, st, nullptr,
+                                       nullptr, nullptr, nullptr);
+        if (rc != KQ_OK) return rc;
+    }
+    return KQ_OK;
 }
 
 }  // namespace kq
