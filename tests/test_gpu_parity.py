@@ -205,8 +205,11 @@ def sample_rows(n):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
-@pytest.mark.parametrize("t", [1, 4])
+@pytest.mark.parametrize("t", [1, 4, 8])
 def test_gemv_full_size_sampled(fmt, n, k, t):
+    # batch 4 stages the Q8_K image in LDS at both shapes; batch 8 stages it
+    # on W_up and runs W_down (an 88 KB image) as two staged launches of 4
+    # tokens, the partials entry point included, in the same sum order
     c = Case(fmt, n, k, t, seed=3)
     y, P, M = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
     check(c, y, P, M, rows=sample_rows(n))
