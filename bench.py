@@ -37,7 +37,8 @@ logits, gather-quantise + kq_gemm_grouped for each projection).  Both are
 bound by the weight bytes, so their rooflines are in GB/s of HBM.
 `layers` runs every matmul of one decode token and of one 512-token prefill
 through a 36-layer Qwen3-4B-shaped set (q, k, v, o, gate, up, down; 2.3 GB
-of weights), and `probes` measures this machine's achievable ceilings -- a
+of weights), both as seven matrices per layer and with q|k and gate|up packed
+as one matrix each (`*_fused`), and `probes` measures this machine's achievable ceilings -- a
 plain streaming read of the same plane buffers and a plain int8 MFMA loop --
 which `roofline.achievable` / `roofline_gemm.achievable` set beside the
 datasheet peaks.  `dense` runs the large dense projections (17408 x 5120 and
@@ -528,6 +529,8 @@ def bench_layers(reps, stream, capture, ev):
     fused_layer = [cat(["q", "k"]), single("v"), single("o"), cat(["gate", "up"]), single("down")]
     fused_in = ["attn", "attn", "o", "ffn", "down"]
     yf = [torch.empty((1, n), device="cuda") for _, n, _, _ in fused_layer]
+    ymf = [torch.empty((GEMM_M, n), device="cuda") for _, n, _, _ in fused_layer]
+    wsf = [ops.gemm_workspace(fmt, n, k, GEMM_M) for fmt, n, k, _ in fused_layer]
     torch.cuda.synchronize()
 
     def decode_fused():
@@ -539,9 +542,19 @@ def bench_layers(reps, stream, capture, ev):
                     kq.kq_quantize_q8k(x1[inp], 1, k, *q1[inp])
                     kq.kq_gemv(fmt, pl[L], n, k, *q1[inp], 1, yf[j])
 
+    # the prefill over the same merged matrices (q|k: 5120 rows, gate|up:
+    # 19456 rows), one quantisation per distinct input
+    def prefill_fused():
+        for L in range(N_LAYERS):
+            for j, ((fmt, n, k, pl), inp) in enumerate(zip(fused_layer, fused_in)):
+                if j == 0 or inp != fused_in[j - 1]:
+                    kq.kq_quantize_q8k_tiles(xm[inp], GEMM_M, k, *qm[inp])
+                kq.kq_gemm(fmt, pl[L], n, k, *qm[inp], GEMM_M, ymf[j], wsf[j])
+
     res = {}
     for kind, fn, nrep in (("decode", decode, reps), ("decode_fused", decode_fused, reps),
-                           ("prefill", prefill, max(2, reps // 4))):
+                           ("prefill", prefill, max(2, reps // 4)),
+                           ("prefill_fused", prefill_fused, max(2, reps // 4))):
         g = capture(fn)
         g.replay()
         torch.cuda.synchronize()
@@ -567,7 +580,10 @@ def bench_layers(reps, stream, capture, ev):
             "decode_fused_launches_per_token": N_LAYERS * 6,
             "prefill_us": res["prefill"],
             "prefill_TOPS": ops_prefill / (res["prefill"] * 1e-6) / 1e12,
-            "prefill_frac_mfma": ops_prefill / (res["prefill"] * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS}
+            "prefill_frac_mfma": ops_prefill / (res["prefill"] * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS,
+            "prefill_fused_us": res["prefill_fused"],
+            "prefill_fused_TOPS": ops_prefill / (res["prefill_fused"] * 1e-6) / 1e12,
+            "prefill_fused_launches": N_LAYERS * (len(fused_layer) + len(LAYER_INPUTS))}
 
 
 def profile_one(spec, reps):
