@@ -7,7 +7,9 @@
 // workgroup is 4 waves over 128 weight rows x one 32-token tile (a wave: 32
 // rows x 32 tokens, one v_mfma_i32_32x32x32_i8 tile), so each unpacked
 // weight serves 32 tokens; what changes from the 256-token tile is how the
-// weights are unpacked.
+// weights are unpacked.  When the 32-token tiles pair up evenly (33-64 and
+// 97-127 tokens), the Q4_K/Q5_K workgroup covers 64 rows x two token tiles
+// instead, so each fetched and expanded panel serves 64 tokens.
 //  * Q4_K/Q5_K: a 32-weight sub-block is one K step, so the MFMA takes the
 //    raw quants as its B operand, yields dot_j, and P += sc_j * dot_j is one
 //    integer mad per output (cheaper at 32 tokens than folding sc_j into
@@ -222,36 +224,45 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
 // per-output integer mad of the register form.
 constexpr int MID_STRIDE = 272;
 
-template <int FMT, bool GROUPED, bool PART>
+template <int FMT, bool GROUPED, bool PART, int TT>
 __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
     const uint8_t *__restrict__ w, int64_t w_stride, const int32_t *__restrict__ tile_expert, int experts, int64_t n,
     int nsb, const int8_t *__restrict__ xq, const float *__restrict__ xs, const _Float16 *__restrict__ xbs,
     int64_t mtok, float *__restrict__ y, int32_t *__restrict__ Pout, int32_t *__restrict__ Mout, int mtiles, int S)
 {
     static_assert(FMT != KQ_Q6_K, "Q6_K uses the register form");
-    __shared__ __align__(16) int8_t qp[2][128 * MID_STRIDE];
-    __shared__ __align__(16) uint32_t scw[2][128][2];  // 8 sub-scales per row, as bytes
-    __shared__ __align__(16) uint32_t mnw[2][128][2];  // 8 mins per row, as bytes
-    __shared__ float dd[2][128], dmm[2][128];
-    __shared__ __align__(16) float d8s[2][32];
+    static_assert(TT == 1 || (TT == 2 && !GROUPED), "two token tiles share a panel only in the plain form");
+    // TT token tiles x RW row blocks of 32 per workgroup: the panel of PR
+    // rows serves 32*TT tokens
+    constexpr int RW = 4 / TT, PR = 32 * RW;
+    __shared__ __align__(16) int8_t qp[2][PR * MID_STRIDE];
+    __shared__ __align__(16) uint32_t scw[2][PR][2];  // 8 sub-scales per row, as bytes
+    __shared__ __align__(16) uint32_t mnw[2][PR][2];  // 8 mins per row, as bytes
+    __shared__ float dd[2][PR], dmm[2][PR];
+    __shared__ __align__(16) float d8s[2][32 * TT];
 
     const int item = item_of_mid(blockIdx.x, gridDim.x);
     const int tile = item / S, split = item - tile * S;
     // grouped: the 128-row panels of one 32-token tile (one expert) run
     // together, so they share that tile's codes and the expert's planes in
     // L2; otherwise the token tiles of one panel run together and share it
-    int nt, mt;
+    int nt, mg;
     if constexpr (GROUPED) {
         const int ntiles = (int)((n + 127) / 128);
-        mt = tile / ntiles;
-        nt = tile - mt * ntiles;
+        mg = tile / ntiles;
+        nt = tile - mg * ntiles;
     } else {
-        nt = tile / mtiles;
-        mt = tile - nt * mtiles;
+        const int mgroups = (mtiles + TT - 1) / TT;
+        nt = tile / mgroups;
+        mg = tile - nt * mgroups;
     }
     const int s0 = (int)((int64_t)nsb * split / S), s1 = (int)((int64_t)nsb * (split + 1) / S);
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-    const int64_t n0 = (int64_t)nt * 128, m0 = (int64_t)mt * 32;
+    // wave wv: row block wv % RW, token tile wv / RW of the group (a token
+    // tile past the last one still stages and meets the barriers, its codes
+    // read as zero and its outputs unstored)
+    const int rb = TT == 1 ? wv : wv % RW, mt = TT == 1 ? mg : mg * TT + wv / RW;
+    const int64_t n0 = (int64_t)nt * PR, m0 = (int64_t)mt * 32, mg0 = (int64_t)mg * 32 * TT;
     const uint8_t *wb = w;
     if constexpr (GROUPED) {
         const int e = tile_expert[mt];  // uniform over the workgroup
@@ -264,26 +275,26 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
     // panel fetch: thread covers 16 bytes (chunk tid%8) of the quant rows
     // 32j + tid/8, j = 0..3; threads 0..127 also take row tid's header
     const int chunk = tid & 7, rsub = tid >> 3;
-    int64_t qrow[4];
+    int64_t qrow[RW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < RW; ++j) {
         const int64_t r = n0 + 32 * j + rsub;
         qrow[j] = (r < n ? r : n - 1) * nsb;
     }
-    const int64_t hr = n0 + (tid & 127);
+    const int64_t hr = n0 + (tid & (PR - 1));
     const bool hvalid = hr < n;
     const int64_t hrow = (hvalid ? hr : n - 1) * nsb;
-    uint4 rq[4], rqh[4], rh;
+    uint4 rq[RW], rqh[RW], rh;
     auto fetch = [&](int s) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < RW; ++j) {
             rq[j] = *reinterpret_cast<const uint4 *>(wb + pl.off[FMT == KQ_Q5_K ? 2 : 1] + (qrow[j] + s) * 128 + 16 * chunk);
             if constexpr (FMT == KQ_Q5_K)
                 rqh[j] = *reinterpret_cast<const uint4 *>(wb + pl.off[1] + (qrow[j] + s) * 32 + 16 * (chunk & 1));
         }
         rh = *reinterpret_cast<const uint4 *>(wb + pl.off[0] + (hrow + s) * 16);
     };
-    const int64_t td = m0 + (tid & 31);
+    const int64_t td = mg0 + (tid & (32 * TT - 1));  // token whose d8 this thread stages
     const float *xs_row = xs + (td < mtok ? td : mtok - 1) * nsb;
     float d8v = 0.0f;
     // expand the fetched bytes into panel buffer b: quant byte 32c + b of a
@@ -291,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
     auto stage = [&](int b) {
         const int c = chunk >> 1, b0 = 16 * (chunk & 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < RW; ++j) {
             const uint32_t q[4] = {rq[j].x, rq[j].y, rq[j].z, rq[j].w};
             uint32_t lo[4], hi[4];
 #pragma unroll
@@ -308,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
             *reinterpret_cast<uint4 *>(row) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             *reinterpret_cast<uint4 *>(row + 32) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
         }
-        if (tid < 128) {
+        if (tid < PR) {
             // rows past n: scales, mins and d masked to zero
             const uint32_t vm = hvalid ? 0xFFFFFFFFu : 0u;
             const uint32_t s0w = rh.y & vm, s1w = rh.z & vm, s2w = rh.w & vm;
@@ -319,17 +330,21 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
             dd[b][tid] = f16_bits_to_float(rh.x & vm & 0xFFFFu);
             dmm[b][tid] = f16_bits_to_float((rh.x & vm) >> 16);
         }
-        if (tid < 32) d8s[b][tid] = td < mtok ? d8v : 0.0f;
+        if (tid < 32 * TT) d8s[b][tid] = td < mtok ? d8v : 0.0f;
     };
 
     // the tile's 32 tokens of codes and f16 bsums (tile image)
     const int64_t mpad = (mtok + 31) & ~(int64_t)31;
-    const uint64_t a_bytes = (uint64_t)(mpad - m0) * (uint64_t)K;
-    const uint64_t b_bytes = (uint64_t)(mpad - m0) * (uint64_t)nsb * 32;
+    // a token tile past the image gets empty ranges (every load reads zero)
+    // based at the image start
+    const bool mvalid = TT == 1 || m0 < mpad;
+    const int64_t mb = mvalid ? m0 : 0;
+    const uint64_t a_bytes = mvalid ? (uint64_t)(mpad - m0) * (uint64_t)K : 0;
+    const uint64_t b_bytes = mvalid ? (uint64_t)(mpad - m0) * (uint64_t)nsb * 32 : 0;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(xq + m0 * K), 0, (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu), 0x00020000);
+        (void *)(xq + mb * K), 0, (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu), 0x00020000);
     const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(xbs + m0 * nsb * 16), 0, (int)(uint32_t)(b_bytes < 0xFFFFFFFFu ? b_bytes : 0xFFFFFFFFu),
+        (void *)(xbs + mb * nsb * 16), 0, (int)(uint32_t)(b_bytes < 0xFFFFFFFFu ? b_bytes : 0xFFFFFFFFu),
         0x00020000);
     i32x4 A[8];
     f16x8 Ab;
@@ -353,7 +368,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
     }
     __syncthreads();
 
-    const int rl = 32 * wv + lr;  // this lane's panel row
+    const int rl = 32 * rb + lr;  // this lane's panel row
+    const int tb = TT == 1 ? 0 : 32 * (wv / RW);  // this wave's token tile within the group's d8s
     const int64_t row = n0 + rl;
     f32x16 accf = f32x16{};
     for (int s = s0; s < s1; ++s) {
@@ -391,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
         for (int i = 0; i < 16; ++i) {
             const int tl = 8 * (i >> 2) + 4 * lh + (i & 3);
             const float u = fmaf(dv, (float)P[i], -(dm * mf[i]));
-            accf[i] = fmaf(d8s[b][tl], u, accf[i]);
+            accf[i] = fmaf(d8s[b][tb + tl], u, accf[i]);
             if (PART) {
                 const int64_t t = m0 + tl;
                 if (t < mtok && row < n) {
@@ -446,8 +462,11 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
                     int64_t n, int nsb, const int8_t *xq, const float *xs, const _Float16 *xbs, int64_t m, float *y,
                     int32_t *P, int32_t *M, int S, hipStream_t st)
 {
-    const int64_t ntiles = (n + 127) / 128, mtiles = (m + 31) / 32;
-    const dim3 g((unsigned)(ntiles * mtiles * S)), b(256);
+    const int64_t mtiles = (m + 31) / 32;
+    // two token tiles share each 64-row panel when they pair up evenly
+    const bool pair = !GROUPED && FMT != KQ_Q6_K && mtiles % 2 == 0;
+    const int64_t ntiles = pair ? (n + 63) / 64 : (n + 127) / 128;
+    const dim3 g((unsigned)(ntiles * (pair ? mtiles / 2 : mtiles) * S)), b(256);
     if constexpr (FMT == KQ_Q6_K) {
         if (part)
             hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, true>), g, b, 0, st, w, w_stride, tile_expert, experts, n,
@@ -456,11 +475,22 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
             hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, false>), g, b, 0, st, w, w_stride, tile_expert, experts,
                                n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
     } else {
+        if constexpr (!GROUPED) {
+            if (pair) {
+                if (part)
+                    hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, false, true, 2>), g, b, 0, st, w, w_stride,
+                                       tile_expert, experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+                else
+                    hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, false, false, 2>), g, b, 0, st, w, w_stride,
+                                       tile_expert, experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+                return;
+            }
+        }
         if (part)
-            hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, true>), g, b, 0, st, w, w_stride, tile_expert,
+            hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, true, 1>), g, b, 0, st, w, w_stride, tile_expert,
                                experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
         else
-            hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, false>), g, b, 0, st, w, w_stride, tile_expert,
+            hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, false, 1>), g, b, 0, st, w, w_stride, tile_expert,
                                experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
     }
 }

@@ -267,7 +267,7 @@ def test_gemm_split_parts_meet_through_any_workspace(fmt, n, k, m):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
-@pytest.mark.parametrize("m", [16, 96])
+@pytest.mark.parametrize("m", [16, 64, 96])  # 64: two token tiles share each row panel
 def test_gemm_mid_full_size_sampled(fmt, n, k, m):
     c = Case(fmt, n, k, m, seed=6)
     y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
@@ -276,10 +276,11 @@ def test_gemm_mid_full_size_sampled(fmt, n, k, m):
 
 
 # ------------------------------------------ poison, guards, determinism --
-@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_mid"])
+@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_mid", "gemm_mid_pair"])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_outputs_fully_written_and_guards_intact(kind, fmt):
-    n, k, t = 70, 768, {"gemv": 3, "gemm": 170, "gemm_mid": 70}[kind]
+    # gemm_mid_pair: an even number of 32-token tiles, paired on 64-row panels
+    n, k, t = 70, 768, {"gemv": 3, "gemm": 170, "gemm_mid": 70, "gemm_mid_pair": 60}[kind]
     c = Case(fmt, n, k, t, seed=9)
     g = 4096
     buf = torch.full((g + t * n + g,), float("nan"), dtype=torch.float32, device="cuda")
