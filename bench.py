@@ -80,9 +80,9 @@ GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "16043
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "11609855197ded27",
                 "bytes_per_launch": 74635230}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "1677a7f22b2396ed", "bytes_per_launch": 35962791}
+               "src_sha256_16": "4f44ab4f3226604d", "bytes_per_launch": 35192523}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "affe26a6a6a15d54", "bytes_per_launch": 229738285}
+               "src_sha256_16": "439d8654cd5735a8", "bytes_per_launch": 229720947}
 
 
 def src_hash(files):

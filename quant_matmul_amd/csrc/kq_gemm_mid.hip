@@ -9,7 +9,8 @@
 // weight serves 32 tokens; what changes from the 256-token tile is how the
 // weights are unpacked.  When the 32-token tiles pair up evenly (33-64 and
 // 97-127 tokens), the Q4_K/Q5_K workgroup covers 64 rows x two token tiles
-// instead, so each fetched and expanded panel serves 64 tokens.
+// instead, so each fetched and expanded panel serves 64 tokens, and a Q6_K
+// wave covers both tiles, so each digit it unpacks serves 64 tokens.
 //  * Q4_K/Q5_K: a 32-weight sub-block is one K step, so the MFMA takes the
 //    raw quants as its B operand, yields dot_j, and P += sc_j * dot_j is one
 //    integer mad per output (cheaper at 32 tokens than folding sc_j into
@@ -97,14 +98,17 @@ __device__ inline int item_of_mid(int b, int G)
 // MFMA B-operand registers (no LDS panel, no barriers); its 16-weight
 // sub-blocks do not match a K step, so the signed sub-scale is folded into
 // two digit passes (kq_digits.h), high and low digit in two accumulators.
-template <int FMT, bool GROUPED, bool PART>
+// With TT = 2 a wave covers two consecutive 32-token tiles, so each digit
+// it unpacks feeds four MFMAs (two tiles x two digits) instead of two.
+template <int FMT, bool GROUPED, bool PART, int TT>
 __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     const uint8_t *__restrict__ w, int64_t w_stride, const int32_t *__restrict__ tile_expert, int experts, int64_t n,
     int nsb, const int8_t *__restrict__ xq, const float *__restrict__ xs, const _Float16 *__restrict__ xbs,
     int64_t mtok, float *__restrict__ y, int32_t *__restrict__ Pout, int32_t *__restrict__ Mout, int mtiles, int S)
 {
     static_assert(FMT == KQ_Q6_K, "Q4_K/Q5_K use the LDS-panel form");
-    __shared__ __align__(16) float d8w[4][32];
+    static_assert(TT == 1 || (TT == 2 && !GROUPED), "two token tiles per wave only in the plain form");
+    __shared__ __align__(16) float d8w[4][32 * TT];
 
     // item = (128-row panel, 32-token tile, K split): the token tiles of a
     // panel run on one XCD and share its L2 copy of the panel's planes
@@ -118,9 +122,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
         const int ntiles = (int)((n + 127) / 128);
         mt = tile / ntiles;
         nt = tile - mt * ntiles;
-    } else {
+    } else if constexpr (TT == 1) {
         nt = tile / mtiles;
         mt = tile - nt * mtiles;
+    } else {
+        const int mgroups = (mtiles + 1) / 2;
+        nt = tile / mgroups;
+        mt = 2 * (tile - nt * mgroups);  // the first of the wave's two token tiles
     }
     const int s0 = (int)((int64_t)nsb * split / S), s1 = (int)((int64_t)nsb * (split + 1) / S);
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
@@ -143,20 +151,36 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     // term, so the bsums are not read
     (void)xbs;
     const int64_t mpad = (mtok + 31) & ~(int64_t)31;
-    const uint64_t a_bytes = (uint64_t)(mpad - m0) * (uint64_t)K;
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(xq + m0 * K), 0, (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu), 0x00020000);
-    const int64_t td = m0 + lr;  // token whose d8 this lane stages
+    // token tile j of the wave: a tile past the image gets an empty range
+    // (every load reads zero) based at the image start
+    __amdgpu_buffer_rsrc_t rA[TT];
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+        const int64_t mj = m0 + 32 * j;
+        const bool ok = TT == 1 || mj < mpad;
+        const uint64_t a_bytes = ok ? (uint64_t)(mpad - mj) * (uint64_t)K : 0;
+        rA[j] = __builtin_amdgcn_make_buffer_rsrc((void *)(xq + (ok ? mj : 0) * K), 0,
+                                                  (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu),
+                                                  0x00020000);
+    }
+    // token whose d8 this lane stages: lanes of half 0 for one tile, every
+    // lane for two
+    const int64_t td = m0 + (TT == 1 ? lr : lane);
     const float *xs_row = xs + (td < mtok ? td : mtok - 1) * nsb;
 
-    i32x4 A[8];
+    i32x4 A[TT][8];
     Lane6 raw, nxt;
     float d8v;
     auto load_a = [&](int s, int ks) {
-        A[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, 16 * lane, (s * 8 + ks) * 1024, 0));
+#pragma unroll
+        for (int j = 0; j < TT; ++j)
+            A[j][ks] = __builtin_bit_cast(
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA[j], 16 * lane, (s * 8 + ks) * 1024, 0));
     };
 
-    f32x16 accf = f32x16{};
+    f32x16 accf[TT];
+#pragma unroll
+    for (int j = 0; j < TT; ++j) accf[j] = f32x16{};
     load_lane(raw, wb, pl, wrow + s0, lh);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) load_a(s0, ks);
@@ -169,34 +193,43 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
         const int sn = s + 1 < s1 ? s + 1 : s;
         // stage the 32 d8s of superblock s for the fold (wave-private LDS:
         // the wave's own later reads see these writes in order)
-        if (lh == 0) d8w[wv][lr] = d8v;
+        if (TT == 2 || lh == 0) d8w[wv][TT == 1 ? lr : lane] = d8v;
         load_lane(nxt, wb, pl, wrow + sn, lh);
         d8v = td < mtok ? xs_row[sn] : 0.0f;
         // 16-weight sub-blocks: the scale is folded into the two digit
         // passes (kq_digits.h)
-        i32x16 acch = i32x16{}, accl = i32x16{};
+        i32x16 acch[TT], accl[TT];
+#pragma unroll
+        for (int j = 0; j < TT; ++j) acch[j] = accl[j] = i32x16{};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             i32x4 bh, bl;
             digits_ks(raw, ks, lh, bh, bl);
-            acch = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bh, acch, 0, 0, 0);
-            accl = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], bl, accl, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < TT; ++j) {
+                acch[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[j][ks], bh, acch[j], 0, 0, 0);
+                accl[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[j][ks], bl, accl[j], 0, 0, 0);
+            }
             load_a(sn, ks);
         }
-        const i32x16 P = (acch << 7) + accl;
         const float dv = rvalid ? f16_bits_to_float(raw.d) : 0.0f;
         __builtin_amdgcn_wave_barrier();
-        // lane holds tokens 8*(i/4) + 4*lh + i%4, i = 0..15, of row `row`
+        // lane holds tokens 8*(i/4) + 4*lh + i%4, i = 0..15, of each tile,
+        // of row `row`
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tl = 8 * (i >> 2) + 4 * lh + (i & 3);
-            accf[i] = fmaf(d8w[wv][tl], dv * (float)P[i], accf[i]);
-            if (PART) {
-                const int64_t t = m0 + tl;
-                if (t < mtok && rvalid) {
-                    const int64_t o = (t * n + row) * nsb + s;
-                    Pout[o] = P[i];
-                    if (Mout) Mout[o] = 0;
+        for (int j = 0; j < TT; ++j) {
+            const i32x16 P = (acch[j] << 7) + accl[j];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int tl = 8 * (i >> 2) + 4 * lh + (i & 3);
+                accf[j][i] = fmaf(d8w[wv][32 * j + tl], dv * (float)P[i], accf[j][i]);
+                if (PART) {
+                    const int64_t t = m0 + 32 * j + tl;
+                    if (t < mtok && rvalid) {
+                        const int64_t o = (t * n + row) * nsb + s;
+                        Pout[o] = P[i];
+                        if (Mout) Mout[o] = 0;
+                    }
                 }
             }
         }
@@ -208,9 +241,12 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     if (!rvalid) return;
     float *yo = y + (int64_t)split * mtok * n;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int64_t t = m0 + 8 * (i >> 2) + 4 * lh + (i & 3);
-        if (t < mtok) yo[t * n + row] = accf[i];
+    for (int j = 0; j < TT; ++j) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t t = m0 + 32 * j + 8 * (i >> 2) + 4 * lh + (i & 3);
+            if (t < mtok) yo[t * n + row] = accf[j][i];
+        }
     }
 }
 
@@ -463,17 +499,29 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
                     int32_t *P, int32_t *M, int S, hipStream_t st)
 {
     const int64_t mtiles = (m + 31) / 32;
-    // two token tiles share each 64-row panel when they pair up evenly
-    const bool pair = !GROUPED && FMT != KQ_Q6_K && mtiles % 2 == 0;
-    const int64_t ntiles = pair ? (n + 63) / 64 : (n + 127) / 128;
+    // token tiles pair up when their count is even: on 64-row panels
+    // (Q4_K/Q5_K) or within each wave (Q6_K)
+    const bool pair = !GROUPED && mtiles % 2 == 0;
+    const int64_t ntiles = pair && FMT != KQ_Q6_K ? (n + 63) / 64 : (n + 127) / 128;
     const dim3 g((unsigned)(ntiles * (pair ? mtiles / 2 : mtiles) * S)), b(256);
     if constexpr (FMT == KQ_Q6_K) {
+        if constexpr (!GROUPED) {
+            if (pair) {
+                if (part)
+                    hipLaunchKernelGGL((gemm_mid_kernel<FMT, false, true, 2>), g, b, 0, st, w, w_stride, tile_expert,
+                                       experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+                else
+                    hipLaunchKernelGGL((gemm_mid_kernel<FMT, false, false, 2>), g, b, 0, st, w, w_stride,
+                                       tile_expert, experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+                return;
+            }
+        }
         if (part)
-            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, true>), g, b, 0, st, w, w_stride, tile_expert, experts, n,
-                               nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
-        else
-            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, false>), g, b, 0, st, w, w_stride, tile_expert, experts,
+            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, true, 1>), g, b, 0, st, w, w_stride, tile_expert, experts,
                                n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+        else
+            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, false, 1>), g, b, 0, st, w, w_stride, tile_expert,
+                               experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
     } else {
         if constexpr (!GROUPED) {
             if (pair) {
