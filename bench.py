@@ -80,9 +80,9 @@ GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "16043
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "11609855197ded27",
                 "bytes_per_launch": 74635230}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "4f44ab4f3226604d", "bytes_per_launch": 35192523}
+               "src_sha256_16": "19d8ba033cc0c3b9", "bytes_per_launch": 35192565}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "439d8654cd5735a8", "bytes_per_launch": 229720947}
+               "src_sha256_16": "87a344696de05b82", "bytes_per_launch": 229663143}
 
 
 def src_hash(files):

@@ -110,8 +110,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     static_assert(TT == 1 || (TT == 2 && !GROUPED), "two token tiles per wave only in the plain form");
     __shared__ __align__(16) float d8w[4][32 * TT];
 
-    // item = (128-row panel, 32-token tile, K split): the token tiles of a
-    // panel run on one XCD and share its L2 copy of the panel's planes
+    // item = (128-row panel, 32-token tile -- or pair of tiles when TT = 2 --,
+    // K split): the token tiles of a panel run on one XCD and share its L2
+    // copy of the panel's planes
     const int item = item_of_mid(blockIdx.x, gridDim.x);
     const int tile = item / S, split = item - tile * S;
     // grouped: the 128-row panels of one 32-token tile (one expert) run
@@ -191,8 +192,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
         // last step re-reads its own, in bounds): a branch here would split
         // the K loop into blocks the scheduler cannot interleave across
         const int sn = s + 1 < s1 ? s + 1 : s;
-        // stage the 32 d8s of superblock s for the fold (wave-private LDS:
-        // the wave's own later reads see these writes in order)
+        // stage the d8s of superblock s for the fold, 32 per token tile
+        // (wave-private LDS: the wave's own later reads see these writes in
+        // order)
         if (TT == 2 || lh == 0) d8w[wv][TT == 1 ? lr : lane] = d8v;
         load_lane(nxt, wb, pl, wrow + sn, lh);
         d8v = td < mtok ? xs_row[sn] : 0.0f;
@@ -250,14 +252,14 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     }
 }
 
-// Q4_K/Q5_K form with an LDS weight panel.  The workgroup's 128 rows x one
-// superblock are fetched cooperatively, eight lanes per row (16 bytes each,
+// Q4_K/Q5_K form with an LDS weight panel.  The workgroup's 128 rows (64 with
+// TT = 2 token tiles) x one superblock are fetched cooperatively, eight lanes per row (16 bytes each,
 // so every load instruction covers eight whole 128-byte lines), expanded to
 // one byte per quant into an LDS panel (row stride 272 bytes: the B-operand
 // reads of 32 rows hit distinct banks) with the decoded scales, mins and
 // d/dmin beside it, double-buffered with one barrier per superblock.  Each
-// wave then reads its 32 rows' B operands from LDS; the sub-scale is the
-// per-output integer mad of the register form.
+// wave then reads its 32 rows' B operands from LDS for its token tile; the
+// sub-scale is the per-output integer mad of the register form.
 constexpr int MID_STRIDE = 272;
 
 template <int FMT, bool GROUPED, bool PART, int TT>
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
     const Planes pl = planes_of(FMT, n, nsb);
 
     // panel fetch: thread covers 16 bytes (chunk tid%8) of the quant rows
-    // 32j + tid/8, j = 0..3; threads 0..127 also take row tid's header
+    // 32j + tid/8, j < RW; threads below PR also take row tid's header
     const int chunk = tid & 7, rsub = tid >> 3;
     int64_t qrow[RW];
 #pragma unroll
