@@ -259,7 +259,7 @@ def bench_mid(mats, copies, reps, stream, capture, ev):
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic(MID_TRAFFIC),
                          "algorithmic_bytes_per_launch": kb_total / len(mats),
-                         "kernel": "kq::gemm_mid_lds_kernel (Q4_K, Q5_K) / kq::gemm_mid_kernel (Q6_K) (kq_gemm, m <= 127)",
+                         "kernel": "kq::gemm_mid_lds_kernel (Q4_K, Q5_K) / kq::gemm_mid_kernel (Q6_K) (kq_gemm, 32-token tile)",
                          "avg_launch_us": kus_total / len(mats)}}
 
 

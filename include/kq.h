@@ -155,18 +155,19 @@ size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
 
 /* Prefill GEMM, m >= 1 tokens: y[m][n], the folds of kq_gemv.  The codes
  * and bsums are the tile image of kq_quantize_q8k_tiles, xs row-major.
- * k <= 2^23 - 256 (KQ_EINVAL above).  m <= 127 runs a 32-token tile that
- * unpacks each weight once per 32 tokens (in registers for Q6_K, through an
- * LDS panel for Q4_K/Q5_K), m >= 128 a 256-token tile that unpacks it once
- * per 256 tokens into LDS.
+ * k <= 2^23 - 256 (KQ_EINVAL above).  m <= 127, and m = 128 or 161..192
+ * (an even number of 32-token tiles), run a 32-token tile that unpacks each
+ * weight once per 32 tokens, or per 64 when the tiles pair up (in registers
+ * for Q6_K, through an LDS panel for Q4_K/Q5_K); other m a 256-token tile
+ * that unpacks it once per 256 tokens into LDS.
  * workspace: NULL, or a 256-byte aligned device buffer of workspace_bytes
  * >= kq_gemm_workspace_bytes bytes (no initial contents needed).  With it,
- * a grid too small to fill the GPU is split along k: for m >= 128 each
- * tile's parts write partial sums to the workspace and the last part of the
- * tile to finish adds them into y (one launch); for m <= 127 whole-output
- * slices that a second kernel adds.  Both add in split order, so results
+ * a grid too small to fill the GPU is split along k: for the 256-token tile
+ * each tile's parts write partial sums to the workspace and the last part of
+ * the tile to finish adds them into y (one launch); for the 32-token tile
+ * whole-output slices that a second kernel adds.  Both add in split order, so results
  * are the same from call to call (they may differ from the unsplit sum in
- * the last bits, within the fold's float tolerance).  The m >= 128 parts count in through counter words at the
+ * the last bits, within the fold's float tolerance).  The 256-token tile's parts count in through counter words at the
  * start of the workspace that every call tags as its own, so stale contents
  * are ignored and graph replays may reuse the workspace.  Calls sharing one
  * workspace must be ordered on one stream.  A NULL or too small workspace

@@ -19,8 +19,15 @@ size_t gemm_mid_workspace_bytes(int64_t n, int64_t k, int64_t m);
 int launch_gemm_grouped(int fmt, const void *w, int64_t w_stride, int64_t experts, const int32_t *tile_expert,
                         int64_t n, int64_t k, const int8_t *xq, const float *xs, const void *xbs, int64_t m,
                         float *y, int32_t *P, int32_t *M, hipStream_t st);
-// token counts below this run the mid-size tile, the rest the prefill tile
-constexpr int64_t GEMM_MID_MAX = 127;
+// token counts up to GEMM_MID_MAX run the 32-token tile, and so do those up
+// to GEMM_MID_PAIRED_MAX whose 32-token tiles pair up evenly (the paired
+// tile beats a 256-token tile that would run at most three-quarters full);
+// the rest run the 256-token prefill tile
+constexpr int64_t GEMM_MID_MAX = 127, GEMM_MID_PAIRED_MAX = 192;
+inline bool gemm_uses_mid(int64_t m)
+{
+    return m <= GEMM_MID_MAX || (m <= GEMM_MID_PAIRED_MAX && ((m + 31) / 32) % 2 == 0);
+}
 int launch_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, hipStream_t stream);
 int launch_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, hipStream_t stream);
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -178,7 +185,7 @@ int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
 size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m)
 {
     if (!known(fmt) || check_nk(n, k) || m < 1 || m > INT_MAX || k > kq::GEMM_KMAX) return 0;
-    return m <= kq::GEMM_MID_MAX ? kq::gemm_mid_workspace_bytes(n, k, m) : kq::gemm_workspace_bytes(n, k, m);
+    return kq::gemm_uses_mid(m) ? kq::gemm_mid_workspace_bytes(n, k, m) : kq::gemm_workspace_bytes(n, k, m);
 }
 
 int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -188,7 +195,7 @@ int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
                           false);
     if (rc) return rc;
     if (workspace && !aligned(workspace, 256)) return KQ_EALIGN;
-    if (m <= kq::GEMM_MID_MAX)
+    if (kq::gemm_uses_mid(m))
         return kq::launch_gemm_mid(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, workspace,
                                    workspace_bytes, (hipStream_t)stream);
     return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, workspace, workspace_bytes,
@@ -214,7 +221,7 @@ int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
 {
     int rc = check_matmul(fmt, w_planes, n, k, xq, xs, (const int16_t *)xbs, m, INT_MAX, y, P, M, true);
     if (rc) return rc;
-    if (m <= kq::GEMM_MID_MAX)
+    if (kq::gemm_uses_mid(m))
         return kq::launch_gemm_mid(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, nullptr, 0, (hipStream_t)stream);
     return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, nullptr, 0, (hipStream_t)stream);
 }
