@@ -31,7 +31,7 @@ of HIP events on the launch stream, inside the timed region).
 
 Two further measurements run after the timed steps, each in its own graphs:
 `gemm_mid` (the 32-token tile: quantise 64 rows + kq_gemm on the same six
-matrices) and `moe` (a mixture-of-experts layer: 128 Q4_K experts of gate|up
+matrices; `gemm_m128` the same at 128 tokens, the low end of the prefill range) and `moe` (a mixture-of-experts layer: 128 Q4_K experts of gate|up
 1536 x 2048 and down 2048 x 768, 512 tokens routed top-8 by seeded U(0,1)
 logits, gather-quantise + kq_gemm_grouped for each projection).  Both are
 bound by the weight bytes, so their rooflines are in GB/s of HBM.
@@ -208,9 +208,11 @@ def bench_probes(mats, copies, stream, capture, ev):
             "mfma_i8_TOPS": max(m["TOPS"] for m in mfma), "mfma_i8_runs": mfma}
 
 
-def bench_mid(mats, copies, reps, stream, capture, ev):
-    """The 32-token tile: quantise MID_M rows to the tile image + kq_gemm,
-    per matrix, rotating the weight copies; HBM-bound at this size."""
+def bench_mid(mats, copies, reps, stream, capture, ev, tokens=MID_M):
+    """The 32-token tile: quantise `tokens` rows to the tile image + kq_gemm,
+    per matrix, rotating the weight copies; HBM-bound at 64 tokens.  At 128
+    tokens (the low end of the prefill range) kq_gemm also runs the 32-token
+    tile, its four tiles paired."""
     import torch
 
     import synth
@@ -219,17 +221,17 @@ def bench_mid(mats, copies, reps, stream, capture, ev):
 
     res, kb_total, kus_total = {}, 0, 0.0
     for j, (fmt, n, k, pl) in enumerate(mats):
-        x = torch.from_numpy(synth.activations(MID_M, k, synth.seed_for(3, 50 + j))).cuda()
-        q = ops.q8k_tile_buffers(MID_M, k)
-        y = torch.empty((MID_M, n), device="cuda")
-        ws = ops.gemm_workspace(fmt, n, k, MID_M)
+        x = torch.from_numpy(synth.activations(tokens, k, synth.seed_for(3, 50 + j))).cuda()
+        q = ops.q8k_tile_buffers(tokens, k)
+        y = torch.empty((tokens, n), device="cuda")
+        ws = ops.gemm_workspace(fmt, n, k, tokens)
 
         def leg(c, kernel_only=False):
             if not kernel_only:
-                kq.kq_quantize_q8k_tiles(x, MID_M, k, *q)
-            kq.kq_gemm(fmt, pl[c], n, k, *q, MID_M, y, ws)
+                kq.kq_quantize_q8k_tiles(x, tokens, k, *q)
+            kq.kq_gemm(fmt, pl[c], n, k, *q, tokens, y, ws)
 
-        kq.kq_quantize_q8k_tiles(x, MID_M, k, *q)
+        kq.kq_quantize_q8k_tiles(x, tokens, k, *q)
         g_leg = [capture(leg, c) for c in range(copies)]
         g_k = capture(lambda: [leg(r % copies, True) for r in range(copies)])
         for g in g_leg:
@@ -249,15 +251,15 @@ def bench_mid(mats, copies, reps, stream, capture, ev):
         leg_us = a.elapsed_time(b) * 1e3 / reps
         kus = c_.elapsed_time(d_) * 1e3 / (max(1, reps // copies) * copies)
         wb = n * (k // 256) * BYTES[fmt]
-        byts = wb + MID_M * (k // 256) * 292 + 4 * MID_M * n
+        byts = wb + tokens * (k // 256) * 292 + 4 * tokens * n
         res[f"{fmt}_{n}x{k}"] = {"us": kus, "leg_us": leg_us, "GBps": byts / (kus * 1e-6) / 1e9,
-                                 "TOPS": 2 * MID_M * n * k / (kus * 1e-6) / 1e12, "split_k": ws is not None}
+                                 "TOPS": 2 * tokens * n * k / (kus * 1e-6) / 1e12, "split_k": ws is not None}
         kb_total += byts
         kus_total += kus
     ach = kb_total / (kus_total * 1e-6) / 1e9
-    return {"tokens": MID_M, "per_matrix": res,
+    return {"tokens": tokens, "per_matrix": res,
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic(MID_TRAFFIC),
+                         "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic(MID_TRAFFIC) if tokens == MID_M else None,
                          "algorithmic_bytes_per_launch": kb_total / len(mats),
                          "kernel": "kq::gemm_mid_lds_kernel (Q4_K, Q5_K) / kq::gemm_mid_kernel (Q6_K) (kq_gemm, 32-token tile)",
                          "avg_launch_us": kus_total / len(mats)}}
@@ -847,6 +849,7 @@ def main():
         out["layers"] = bench_layers(args.side_reps, stream, capture, ev)
     if "mid" in legs:
         out["gemm_mid"] = bench_mid(mats, copies, args.side_reps, stream, capture, ev)
+        out["gemm_m128"] = bench_mid(mats, copies, args.side_reps, stream, capture, ev, tokens=128)
     if "moe" in legs:
         out["moe"] = bench_moe(args.side_reps, stream, capture, ev)
     if "batch" in legs:
