@@ -80,9 +80,9 @@ GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "16043
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "11609855197ded27",
                 "bytes_per_launch": 74635230}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "19d8ba033cc0c3b9", "bytes_per_launch": 35192565}
+               "src_sha256_16": "81cae00ede1dceca", "bytes_per_launch": 35192565}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "87a344696de05b82", "bytes_per_launch": 229663143}
+               "src_sha256_16": "5c67f30eb0f16515", "bytes_per_launch": 229721395}
 
 
 def src_hash(files):

@@ -155,11 +155,11 @@ size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
 
 /* Prefill GEMM, m >= 1 tokens: y[m][n], the folds of kq_gemv.  The codes
  * and bsums are the tile image of kq_quantize_q8k_tiles, xs row-major.
- * k <= 2^23 - 256 (KQ_EINVAL above).  m <= 127, and m = 128 or 161..192
- * (an even number of 32-token tiles), run a 32-token tile that unpacks each
- * weight once per 32 tokens, or per 64 when the tiles pair up (in registers
- * for Q6_K, through an LDS panel for Q4_K/Q5_K); other m a 256-token tile
- * that unpacks it once per 256 tokens into LDS.
+ * k <= 2^23 - 256 (KQ_EINVAL above).  m <= 192 runs a 32-token tile that
+ * unpacks each weight once per 32 tokens, or per 64 when the tiles pair up
+ * (33..64 and 97..192 tokens; in registers for Q6_K, through an LDS panel
+ * for Q4_K/Q5_K); m >= 193 a 256-token tile that unpacks it once per 256
+ * tokens into LDS.
  * workspace: NULL, or a 256-byte aligned device buffer of workspace_bytes
  * >= kq_gemm_workspace_bytes bytes (no initial contents needed).  With it,
  * a grid too small to fill the GPU is split along k: for the 256-token tile

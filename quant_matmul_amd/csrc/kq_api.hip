@@ -19,15 +19,11 @@ size_t gemm_mid_workspace_bytes(int64_t n, int64_t k, int64_t m);
 int launch_gemm_grouped(int fmt, const void *w, int64_t w_stride, int64_t experts, const int32_t *tile_expert,
                         int64_t n, int64_t k, const int8_t *xq, const float *xs, const void *xbs, int64_t m,
                         float *y, int32_t *P, int32_t *M, hipStream_t st);
-// token counts up to GEMM_MID_MAX run the 32-token tile, and so do those up
-// to GEMM_MID_PAIRED_MAX whose 32-token tiles pair up evenly (the paired
-// tile beats a 256-token tile that would run at most three-quarters full);
-// the rest run the 256-token prefill tile
-constexpr int64_t GEMM_MID_MAX = 127, GEMM_MID_PAIRED_MAX = 192;
-inline bool gemm_uses_mid(int64_t m)
-{
-    return m <= GEMM_MID_MAX || (m <= GEMM_MID_PAIRED_MAX && ((m + 31) / 32) % 2 == 0);
-}
+// token counts up to GEMM_MID_MAX run the 32-token tile (above 127 tokens
+// its tiles pair up and beat a 256-token tile that would run at most
+// three-quarters full); the rest run the 256-token prefill tile
+constexpr int64_t GEMM_MID_MAX = 192;
+inline bool gemm_uses_mid(int64_t m) { return m <= GEMM_MID_MAX; }
 int launch_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, hipStream_t stream);
 int launch_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, hipStream_t stream);
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,

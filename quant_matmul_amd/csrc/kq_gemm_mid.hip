@@ -1,5 +1,5 @@
 // kq_gemm_mid.hip -- the K-quant x Q8_K matmul for token counts between the
-// GEMV and the prefill tile (9..127 tokens), and the grouped form that runs
+// GEMV and the prefill tile (9..192 tokens), and the grouped form that runs
 // every expert of a mixture-of-experts layer in one launch.
 //
 // Same integer partials and float fold as kq_gemm (K-quant kernel arc page,
@@ -7,8 +7,8 @@
 // workgroup is 4 waves over 128 weight rows x one 32-token tile (a wave: 32
 // rows x 32 tokens, one v_mfma_i32_32x32x32_i8 tile), so each unpacked
 // weight serves 32 tokens; what changes from the 256-token tile is how the
-// weights are unpacked.  When the 32-token tiles pair up evenly (33-64 and
-// 97-127 tokens), the Q4_K/Q5_K workgroup covers 64 rows x two token tiles
+// weights are unpacked.  When the 32-token tiles pair up (2, 4, 5 or 6 of
+// them: 33-64 and 97-192 tokens), the Q4_K/Q5_K workgroup covers 64 rows x two token tiles
 // instead, so each fetched and expanded panel serves 64 tokens, and a Q6_K
 // wave covers both tiles, so each digit it unpacks serves 64 tokens.
 //  * Q4_K/Q5_K: a 32-weight sub-block is one K step, so the MFMA takes the
@@ -501,11 +501,12 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
                     int32_t *P, int32_t *M, int S, hipStream_t st)
 {
     const int64_t mtiles = (m + 31) / 32;
-    // token tiles pair up when their count is even: on 64-row panels
-    // (Q4_K/Q5_K) or within each wave (Q6_K)
-    const bool pair = !GROUPED && mtiles % 2 == 0;
+    // token tiles pair up, on 64-row panels (Q4_K/Q5_K) or within each wave
+    // (Q6_K), when their count is even or five (129-160 tokens: three pairs,
+    // the last one's second tile empty, beat five single tiles)
+    const bool pair = !GROUPED && (mtiles % 2 == 0 || mtiles == 5);
     const int64_t ntiles = pair && FMT != KQ_Q6_K ? (n + 63) / 64 : (n + 127) / 128;
-    const dim3 g((unsigned)(ntiles * (pair ? mtiles / 2 : mtiles) * S)), b(256);
+    const dim3 g((unsigned)(ntiles * (pair ? (mtiles + 1) / 2 : mtiles) * S)), b(256);
     if constexpr (FMT == KQ_Q6_K) {
         if constexpr (!GROUPED) {
             if (pair) {

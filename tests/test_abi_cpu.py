@@ -90,7 +90,7 @@ def test_gemm_workspace_bytes():
     assert kq.kq_gemm_workspace_bytes("q6_k", 2560, 9728, 512) == 1280 + 160 * 3 * tile
     assert kq.kq_gemm_workspace_bytes("q4_k", 9728, 2560, 512) == 0
     assert kq.kq_gemm_workspace_bytes("q4_k", 8192, 2560, 512) == 0  # exactly one round
-    # the 32-token tile (m <= 127): S = 3 partial slices of the m x n output
+    # the 32-token tile (m <= 192): S = 3 partial slices of the m x n output
     assert kq.kq_gemm_workspace_bytes("q4_k", 300, 2560, 100) > 0
     assert kq.kq_gemm_workspace_bytes("q4_k", 300, 300, 130) == 0
     assert kq.kq_gemm_workspace_bytes(9, 300, 2560, 130) == 0

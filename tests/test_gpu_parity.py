@@ -175,9 +175,10 @@ def test_gemv_f32_fused_matches_two_step(fmt, t, n, k):
                                    # the 32-token tile (m <= 127): ragged tokens and rows
                                    (9, 256, 2560), (32, 128, 512), (33, 300, 768), (100, 129, 1024),
                                    (127, 40, 256),
-                                   # 128-192 tokens: paired 32-token tiles when their count is
-                                   # even (176: six tiles), else the 256-token tile (160: five)
-                                   (176, 130, 1024), (160, 64, 512)])
+                                   # 128-192 tokens: paired 32-token tiles (176: six tiles;
+                                   # 160: five, the last pair's second tile empty); 200: the
+                                   # 256-token tile, one ragged block
+                                   (176, 130, 1024), (160, 64, 512), (200, 96, 768)])
 def test_gemm_parity(fmt, m, n, k):
     c = Case(fmt, n, k, m, seed=m + n)
     y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
@@ -270,7 +271,7 @@ def test_gemm_split_parts_meet_through_any_workspace(fmt, n, k, m):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
-@pytest.mark.parametrize("m", [16, 64, 96, 128])  # 64, 128: token tiles paired
+@pytest.mark.parametrize("m", [16, 64, 96, 128, 150])  # 64, 128, 150: token tiles paired
 def test_gemm_mid_full_size_sampled(fmt, n, k, m):
     c = Case(fmt, n, k, m, seed=6)
     y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
