@@ -18,6 +18,7 @@ import pytest
 import oracle
 import synth
 from kq_encode import dequant_fields, encode, random_fields, pack_scale_min
+from q8k_cases import exact_q8k_chunk, quotient_chunks, reciprocal_codes
 
 FMTS = ["q4_k", "q5_k", "q6_k"]
 
@@ -160,6 +161,40 @@ def test_q8k_power_of_two_scaling_is_equivariant():
         assert np.array_equal(xs1, np.ldexp(xs0, e))
 
 
+def test_q8k_code_is_the_rounded_binary32_quotient():
+    # the code of x is rint(binary32(x / d8)) with d8 = binary32(amax / 127),
+    # both correctly rounded, ties to even ("The pieces", kq v2 item: q =
+    # round(x/d) per 256-value chunk), worked out here in exact rationals.
+    # These chunks sit where a reciprocal multiply x * (1/d8) lands on the
+    # other side of a .5 boundary, so that reading fails this pin.
+    x = quotient_chunks(6, seed=31)
+    xq, xs, xbs = oracle.quantize_q8k(x.reshape(2, 768))
+    xq, xs = xq.reshape(6, 256), xs.reshape(6)
+    for c in range(6):
+        codes, d8 = exact_q8k_chunk(x[c])
+        assert float(d8) == float(xs[c])
+        assert np.array_equal(xq[c].astype(np.int64), codes), f"chunk {c}"
+        # the chunk separates the two readings in at least 20 places
+        assert (reciprocal_codes(x[c]) != codes).sum() >= 20
+    assert np.array_equal(xbs.reshape(6, 16), xq.reshape(6, 16, 16).astype(np.int64).sum(-1))
+
+
+def test_q8k_code_definition_on_random_and_tie_chunks():
+    # the same exact definition on ordinary N(0,1) chunks, exact .5 ties at
+    # d8 = 1, tiny magnitudes and a chunk whose amax is negative
+    x = synth.activations(1, 1024, 32).reshape(4, 256)
+    x[1] = 0.0
+    x[1, 0] = -127.0
+    x[1, 1:9] = [2.5, 3.5, -2.5, -3.5, 0.5, 126.5, -0.5, 1.5]
+    x[2] *= np.float32(2.0 ** -60)
+    x[3, 7] = -np.abs(x[3]).max() * np.float32(1.5)
+    xq, xs, _ = oracle.quantize_q8k(x.reshape(1, 1024))
+    for c in range(4):
+        codes, d8 = exact_q8k_chunk(x[c])
+        assert float(d8) == float(xs[0, c])
+        assert np.array_equal(xq[0, 256 * c:256 * (c + 1)].astype(np.int64), codes), f"chunk {c}"
+
+
 # ------------------------------------------------------------ folds ------
 def _brute_partials(fmt, fields, a):
     """int64 brute force of P and M for one superblock: elementwise."""
@@ -296,6 +331,8 @@ _MUTATIONS = {
     # 6-bit packing: wrong high bits for j >= 4
     "pack": ("sc[j] = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);",
              "sc[j] = (s[j + 4] & 15) | ((s[j] >> 6) << 4);"),
+    # the Q8_K quotient taken as a reciprocal multiply
+    "recip": ("float v = c[i] / d8;", "float v = c[i] * (1.0f / d8);"),
 }
 
 
@@ -324,13 +361,14 @@ def test_planted_mistakes_are_caught(name, tmp_path):
         mut.orc_f16_to_double.restype = ctypes.c_double
         oracle._lib = mut
         failed = False
-        for fmt in FMTS:
-            for test in (test_partials_match_elementwise_brute_force,
-                         test_dequantize_matches_format_definition):
-                try:
-                    test(fmt)
-                except AssertionError:
-                    failed = True
+        checks = [lambda f=f, t=t: t(f) for f in FMTS
+                  for t in (test_partials_match_elementwise_brute_force, test_dequantize_matches_format_definition)]
+        checks += [test_q8k_code_is_the_rounded_binary32_quotient, test_q8k_code_definition_on_random_and_tie_chunks]
+        for check in checks:
+            try:
+                check()
+            except AssertionError:
+                failed = True
         assert failed, f"planted mistake {name!r} went unnoticed"
     finally:
         oracle._lib = saved
