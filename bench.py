@@ -160,11 +160,12 @@ def cpu_baseline(seconds):
 
 
 def bench_probes(mats, copies, stream, capture, ev):
-    """Achievable ceilings on this machine (include/kq_probe.h): a plain
+    """Achievable ceilings on this machine (probes/kq_probe.h): a plain
     streaming read of each matrix's plane buffers, rotated over the same
     weight copies the GEMV reads, and a plain int8 32x32x32 MFMA loop."""
     import torch
     import quant_matmul_amd as kq
+    import probes
     sink = torch.zeros(65536 * 256, dtype=torch.int32, device="cuda")
     reps = 8 * copies
     read = []
@@ -174,7 +175,7 @@ def bench_probes(mats, copies, stream, capture, ev):
         for grid in (1024, 2048, 4096, 8192):
             def run(grid=grid):
                 for r in range(reps):
-                    kq.kq_probe_read(pl[r % copies], nbytes, sink, grid)
+                    probes.kq_probe_read(pl[r % copies], nbytes, sink, grid)
             g = capture(run)
             g.replay()
             a, b = ev(), ev()
@@ -193,7 +194,7 @@ def bench_probes(mats, copies, stream, capture, ev):
     for grid in (512, 1024, 2048):
         def run(grid=grid):
             for _ in range(4):
-                kq.kq_probe_mfma_i8(iters, grid, sink)
+                probes.kq_probe_mfma_i8(iters, grid, sink)
         g = capture(run)
         g.replay()
         a, b = ev(), ev()
@@ -224,12 +225,12 @@ def bench_mid(mats, copies, reps, stream, capture, ev, tokens=MID_M):
         x = torch.from_numpy(synth.activations(tokens, k, synth.seed_for(3, 50 + j))).cuda()
         q = ops.q8k_tile_buffers(tokens, k)
         y = torch.empty((tokens, n), device="cuda")
-        ws = ops.gemm_workspace(fmt, n, k, tokens)
+        ws = ops.gemm_tiles_workspace(fmt, n, k, tokens)
 
         def leg(c, kernel_only=False):
             if not kernel_only:
                 kq.kq_quantize_q8k_tiles(x, tokens, k, *q)
-            kq.kq_gemm(fmt, pl[c], n, k, *q, tokens, y, ws)
+            kq.kq_gemm_tiles(fmt, pl[c], n, k, *q, tokens, y, ws)
 
         kq.kq_quantize_q8k_tiles(x, tokens, k, *q)
         g_leg = [capture(leg, c) for c in range(copies)]
@@ -318,6 +319,7 @@ def bench_dense(pool_gib, reps, stream, capture, ev):
 
     import synth
     import quant_matmul_amd as kq
+    import probes
     from quant_matmul_amd import torch_ops as ops
 
     sink = torch.zeros(65536 * 256, dtype=torch.int32, device="cuda")
@@ -333,7 +335,7 @@ def bench_dense(pool_gib, reps, stream, capture, ev):
         q1, qm = ops.quantize_q8k(x1), ops.quantize_q8k_tiles(xm)
         y1 = torch.empty((1, n), device="cuda")
         ym = torch.empty((GEMM_M, n), device="cuda")
-        ws = ops.gemm_workspace(fmt, n, k, GEMM_M)
+        ws = ops.gemm_tiles_workspace(fmt, n, k, GEMM_M)
         nbytes = pl[0].numel()
 
         def gemv_run():
@@ -342,11 +344,11 @@ def bench_dense(pool_gib, reps, stream, capture, ev):
 
         def read_run():
             for r in range(copies):
-                kq.kq_probe_read(pl[r], nbytes, sink, 4096)
+                probes.kq_probe_read(pl[r], nbytes, sink, 4096)
 
         def gemm_run():
             for r in range(copies):
-                kq.kq_gemm(fmt, pl[r], n, k, *qm, GEMM_M, ym, ws)
+                kq.kq_gemm_tiles(fmt, pl[r], n, k, *qm, GEMM_M, ym, ws)
 
         out = {}
         for name, fn in (("gemv", gemv_run), ("read", read_run), ("gemm", gemm_run)):
@@ -492,7 +494,7 @@ def bench_layers(reps, stream, capture, ev):
     qm = {inp: ops.q8k_tile_buffers(GEMM_M, k) for inp, k in LAYER_INPUTS.items()}
     y1 = [torch.empty((1, n), device="cuda") for _, _, n, _, _, _ in layer]
     ym = [torch.empty((GEMM_M, n), device="cuda") for _, _, n, _, _, _ in layer]
-    wss = [ops.gemm_workspace(fmt, n, k, GEMM_M) for _, fmt, n, k, _, _ in layer]
+    wss = [ops.gemm_tiles_workspace(fmt, n, k, GEMM_M) for _, fmt, n, k, _, _ in layer]
 
     def decode():
         for L in range(N_LAYERS):
@@ -506,7 +508,7 @@ def bench_layers(reps, stream, capture, ev):
             for j, (name, fmt, n, k, inp, pl) in enumerate(layer):
                 if j == 0 or inp != layer[j - 1][4]:
                     kq.kq_quantize_q8k_tiles(xm[inp], GEMM_M, k, *qm[inp])
-                kq.kq_gemm(fmt, pl[L], n, k, *qm[inp], GEMM_M, ym[j], wss[j])
+                kq.kq_gemm_tiles(fmt, pl[L], n, k, *qm[inp], GEMM_M, ym[j], wss[j])
 
     # The same token as a model would lay it out: q|k and gate|up, which
     # share an input and a format, packed as one matrix each (rows
@@ -532,7 +534,7 @@ def bench_layers(reps, stream, capture, ev):
     fused_in = ["attn", "attn", "o", "ffn", "down"]
     yf = [torch.empty((1, n), device="cuda") for _, n, _, _ in fused_layer]
     ymf = [torch.empty((GEMM_M, n), device="cuda") for _, n, _, _ in fused_layer]
-    wsf = [ops.gemm_workspace(fmt, n, k, GEMM_M) for fmt, n, k, _ in fused_layer]
+    wsf = [ops.gemm_tiles_workspace(fmt, n, k, GEMM_M) for fmt, n, k, _ in fused_layer]
     torch.cuda.synchronize()
 
     def decode_fused():
@@ -551,7 +553,7 @@ def bench_layers(reps, stream, capture, ev):
             for j, ((fmt, n, k, pl), inp) in enumerate(zip(fused_layer, fused_in)):
                 if j == 0 or inp != fused_in[j - 1]:
                     kq.kq_quantize_q8k_tiles(xm[inp], GEMM_M, k, *qm[inp])
-                kq.kq_gemm(fmt, pl[L], n, k, *qm[inp], GEMM_M, ymf[j], wsf[j])
+                kq.kq_gemm_tiles(fmt, pl[L], n, k, *qm[inp], GEMM_M, ymf[j], wsf[j])
 
     res = {}
     for kind, fn, nrep in (("decode", decode, reps), ("decode_fused", decode_fused, reps),
@@ -618,9 +620,9 @@ def profile_one(spec, reps):
                 kq.kq_gemv(fmt, planes, n, k, *q, t, y)
         else:
             q = ops.quantize_q8k_tiles(x)
-            ws = ops.gemm_workspace(fmt, n, k, t)
+            ws = ops.gemm_tiles_workspace(fmt, n, k, t)
             for _ in range(reps):
-                kq.kq_gemm(fmt, planes, n, k, *q, t, y, ws)
+                kq.kq_gemm_tiles(fmt, planes, n, k, *q, t, y, ws)
     torch.cuda.synchronize()
     print(json.dumps({"profile_one": spec, "reps": reps}), flush=True)
     return 0
@@ -681,7 +683,7 @@ def main():
     ys = [(torch.empty((1, m[1]), device="cuda"), torch.empty((GEMM_M, m[1]), device="cuda"))
           for m in mats]
     # kq_gemm workspaces (zero-filled once; each call leaves them reusable)
-    wss = [ops.gemm_workspace(fmt, n, k, GEMM_M) for fmt, n, k, _ in mats]
+    wss = [ops.gemm_tiles_workspace(fmt, n, k, GEMM_M) for fmt, n, k, _ in mats]
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -704,7 +706,7 @@ def main():
         for j, (fmt, n, k, pl) in enumerate(mats):
             _, _, xm, (xq, xs, xbs) = acts[k]
             kq.kq_quantize_q8k_tiles(xm, GEMM_M, k, xq, xs, xbs)
-            kq.kq_gemm(fmt, pl[c], n, k, xq, xs, xbs, GEMM_M, ys[j][1], wss[j])
+            kq.kq_gemm_tiles(fmt, pl[c], n, k, xq, xs, xbs, GEMM_M, ys[j][1], wss[j])
 
     def kernel_only(kind, j, reps):
         fmt, n, k, pl = mats[j]
@@ -714,7 +716,7 @@ def main():
             if kind == "gemv":
                 kq.kq_gemv(fmt, pl[c], n, k, *q1, 1, ys[j][0])
             else:
-                kq.kq_gemm(fmt, pl[c], n, k, *qm, GEMM_M, ys[j][1], wss[j])
+                kq.kq_gemm_tiles(fmt, pl[c], n, k, *qm, GEMM_M, ys[j][1], wss[j])
 
     def capture(fn, *a):
         g = torch.cuda.CUDAGraph()

@@ -29,15 +29,15 @@
  *  - Buffers.  Every pointer argument except the host side of a copy is a
  *    DEVICE pointer on the current HIP device, owned by the caller.  The
  *    library allocates nothing.  Its only global state is on the host: the
- *    CU count, read once, and an atomic call counter that tags kq_gemm's
+ *    CU count, read once, and an atomic call counter that tags the GEMM's
  *    split counters; calls are reentrant and thread-safe.
  *  - Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  Every call only enqueues work and returns; nothing
  *    synchronises.  Outputs are fully overwritten.
  *  - Layouts.  Row-major and dense: x[t][k], xq[t][k], xs[t][k/256],
  *    xbs[t][k/16], y[t][n], partials[t][n][k/256] -- except the codes and
- *    bsums the GEMM reads, which come in the tile image
- *    (kq_quantize_q8k_tiles).
+ *    bsums that kq_gemm_tiles and kq_gemm_grouped read, which come in the
+ *    tile image (kq_quantize_q8k_tiles).
  *  - Alignment.  w_ggml, w_planes, x, xq and xbs must be 16-byte aligned;
  *    xs, y and the partials 4-byte aligned.
  *  - Errors.  All arguments are checked on the host before any HIP call, so
@@ -149,32 +149,58 @@ int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
 int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float *x, int64_t t,
                 float *y, int8_t *xq, float *xs, int16_t *xbs, void *stream);
 
-/* Bytes of the optional kq_gemm workspace for this shape on the current
- * device (0: kq_gemm would not use one), or 0 on bad arguments. */
+/* Bytes of the workspace kq_gemm and kq_gemm_partials need for this shape on
+ * the current device, or 0 on bad arguments (see kq_gemm). */
 size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
 
-/* Prefill GEMM, m >= 1 tokens: y[m][n], the folds of kq_gemv.  The codes
- * and bsums are the tile image of kq_quantize_q8k_tiles, xs row-major.
- * k <= 2^23 - 256 (KQ_EINVAL above).  m <= 192 runs a 32-token tile that
- * unpacks each weight once per 32 tokens, or per 64 when the tiles pair up
- * (33..64 and 97..192 tokens; in registers for Q6_K, through an LDS panel
- * for Q4_K/Q5_K); m >= 193 a 256-token tile that unpacks it once per 256
- * tokens into LDS.
- * workspace: NULL, or a 256-byte aligned device buffer of workspace_bytes
- * >= kq_gemm_workspace_bytes bytes (no initial contents needed).  With it,
- * a grid too small to fill the GPU is split along k: for the 256-token tile
- * each tile's parts write partial sums to the workspace and the last part of
- * the tile to finish adds them into y (one launch); for the 32-token tile
- * whole-output slices that a second kernel adds.  Both add in split order, so results
- * are the same from call to call (they may differ from the unsplit sum in
- * the last bits, within the fold's float tolerance).  The 256-token tile's parts count in through counter words at the
- * start of the workspace that every call tags as its own, so stale contents
- * are ignored and graph replays may reuse the workspace.  Calls sharing one
- * workspace must be ordered on one stream.  A NULL or too small workspace
- * runs unsplit. */
-int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq_tiles, const float *xs,
-            const uint16_t *xbs_tiles, int64_t m, float *y, void *workspace, size_t workspace_bytes,
-            void *stream);
+/* Prefill GEMM, m >= 1 tokens: y[m][n], the folds of kq_gemv, from the Q8_K
+ * row image that kq_quantize_q8k writes (xq[m][k], xs[m][k/256],
+ * xbs[m][k/16] int16) -- the pages' matmul sequence: quantise to Q8_K, then
+ * dot (K-quant kernel arc page, k5/k6 v2 commit message; the regrain commit
+ * message keeps one activation image per consumed form).
+ * workspace: a 256-byte aligned device buffer of workspace_bytes >=
+ * kq_gemm_workspace_bytes(fmt, n, k, m) bytes (no initial contents needed;
+ * KQ_EINVAL if NULL or smaller).  The call first re-lays the image into the
+ * tile form at the start of the workspace (kq_quantize_q8k_tiles's layout,
+ * bit for bit), then runs kq_gemm_tiles on it with the rest of the workspace
+ * as that call's k-split workspace, so y is bit-identical to
+ * kq_quantize_q8k_tiles + kq_gemm_tiles with the same split.  Calls sharing
+ * one workspace must be ordered on one stream.  k <= 2^23 - 256. */
+int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+            const int16_t *xbs, int64_t m, float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of the optional kq_gemm_tiles workspace for this shape on the current
+ * device (0: kq_gemm_tiles would not use one), or 0 on bad arguments. */
+size_t kq_gemm_tiles_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
+
+/* Token count of the tile kq_gemm / kq_gemm_tiles runs for this shape: 32
+ * (the 32-token tile, whose tiles pair up on 64-row panels where their count
+ * allows) or 256 (the 256-token tile); 0 on bad arguments. */
+int kq_gemm_tile_tokens(int fmt, int64_t n, int64_t k, int64_t m);
+
+/* Prefill GEMM, m >= 1 tokens, on the tile image of kq_quantize_q8k_tiles
+ * (codes and f16 bsums in MFMA operand order, xs row-major): y[m][n], the
+ * folds of kq_gemv.  k <= 2^23 - 256 (KQ_EINVAL above).  m <= 192 runs a
+ * 32-token tile that unpacks each weight once per 32 tokens, or per 64 when
+ * the tiles pair up (33..64 and 97..192 tokens; in registers for Q6_K,
+ * through an LDS panel for Q4_K/Q5_K); m >= 193 a 256-token tile that
+ * unpacks it once per 256 tokens into LDS.
+ * workspace: NULL, or a 256-byte aligned device buffer of workspace_bytes >=
+ * kq_gemm_tiles_workspace_bytes bytes (no initial contents needed).  With
+ * it, a grid too small to fill the GPU is split along k: for the 256-token
+ * tile each tile's parts write partial sums to the workspace and the last
+ * part of the tile to finish adds them into y (one launch); for the 32-token
+ * tile whole-output slices that a second kernel adds.  Both add in split
+ * order, so results are the same from call to call (they may differ from the
+ * unsplit sum in the last bits, within the fold's float tolerance).  The
+ * 256-token tile's parts count in through counter words at the start of the
+ * workspace that every call tags as its own, so stale contents are ignored
+ * and graph replays may reuse the workspace.  Calls sharing one workspace
+ * must be ordered on one stream.  A NULL or too small workspace runs
+ * unsplit. */
+int kq_gemm_tiles(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq_tiles, const float *xs,
+                  const uint16_t *xbs_tiles, int64_t m, float *y, void *workspace, size_t workspace_bytes,
+                  void *stream);
 
 /* kq_gemv that also stores each superblock's int32 partials:
  * P[t][n][k/256] and M[t][n][k/256] (Q6_K: P = iacc - 32*bacc and M = 0;
@@ -190,17 +216,23 @@ int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
  * whose 32-row tile i belongs to expert tile_expert[i] (device
  * int32[ceil(m/32)]).  y[m][n]: row i is row i of the image times that
  * expert's matrix.  A tile whose expert id is outside [0, experts) is left
- * unwritten.  Unsplit; each tile runs the kq_gemm 32-token tile body, so a
- * tile's outputs equal kq_gemm's on the same rows bit for bit. */
+ * unwritten.  Unsplit; each tile runs the kq_gemm_tiles 32-token tile body, so a
+ * tile's outputs equal kq_gemm_tiles's on the same rows bit for bit. */
 int kq_gemm_grouped(int fmt, const void *w_planes, int64_t w_stride, int64_t experts, const int32_t *tile_expert,
                     int64_t n, int64_t k, const int8_t *xq_tiles, const float *xs, const uint16_t *xbs_tiles,
                     int64_t m, float *y, void *stream);
 
-/* kq_gemm (unsplit, no workspace) that also stores the int32 partials, as
- * kq_gemv_partials. */
-int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq_tiles,
-                     const float *xs, const uint16_t *xbs_tiles, int64_t m, float *y, int32_t *P,
-                     int32_t *M, void *stream);
+/* kq_gemm (unsplit) that also stores the int32 partials, as
+ * kq_gemv_partials; same row image and workspace as kq_gemm. */
+int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                     const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* kq_gemm_tiles (unsplit, no workspace) that also stores the int32
+ * partials, as kq_gemv_partials. */
+int kq_gemm_tiles_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq_tiles,
+                           const float *xs, const uint16_t *xbs_tiles, int64_t m, float *y, int32_t *P,
+                           int32_t *M, void *stream);
 
 /* Static text for a status code. */
 const char *kq_strerror(int code);

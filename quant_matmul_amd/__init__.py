@@ -24,11 +24,12 @@ KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 4, 5, 6
 FORMATS = {"q4_k": KQ_Q4_K, "q5_k": KQ_Q5_K, "q6_k": KQ_Q6_K}
 KQ_OK, KQ_EINVAL, KQ_EFORMAT, KQ_EALIGN, KQ_ELAUNCH = 0, -1, -2, -3, -4
 
-# every entry point of include/kq.h and include/kq_probe.h
+# every entry point of include/kq.h
 SYMBOLS = ("kq_record_bytes", "kq_packed_bytes", "kq_pack", "kq_unpack", "kq_quantize_q8k",
            "kq_q8k_tiles_bytes", "kq_quantize_q8k_tiles", "kq_quantize_q8k_tiles_gather", "kq_gemv",
-           "kq_gemv_f32", "kq_gemm_workspace_bytes", "kq_gemm", "kq_gemm_grouped", "kq_gemv_partials",
-           "kq_gemm_partials", "kq_strerror", "kq_probe_read", "kq_probe_mfma_i8")
+           "kq_gemv_f32", "kq_gemm_workspace_bytes", "kq_gemm", "kq_gemm_tiles_workspace_bytes",
+           "kq_gemm_tile_tokens", "kq_gemm_tiles", "kq_gemm_grouped", "kq_gemv_partials", "kq_gemm_partials",
+           "kq_gemm_tiles_partials", "kq_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python quant_matmul_amd/build.py`")
@@ -51,16 +52,20 @@ lib.kq_gemv.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
 lib.kq_gemm_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
 lib.kq_gemm_workspace_bytes.restype = ctypes.c_size_t
 lib.kq_gemm.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, ctypes.c_size_t, _p]
+lib.kq_gemm_tiles_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
+lib.kq_gemm_tiles_workspace_bytes.restype = ctypes.c_size_t
+lib.kq_gemm_tile_tokens.argtypes = [_int, _i64, _i64, _i64]
+lib.kq_gemm_tile_tokens.restype = _int
+lib.kq_gemm_tiles.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, ctypes.c_size_t, _p]
 lib.kq_gemv_f32.argtypes = [_int, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
 lib.kq_gemv_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
-lib.kq_gemm_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
-lib.kq_probe_read.argtypes = [_p, ctypes.c_size_t, _p, _int, _p]
-lib.kq_probe_mfma_i8.argtypes = [_i64, _int, _p, _p]
+lib.kq_gemm_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p, ctypes.c_size_t, _p]
+lib.kq_gemm_tiles_partials.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _p, _p]
 lib.kq_strerror.argtypes = [_int]
 lib.kq_strerror.restype = ctypes.c_char_p
 for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_quantize_q8k_tiles", "kq_quantize_q8k_tiles_gather",
-           "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemm_grouped",
-           "kq_gemv_partials", "kq_gemm_partials", "kq_probe_read", "kq_probe_mfma_i8"):
+           "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemm_tiles", "kq_gemm_grouped",
+           "kq_gemv_partials", "kq_gemm_partials", "kq_gemm_tiles_partials"):
     getattr(lib, _f).restype = _int
 
 
@@ -142,16 +147,35 @@ def kq_gemv_f32(fmt, w_planes, n: int, k: int, x, t: int, y, xq=None, xs=None, x
                         _ptr(xbs), _stream(stream)), "kq_gemv_f32")
 
 
+def _nbytes(buf, nbytes):
+    if nbytes is not None:
+        return nbytes
+    return 0 if buf is None or isinstance(buf, int) else buf.numel() * buf.element_size()
+
+
 def kq_gemm_workspace_bytes(fmt, n: int, k: int, m: int) -> int:
     return lib.kq_gemm_workspace_bytes(_fmt(fmt), n, k, m)
 
 
-def kq_gemm(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, workspace=None, workspace_bytes=None,
-            stream=None):
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _ok(lib.kq_gemm(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), m, _ptr(y),
-                    _ptr(workspace), workspace_bytes, _stream(stream)), "kq_gemm")
+def kq_gemm(fmt, w_planes, n: int, k: int, xq, xs, xbs, m: int, y, workspace, workspace_bytes=None, stream=None):
+    """GEMM on the row image of kq_quantize_q8k (workspace required)."""
+    _ok(lib.kq_gemm(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), m, _ptr(y),
+                    _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)), "kq_gemm")
+
+
+def kq_gemm_tiles_workspace_bytes(fmt, n: int, k: int, m: int) -> int:
+    return lib.kq_gemm_tiles_workspace_bytes(_fmt(fmt), n, k, m)
+
+
+def kq_gemm_tile_tokens(fmt, n: int, k: int, m: int) -> int:
+    return lib.kq_gemm_tile_tokens(_fmt(fmt), n, k, m)
+
+
+def kq_gemm_tiles(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, workspace=None,
+                  workspace_bytes=None, stream=None):
+    """GEMM on the tile image of kq_quantize_q8k_tiles (workspace optional)."""
+    _ok(lib.kq_gemm_tiles(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), m, _ptr(y),
+                          _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)), "kq_gemm_tiles")
 
 
 def kq_gemm_grouped(fmt, w_planes, w_stride: int, experts: int, tile_expert, n: int, k: int, xq_tiles, xs, xbs,
@@ -165,20 +189,17 @@ def kq_gemv_partials(fmt, w_planes, n: int, k: int, xq, xs, xbs, t: int, y, P, M
                              _ptr(y), _ptr(P), _ptr(M), _stream(stream)), "kq_gemv_partials")
 
 
-def kq_gemm_partials(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, P, M, stream=None):
-    _ok(lib.kq_gemm_partials(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), m,
-                             _ptr(y), _ptr(P), _ptr(M), _stream(stream)), "kq_gemm_partials")
+def kq_gemm_partials(fmt, w_planes, n: int, k: int, xq, xs, xbs, m: int, y, P, M, workspace, workspace_bytes=None,
+                     stream=None):
+    _ok(lib.kq_gemm_partials(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), m, _ptr(y), _ptr(P),
+                             _ptr(M), _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)),
+        "kq_gemm_partials")
+
+
+def kq_gemm_tiles_partials(fmt, w_planes, n: int, k: int, xq_tiles, xs, xbs, m: int, y, P, M, stream=None):
+    _ok(lib.kq_gemm_tiles_partials(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq_tiles), _ptr(xs), _ptr(xbs), m,
+                                   _ptr(y), _ptr(P), _ptr(M), _stream(stream)), "kq_gemm_tiles_partials")
 
 
 def kq_strerror(code: int) -> str:
     return lib.kq_strerror(code).decode()
-
-
-def kq_probe_read(buf, nbytes: int, sink, grid: int, stream=None):
-    """Streaming-read probe (include/kq_probe.h): reads nbytes at buf once."""
-    _ok(lib.kq_probe_read(_ptr(buf), nbytes, _ptr(sink), grid, _stream(stream)), "kq_probe_read")
-
-
-def kq_probe_mfma_i8(iters: int, grid: int, sink, stream=None):
-    """Matrix-core probe (include/kq_probe.h): grid*4*iters*4 int8 32x32x32 MFMAs."""
-    _ok(lib.kq_probe_mfma_i8(iters, grid, _ptr(sink), _stream(stream)), "kq_probe_mfma_i8")

@@ -1,4 +1,6 @@
-"""Build libkq.so (the kq C ABI + its gfx950 kernels) in-tree with hipcc.
+"""Build libkq.so (the kq C ABI + its gfx950 kernels) in-tree with hipcc,
+and the benchmark's measurement probes (probes/libkq_probe.so, not part of
+the matmul library).
 
     python quant_matmul_amd/build.py
 
@@ -16,8 +18,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
-SOURCES = ["kq_api.hip", "kq_quantize.hip", "kq_pack.hip", "kq_gemv.hip", "kq_gemm.hip", "kq_gemm_mid.hip",
-           "kq_probe.hip"]
+SOURCES = ["kq_api.hip", "kq_quantize.hip", "kq_pack.hip", "kq_gemv.hip", "kq_gemm.hip", "kq_gemm_mid.hip"]
+PROBE_DIR = os.path.join(ROOT, "probes")
+PROBE_SRC = os.path.join(PROBE_DIR, "kq_probe.hip")
+PROBE_LIB = os.path.join(PROBE_DIR, "libkq_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -30,8 +34,9 @@ FLAGS = [
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    obj = os.path.join(OBJ, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-I" + PROBE_DIR, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -40,16 +45,18 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+    srcs = SOURCES + [PROBE_SRC]
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    for lib, parts in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *parts]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 

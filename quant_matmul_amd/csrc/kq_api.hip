@@ -10,6 +10,8 @@ int launch_quantize_q8k(const float *x, int64_t t, int64_t k, int8_t *xq, float 
                         hipStream_t stream);
 int launch_quantize_q8k_tiles(const float *x, int64_t t, int64_t k, int8_t *xq, float *xs, int16_t *xbs,
                               hipStream_t stream);
+int launch_relay_tiles(const int8_t *xq, const int16_t *xbs, int64_t m, int64_t k, int8_t *xqt, uint16_t *xbt,
+                       hipStream_t stream);
 int launch_quantize_q8k_tiles_gather(const float *x, int64_t t, const int32_t *src, int64_t m, int64_t k,
                                      int8_t *xq, float *xs, int16_t *xbs, hipStream_t stream);
 int launch_gemm_mid(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -178,14 +180,20 @@ int kq_gemv_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
     return kq::launch_gemv(fmt, w_planes, n, k, xq, xs, xbs, t, y, P, M, (hipStream_t)stream);
 }
 
-size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m)
+size_t kq_gemm_tiles_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m)
 {
     if (!known(fmt) || check_nk(n, k) || m < 1 || m > INT_MAX || k > kq::GEMM_KMAX) return 0;
     return kq::gemm_uses_mid(m) ? kq::gemm_mid_workspace_bytes(n, k, m) : kq::gemm_workspace_bytes(n, k, m);
 }
 
-int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-            const uint16_t *xbs, int64_t m, float *y, void *workspace, size_t workspace_bytes, void *stream)
+int kq_gemm_tile_tokens(int fmt, int64_t n, int64_t k, int64_t m)
+{
+    if (!known(fmt) || check_nk(n, k) || m < 1 || m > INT_MAX || k > kq::GEMM_KMAX) return 0;
+    return kq::gemm_uses_mid(m) ? 32 : 256;
+}
+
+int kq_gemm_tiles(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                  const uint16_t *xbs, int64_t m, float *y, void *workspace, size_t workspace_bytes, void *stream)
 {
     int rc = check_matmul(fmt, w_planes, n, k, xq, xs, (const int16_t *)xbs, m, INT_MAX, y, nullptr, nullptr,
                           false);
@@ -212,14 +220,72 @@ int kq_gemm_grouped(int fmt, const void *w_planes, int64_t w_stride, int64_t exp
                                    nullptr, nullptr, (hipStream_t)stream);
 }
 
-int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
-                     const uint16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *stream)
+int kq_gemm_tiles_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                           const uint16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *stream)
 {
     int rc = check_matmul(fmt, w_planes, n, k, xq, xs, (const int16_t *)xbs, m, INT_MAX, y, P, M, true);
     if (rc) return rc;
     if (kq::gemm_uses_mid(m))
         return kq::launch_gemm_mid(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, nullptr, 0, (hipStream_t)stream);
     return kq::launch_gemm(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, nullptr, 0, (hipStream_t)stream);
+}
+
+// The row-image GEMM's workspace: the tile image of the m tokens (codes, then
+// f16 bsums, each 256-byte aligned), then the tile GEMM's k-split workspace.
+struct RowWs {
+    size_t codes, bsums, split, total;
+};
+
+static RowWs row_ws(int fmt, int64_t n, int64_t k, int64_t m)
+{
+    RowWs w{};
+    const size_t tb = kq_q8k_tiles_bytes(m, k);
+    if (!tb) return w;
+    w.codes = 0;
+    w.bsums = (size_t)kq::align256((int64_t)tb);
+    w.split = w.bsums + (size_t)kq::align256((int64_t)(tb / 8));
+    w.total = w.split + kq_gemm_tiles_workspace_bytes(fmt, n, k, m);
+    return w;
+}
+
+size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m)
+{
+    if (!known(fmt) || check_nk(n, k) || m < 1 || m > INT_MAX || k > kq::GEMM_KMAX) return 0;
+    return row_ws(fmt, n, k, m).total;
+}
+
+// the row-image calls: re-lay into the workspace, then the tile GEMM
+static int gemm_rows(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                     const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *workspace,
+                     size_t workspace_bytes, void *stream)
+{
+    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, m, INT_MAX, y, P, M, P != nullptr);
+    if (rc) return rc;
+    if ((m + 31) * (k / kq::QK) > ((int64_t)1 << 32)) return KQ_EINVAL;
+    const RowWs l = row_ws(fmt, n, k, m);
+    if (!workspace || workspace_bytes < l.total) return KQ_EINVAL;
+    if (!aligned(workspace, 256)) return KQ_EALIGN;
+    char *ws = (char *)workspace;
+    int8_t *xqt = (int8_t *)(ws + l.codes);
+    uint16_t *xbt = (uint16_t *)(ws + l.bsums);
+    rc = kq::launch_relay_tiles(xq, xbs, m, k, xqt, xbt, (hipStream_t)stream);
+    if (rc) return rc;
+    if (P) return kq_gemm_tiles_partials(fmt, w_planes, n, k, xqt, xs, xbt, m, y, P, M, stream);
+    return kq_gemm_tiles(fmt, w_planes, n, k, xqt, xs, xbt, m, y, ws + l.split, workspace_bytes - l.split, stream);
+}
+
+int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+            const int16_t *xbs, int64_t m, float *y, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return gemm_rows(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                     const int16_t *xbs, int64_t m, float *y, int32_t *P, int32_t *M, void *workspace,
+                     size_t workspace_bytes, void *stream)
+{
+    if (!P) return KQ_EINVAL;
+    return gemm_rows(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, workspace, workspace_bytes, stream);
 }
 
 const char *kq_strerror(int code)

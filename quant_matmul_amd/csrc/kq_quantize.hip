@@ -214,3 +214,54 @@ int launch_quantize_q8k_tiles_gather(const float *x, int64_t t, const int32_t *s
 }
 
 }  // namespace kq
+
+namespace kq {
+
+// Row image -> tile image (the GEMM's operand order), for callers holding the
+// image kq_quantize_q8k writes.  Thread i writes the i-th 16-byte piece of the
+// tile codes, so the stores are one linear stream: piece i is codes
+// 32c + 16q .. +15 of token 32g + r, with i = ((g*(k/32) + c)*2 + q)*32 + r.
+// Those 16 codes are exactly bsum group 2c + q of the token, whose int16 sum
+// goes to its f16 slot (exact: |bsum| <= 2032).  Tokens m .. rows-1 (the
+// padding up to a multiple of 32) get zero codes and zero bsums.  Only bytes
+// move, so the result is bit-identical to kq_quantize_q8k_tiles on the same
+// activations.
+__global__ __launch_bounds__(256) void relay_tiles_kernel(const int8_t *__restrict__ xq,
+                                                          const int16_t *__restrict__ xbs, int64_t m, int64_t rows,
+                                                          int nsb, int8_t *__restrict__ xqt,
+                                                          _Float16 *__restrict__ xbt)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t kc = (int64_t)nsb * 8;  // 32-code chunks per row
+    if (i >= rows * kc * 2) return;
+    const int r = (int)(i & 31);
+    const int64_t rest = i >> 5;
+    const int q = (int)(rest & 1);
+    const int64_t gc = rest >> 1;
+    const int64_t g = gc / kc, c = gc - g * kc;
+    const int64_t row = g * 32 + r;
+    const int64_t p = 2 * c + q;  // 16-code piece of the row = its bsum group
+    uint4 v = make_uint4(0, 0, 0, 0);
+    int b = 0;
+    if (row < m) {
+        v = *reinterpret_cast<const uint4 *>(xq + row * kc * 32 + 16 * p);
+        b = xbs[row * kc * 2 + p];
+    }
+    *reinterpret_cast<uint4 *>(xqt + i * 16) = v;
+    const int64_t s = p >> 4;
+    const int j = (int)(p & 15);
+    xbt[((g * nsb + s) * 64 + (j >> 3) * 32 + r) * 8 + (j & 7)] = (_Float16)b;
+}
+
+int launch_relay_tiles(const int8_t *xq, const int16_t *xbs, int64_t m, int64_t k, int8_t *xqt, uint16_t *xbt,
+                       hipStream_t stream)
+{
+    const int nsb = (int)(k / QK);
+    const int64_t rows = (m + 31) / 32 * 32;
+    const int64_t threads = rows * (k / 16);
+    hipLaunchKernelGGL(relay_tiles_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, xq, xbs, m,
+                       rows, nsb, xqt, reinterpret_cast<_Float16 *>(xbt));
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
+}
+
+}  // namespace kq

@@ -8,10 +8,10 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (kq_gemm, kq_gemm_grouped, kq_gemm_partials, kq_gemm_workspace_bytes, kq_gemv, kq_gemv_f32, kq_gemv_partials, kq_pack,
-               kq_packed_bytes, kq_q8k_tiles_bytes, kq_quantize_q8k, kq_quantize_q8k_tiles,
-               kq_quantize_q8k_tiles_gather,
-               kq_record_bytes, kq_unpack)
+from . import (kq_gemm, kq_gemm_grouped, kq_gemm_partials, kq_gemm_tiles, kq_gemm_tiles_partials,
+               kq_gemm_tiles_workspace_bytes, kq_gemm_workspace_bytes, kq_gemv, kq_gemv_f32, kq_gemv_partials,
+               kq_pack, kq_packed_bytes, kq_q8k_tiles_bytes, kq_quantize_q8k, kq_quantize_q8k_tiles,
+               kq_quantize_q8k_tiles_gather, kq_record_bytes, kq_unpack)
 
 QK = 256
 
@@ -108,33 +108,59 @@ def gemv_f32(fmt, planes, n: int, k: int, x: torch.Tensor, keep_image: bool = Fa
     return (y, q8) if keep_image else y
 
 
-def gemm_workspace(fmt, n: int, k: int, m: int, device="cuda"):
-    """A kq_gemm workspace for this shape (None if it takes none)."""
-    nb = kq_gemm_workspace_bytes(fmt, n, k, m)
-    return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+def gemm_workspace(fmt, n: int, k: int, m: int, device="cuda") -> torch.Tensor:
+    """The workspace kq_gemm needs for this shape (row image re-laid as the
+    tile image, plus the k-split space)."""
+    return torch.empty(kq_gemm_workspace_bytes(fmt, n, k, m), dtype=torch.uint8, device=device)
 
 
-def gemm(fmt, planes, n: int, k: int, q8t, workspace="auto", stream=None) -> torch.Tensor:
-    """q8t: the GEMM's image (code tiles, xs, bsum tiles), as from
-    quantize_q8k_tiles.  workspace: "auto" allocates one, None runs unsplit."""
-    xq, xs, xbs = q8t
-    m = xs.shape[0]
-    if isinstance(workspace, str):
+def gemm(fmt, planes, n: int, k: int, q8, workspace=None, stream=None) -> torch.Tensor:
+    """q8: the row image (xq, xs, xbs) of kq_quantize_q8k.  workspace: None
+    allocates one of kq_gemm_workspace_bytes."""
+    xq, xs, xbs = q8
+    m = xq.shape[0]
+    if workspace is None:
         workspace = gemm_workspace(fmt, n, k, m, xq.device)
     y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
     kq_gemm(fmt, planes, n, k, xq, xs, xbs, m, y, workspace, stream=stream)
     return y
 
 
+def gemm_tiles_workspace(fmt, n: int, k: int, m: int, device="cuda"):
+    """A kq_gemm_tiles workspace for this shape (None if it takes none)."""
+    nb = kq_gemm_tiles_workspace_bytes(fmt, n, k, m)
+    return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+
+
+def gemm_tiles(fmt, planes, n: int, k: int, q8t, workspace="auto", stream=None) -> torch.Tensor:
+    """q8t: the GEMM's tile image (code tiles, xs, bsum tiles), as from
+    quantize_q8k_tiles.  workspace: "auto" allocates one, None runs unsplit."""
+    xq, xs, xbs = q8t
+    m = xs.shape[0]
+    if isinstance(workspace, str):
+        workspace = gemm_tiles_workspace(fmt, n, k, m, xq.device)
+    y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    kq_gemm_tiles(fmt, planes, n, k, xq, xs, xbs, m, y, workspace, stream=stream)
+    return y
+
+
 def matmul_partials(kind: str, fmt, planes, n: int, k: int, q8, stream=None):
-    """(y, P, M) from kq_gemv_partials (kind 'gemv', row image) or
-    kq_gemm_partials (kind 'gemm', tile image)."""
+    """(y, P, M) from kq_gemv_partials (kind 'gemv', row image),
+    kq_gemm_partials (kind 'gemm', row image) or kq_gemm_tiles_partials
+    (kind 'gemm_tiles', tile image)."""
     xq, xs, xbs = q8
     t = xs.shape[0]
     dev = xq.device
     y = torch.empty((t, n), dtype=torch.float32, device=dev)
     P = torch.empty((t, n, k // QK), dtype=torch.int32, device=dev)
     M = torch.empty((t, n, k // QK), dtype=torch.int32, device=dev)
-    f = kq_gemv_partials if kind == "gemv" else kq_gemm_partials
-    f(fmt, planes, n, k, xq, xs, xbs, t, y, P, M, stream)
+    if kind == "gemv":
+        kq_gemv_partials(fmt, planes, n, k, xq, xs, xbs, t, y, P, M, stream)
+    elif kind == "gemm":
+        kq_gemm_partials(fmt, planes, n, k, xq, xs, xbs, t, y, P, M, gemm_workspace(fmt, n, k, t, dev),
+                         stream=stream)
+    elif kind == "gemm_tiles":
+        kq_gemm_tiles_partials(fmt, planes, n, k, xq, xs, xbs, t, y, P, M, stream)
+    else:
+        raise ValueError(kind)
     return y, P, M

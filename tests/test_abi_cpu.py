@@ -1,32 +1,41 @@
-"""CPU tier: libkq.so loads, exports every entry point include/kq.h and
-include/kq_probe.h declare, and rejects bad arguments with the documented status code before
-any HIP call (so these run on a host without a GPU; no call here reaches a
-kernel launch)."""
+"""CPU tier: libkq.so loads, exports every entry point include/kq.h declares
+(and the benchmark's probe library every entry point of probes/kq_probe.h),
+and rejects bad arguments with the documented status code before any HIP
+call (so these run on a host without a GPU; no call here reaches a kernel
+launch)."""
 import os
 import re
 
 import pytest
 
+import probes
 import quant_matmul_amd as kq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("kq.h", "kq_probe.h")]
+HEADERS = [os.path.join(ROOT, "include", "kq.h")]
+PROBE_HEADER = os.path.join(ROOT, "probes", "kq_probe.h")
 
 GOOD16 = 0x10000   # fake but 16-byte aligned "device pointers": never dereferenced,
 GOOD16B = 0x20000  # every call below fails validation first
 ODD = 0x10001
 
 
-def header_symbols():
-    text = "".join(open(h).read() for h in HEADERS)
+def header_symbols(headers):
+    text = "".join(open(h).read() for h in headers)
     return sorted(set(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
-    names = header_symbols()
+    names = header_symbols(HEADERS)
     assert set(names) == set(kq.SYMBOLS)
     for name in names:
         assert hasattr(kq.lib, name), name
+    # the probes live in their own library, not in libkq.so
+    pnames = header_symbols([PROBE_HEADER])
+    assert set(pnames) == set(probes.SYMBOLS)
+    for name in pnames:
+        assert hasattr(probes.lib, name), name
+        assert not hasattr(kq.lib, name), name
 
 
 def test_record_and_packed_bytes():
@@ -65,43 +74,82 @@ def test_gemv_argument_checks():
         assert _gemv(**{name: ODD}) == kq.KQ_EALIGN, name
 
 
-def _gemm(fmt=4, w=GOOD16, n=16, k=256, xq=GOOD16, xs=GOOD16, xbs=GOOD16, m=4, y=GOOD16, ws=None, wsb=0):
+def _gemm_tiles(fmt=4, w=GOOD16, n=16, k=256, xq=GOOD16, xs=GOOD16, xbs=GOOD16, m=4, y=GOOD16, ws=None, wsb=0):
+    return kq.lib.kq_gemm_tiles(fmt, w, n, k, xq, xs, xbs, m, y, ws, wsb, None)
+
+
+def _gemm(fmt=4, w=GOOD16, n=16, k=256, xq=GOOD16, xs=GOOD16, xbs=GOOD16, m=4, y=GOOD16, ws=GOOD16B, wsb=None):
+    if wsb is None:
+        wsb = kq.kq_gemm_workspace_bytes(fmt, n, k, m)
     return kq.lib.kq_gemm(fmt, w, n, k, xq, xs, xbs, m, y, ws, wsb, None)
 
 
-def test_gemm_argument_checks():
+def test_gemm_tiles_argument_checks():
+    assert _gemm_tiles(fmt=8) == kq.KQ_EFORMAT
+    assert _gemm_tiles(k=512 + 16) == kq.KQ_EINVAL
+    assert _gemm_tiles(m=0) == kq.KQ_EINVAL
+    assert _gemm_tiles(xq=None) == kq.KQ_EINVAL
+    assert _gemm_tiles(w=GOOD16 + 8) == kq.KQ_EALIGN
+    # the workspace is optional, and 256-byte aligned when given
+    assert _gemm_tiles(ws=GOOD16 + 16, wsb=1 << 20, y=ODD) == kq.KQ_EALIGN
+    assert _gemm_tiles(ws=GOOD16 + 16, wsb=1 << 20) == kq.KQ_EALIGN
+
+
+def test_gemm_row_image_argument_checks():
+    # kq_gemm reads kq_quantize_q8k's row image and needs its workspace
     assert _gemm(fmt=8) == kq.KQ_EFORMAT
     assert _gemm(k=512 + 16) == kq.KQ_EINVAL
     assert _gemm(m=0) == kq.KQ_EINVAL
-    assert _gemm(xq=None) == kq.KQ_EINVAL
-    assert _gemm(w=GOOD16 + 8) == kq.KQ_EALIGN
-    # the workspace is optional, and 256-byte aligned when given
-    assert _gemm(ws=GOOD16 + 16, wsb=1 << 20, y=ODD) == kq.KQ_EALIGN
-    assert _gemm(ws=GOOD16 + 16, wsb=1 << 20) == kq.KQ_EALIGN
+    assert _gemm(xbs=None) == kq.KQ_EINVAL
+    assert _gemm(ws=None) == kq.KQ_EINVAL
+    need = kq.kq_gemm_workspace_bytes(4, 16, 256, 4)
+    assert _gemm(wsb=need - 1) == kq.KQ_EINVAL
+    assert _gemm(ws=GOOD16B + 16) == kq.KQ_EALIGN
+    assert _gemm(xbs=GOOD16 + 8) == kq.KQ_EALIGN  # the row image's int16 bsums: 16-byte aligned
+    p = kq.lib.kq_gemm_partials
+    assert p(4, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, GOOD16, GOOD16, None, need, None) == kq.KQ_EINVAL
+    assert p(4, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None, GOOD16, GOOD16B, need, None) == kq.KQ_EINVAL
 
 
 def test_gemm_workspace_bytes():
     # on 256 CUs (2 x 256 workgroup slots; a host without a GPU assumes 256):
     # W_down at pp512 (160 tiles of 256 x 32) splits all its tiles in 3,
-    # W_up (608 tiles, more than one round) runs unsplit; the workspace is one
-    # 8-byte counter per split tile (rounded up to 256 bytes), then the
-    # partial tiles
+    # W_up (608 tiles, more than one round) runs unsplit; the tile GEMM's
+    # workspace is one 8-byte counter per split tile (rounded up to 256
+    # bytes), then the partial tiles
     tile = 256 * 32 * 4
-    assert kq.kq_gemm_workspace_bytes("q6_k", 2560, 9728, 512) == 1280 + 160 * 3 * tile
-    assert kq.kq_gemm_workspace_bytes("q4_k", 9728, 2560, 512) == 0
-    assert kq.kq_gemm_workspace_bytes("q4_k", 8192, 2560, 512) == 0  # exactly one round
+    assert kq.kq_gemm_tiles_workspace_bytes("q6_k", 2560, 9728, 512) == 1280 + 160 * 3 * tile
+    assert kq.kq_gemm_tiles_workspace_bytes("q4_k", 9728, 2560, 512) == 0
+    assert kq.kq_gemm_tiles_workspace_bytes("q4_k", 8192, 2560, 512) == 0  # exactly one round
     # the 32-token tile (m <= 192): S = 3 partial slices of the m x n output
-    assert kq.kq_gemm_workspace_bytes("q4_k", 300, 2560, 100) > 0
-    assert kq.kq_gemm_workspace_bytes("q4_k", 300, 300, 130) == 0
+    assert kq.kq_gemm_tiles_workspace_bytes("q4_k", 300, 2560, 100) > 0
+    assert kq.kq_gemm_tiles_workspace_bytes("q4_k", 300, 300, 130) == 0
+    assert kq.kq_gemm_tiles_workspace_bytes(9, 300, 2560, 130) == 0
+    # kq_gemm's workspace: the tile image (codes, then f16 bsums, each
+    # 256-byte aligned) in front of the tile GEMM's own
+    for fmt, n, k, m in (("q6_k", 2560, 9728, 512), ("q4_k", 9728, 2560, 512), ("q5_k", 300, 2560, 100),
+                         ("q4_k", 17, 256, 1)):
+        codes = kq.kq_q8k_tiles_bytes(m, k)
+        img = (codes + 255) // 256 * 256 + (codes // 8 + 255) // 256 * 256
+        assert kq.kq_gemm_workspace_bytes(fmt, n, k, m) == img + kq.kq_gemm_tiles_workspace_bytes(fmt, n, k, m)
     assert kq.kq_gemm_workspace_bytes(9, 300, 2560, 130) == 0
+
+
+def test_gemm_tile_choice():
+    # m <= 192: the 32-token tile; from 193 tokens the 256-token tile
+    for m, tok in ((1, 32), (64, 32), (192, 32), (193, 256), (200, 256), (512, 256)):
+        assert kq.kq_gemm_tile_tokens("q4_k", 9728, 2560, m) == tok
+    assert kq.kq_gemm_tile_tokens("q4_k", 9728, 300, 64) == 0
+    assert kq.kq_gemm_tile_tokens(3, 9728, 2560, 64) == 0
 
 
 def test_gemm_k_bound():
     kmax = (1 << 23) - 256
-    assert _gemm(k=kmax + 256) == kq.KQ_EINVAL
+    assert _gemm_tiles(k=kmax + 256) == kq.KQ_EINVAL
+    assert _gemm(k=kmax + 256, wsb=1 << 40) == kq.KQ_EINVAL
     # the bound is the GEMM's: the GEMV takes the same k (fails later, on alignment)
     assert kq.lib.kq_gemv(4, GOOD16, 16, kmax + 256, GOOD16, GOOD16, GOOD16, 1, ODD, None) == kq.KQ_EALIGN
-    assert _gemm(k=kmax, y=ODD) == kq.KQ_EALIGN
+    assert _gemm_tiles(k=kmax, y=ODD) == kq.KQ_EALIGN
 
 
 def test_tile_image_bytes_and_checks():
@@ -140,7 +188,7 @@ def test_gather_and_grouped_argument_checks():
 
 
 def test_partials_argument_checks():
-    for f in (kq.lib.kq_gemv_partials, kq.lib.kq_gemm_partials):
+    for f in (kq.lib.kq_gemv_partials, kq.lib.kq_gemm_tiles_partials):
         # P missing
         assert f(4, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 1, GOOD16, None, GOOD16, None) == kq.KQ_EINVAL
         # M missing is an error for Q4_K / Q5_K ...
@@ -190,7 +238,7 @@ def test_strerror_and_python_error():
 
 
 def test_probe_arg_checks():
-    lib = kq.lib
+    lib = probes.lib
     assert lib.kq_probe_read(None, 1024, GOOD16, 256, None) == kq.KQ_EINVAL
     assert lib.kq_probe_read(GOOD16, 1000, GOOD16, 256, None) == kq.KQ_EINVAL  # not a multiple of 16
     assert lib.kq_probe_read(GOOD16, 1024, GOOD16, 0, None) == kq.KQ_EINVAL

@@ -1,6 +1,6 @@
 """GPU tier: the grouped GEMM of a mixture-of-experts layer (one launch over
 all experts) and the gather-quantiser that fills its tile image, against
-the CPU oracle on each expert's routed rows, and bit for bit against kq_gemm
+the CPU oracle on each expert's routed rows, and bit for bit against kq_gemm_tiles
 run expert by expert on the same image rows."""
 import numpy as np
 import pytest
@@ -62,10 +62,10 @@ def test_grouped_gemm_matches_oracle_and_per_expert(fmt, tokens, experts, top, n
         y_o = oracle.matmul(fmt, c.recs[e], *q)
         R = oracle.rowmag(fmt, c.recs[e], q[0], q[1])
         assert np.all(np.abs(yh[s0:s0 + cnt].astype(np.float64) - y_o) <= TOL * R), f"expert {e}"
-        # the same rows through kq_gemm (32-token tile), expert by expert
+        # the same rows through kq_gemm_tiles (32-token tile), expert by expert
         mp = -(-cnt // 32) * 32
         ye = torch.empty((mp, n), device="cuda")
-        kq.kq_gemm(fmt, c.planes.data_ptr() + e * c.stride, n, k, xq.data_ptr() + s0 * k,
+        kq.kq_gemm_tiles(fmt, c.planes.data_ptr() + e * c.stride, n, k, xq.data_ptr() + s0 * k,
                    xs.data_ptr() + s0 * nsb * 4, xbs.data_ptr() + s0 * (k // 16) * 2, mp, ye)
         assert torch.equal(ye, y[s0:s0 + mp]), f"expert {e}: grouped and per-expert differ"
 

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import synth
+from q8k_cases import quotient_chunks
 from q8k_tiles import bsum_tiles, from_bsum_tiles, from_tiles, to_tiles
 from quant_matmul_amd import torch_ops as ops
 import quant_matmul_amd as kq
@@ -44,6 +45,13 @@ class Case:
         self.q8t = (dev(to_tiles(self.q8_host[0])), self.q8[1], dev(bsum_tiles(self.q8_host[2])))
 
     def oracle_rows(self, rows=None):
+        key = None if rows is None else tuple(rows)
+        cache = self.__dict__.setdefault("_oracle", {})
+        if key not in cache:
+            cache[key] = self._oracle_rows(rows)
+        return cache[key]
+
+    def _oracle_rows(self, rows):
         recs = self.recs if rows is None else self.recs[rows]
         xq, xs, xbs = self.q8_host
         P, M = oracle.partials(self.fmt, recs, xq, xbs)
@@ -109,6 +117,43 @@ def test_quantize_tiles_bit_exact(t, k):
     assert not bs[t:].any()
 
 
+@pytest.mark.parametrize("t,k", [(1, 2560), (5, 1536), (40, 768), (300, 2560)])
+def test_quantize_quotient_chunks_every_form(t, k):
+    # chunks built so that rint(x/d8) and rint(x * (1/d8)) differ in many
+    # places: every device quantiser (row, tile, gather, and the one fused
+    # into the GEMV) must take the binary32 quotient, as the oracle does
+    nsb = k // 256
+    x = synth.activations(t, k, 80 + t)
+    edge = quotient_chunks(min(t * nsb, 12), seed=81 + t)
+    x.reshape(-1, 256)[: len(edge)] = edge
+    rq, rs, rbs = oracle.quantize_q8k(x)
+    xd = dev(x)
+    xq, xs, xbs = ops.quantize_q8k(xd)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(xbs), rbs)
+    tq, ts, tbs = ops.quantize_q8k_tiles(xd)
+    assert np.array_equal(from_tiles(host(tq), t, k)[:t], rq)
+    assert np.array_equal(host(ts).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(from_bsum_tiles(host(tbs), t, k)[:t], rbs.astype(np.float64))
+    # gathered rows in reverse order, with one padding index
+    rows = np.concatenate([np.arange(t)[::-1], [-1]]).astype(np.int32)
+    gq, gs, gbs = ops.quantize_q8k_tiles_gather(xd, dev(rows))
+    assert np.array_equal(from_tiles(host(gq), t + 1, k)[:t], rq[::-1])
+    assert np.array_equal(host(gs)[:t].view(np.uint32), rs[::-1].view(np.uint32))
+    if t <= 8:
+        n = 64
+        recs = synth.weights("q4_k", n, k, 82)
+        planes = ops.pack("q4_k", ops.upload_records(recs), n, k)
+        _, (fq, fs, fbs) = ops.gemv_f32("q4_k", planes, n, k, xd, keep_image=True)
+        assert np.array_equal(host(fq), rq)
+        assert np.array_equal(host(fs).view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(host(fbs), rbs)
+        if t <= 2:  # the one-kernel form quantises inside every workgroup
+            y1 = ops.gemv_f32("q4_k", planes, n, k, xd)
+            assert torch.equal(y1, ops.gemv("q4_k", planes, n, k, (xq, xs, xbs)))
+
+
 # ------------------------------------------------------------ pack ------
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(1, 256), (17, 2560), (300, 768)])
@@ -132,7 +177,7 @@ def test_pack_round_trip_and_planes(fmt, n, k):
 
 # ------------------------------------------------------------ GEMV ------
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("t", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n,k", [(256, 2560), (37, 256), (1, 512), (17, 9728)])
 def test_gemv_parity(fmt, t, n, k):
     c = Case(fmt, n, k, t, seed=10 * t + n)
@@ -145,7 +190,7 @@ def test_gemv_parity(fmt, t, n, k):
 
 # ------------------------------------------------- fused quantise+GEMV --
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("t", [1, 2, 3, 6, 7, 8])
 @pytest.mark.parametrize("n,k", [(256, 2560), (37, 256), (2560, 9728), (9728, 2560)])
 def test_gemv_f32_fused_matches_two_step(fmt, t, n, k):
     c = Case(fmt, n, k, t, seed=30 + t)
@@ -181,13 +226,22 @@ def test_gemv_f32_fused_matches_two_step(fmt, t, n, k):
                                    (176, 130, 1024), (160, 64, 512), (200, 96, 768)])
 def test_gemm_parity(fmt, m, n, k):
     c = Case(fmt, n, k, m, seed=m + n)
-    y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
+    y, P, M = ops.matmul_partials("gemm_tiles", fmt, c.planes, n, k, c.q8t)
     check(c, y, P, M)
     # the production entry point, unsplit: the same body without the stores
-    y2 = ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=None)
+    y2 = ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=None)
     assert torch.equal(y, y2)
     # with a workspace a grid this small is split along k: same tolerance
-    check_y(c, ops.gemm(fmt, c.planes, n, k, c.q8t))
+    y3 = ops.gemm_tiles(fmt, c.planes, n, k, c.q8t)
+    check_y(c, y3)
+    # the row image of kq_quantize_q8k: re-laid in the workspace, then the
+    # same kernels with the same split, so the same bits
+    assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8), y3)
+    yr, Pr, Mr = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8)
+    assert torch.equal(yr, y) and torch.equal(Pr, P)
+    if fmt != "q6_k":
+        assert torch.equal(Mr, M)
+    assert kq.kq_gemm_tile_tokens(fmt, n, k, m) == (32 if m <= 192 else 256)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -196,7 +250,7 @@ def test_gemv_and_gemm_partials_agree(fmt):
     n, k, t = 200, 2560, 8
     c = Case(fmt, n, k, t, seed=5)
     _, P1, M1 = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
-    _, P2, M2 = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
+    _, P2, M2 = ops.matmul_partials("gemm_tiles", fmt, c.planes, n, k, c.q8t)
     assert torch.equal(P1, P2)
     if fmt != "q6_k":
         assert torch.equal(M1, M2)
@@ -209,11 +263,12 @@ def sample_rows(n):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
-@pytest.mark.parametrize("t", [1, 4, 8])
+@pytest.mark.parametrize("t", [1, 4, 6, 7, 8])
 def test_gemv_full_size_sampled(fmt, n, k, t):
-    # batch 4 stages the Q8_K image in LDS at both shapes; batch 8 stages it
-    # on W_up and runs W_down (an 88 KB image) as two staged launches of 4
-    # tokens, the partials entry point included, in the same sum order
+    # batch 4 stages the Q8_K image in LDS at both shapes; batches 6-8 stage
+    # it on W_up and run W_down (a 66-88 KB image) as staged launches of 4
+    # and 2-4 tokens, the partials entry point included, in the same sum
+    # order
     c = Case(fmt, n, k, t, seed=3)
     y, P, M = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
     check(c, y, P, M, rows=sample_rows(n))
@@ -231,11 +286,15 @@ def test_gemm_pp512_full_size_sampled(fmt, n, k):
     c = Case(fmt, n, k, m, seed=4, x=x)
     for a, b in zip(q8, c.q8t):
         assert torch.equal(a, b)
-    y = ops.gemm(fmt, c.planes, n, k, q8)  # with a workspace: W_down splits k
+    assert kq.kq_gemm_tile_tokens(fmt, n, k, m) == 256
+    y = ops.gemm_tiles(fmt, c.planes, n, k, q8)  # with a workspace: W_down splits k
     rows = sample_rows(n)[:24]
     check_y(c, y, rows)
-    y1 = ops.gemm(fmt, c.planes, n, k, q8, workspace=None)
+    y1 = ops.gemm_tiles(fmt, c.planes, n, k, q8, workspace=None)
     check_y(c, y1, rows)
+    # the pages' sequence: kq_quantize_q8k, then kq_gemm on its row image
+    yr = ops.gemm(fmt, c.planes, n, k, ops.quantize_q8k(xd))
+    assert torch.equal(yr, y)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -251,22 +310,22 @@ def test_gemm_split_parts_meet_through_any_workspace(fmt, n, k, m):
     # garbage or another call's counters and parts gives the same bits as a
     # zeroed one.
     c = Case(fmt, n, k, m, seed=14)
-    nbytes = kq.kq_gemm_workspace_bytes(fmt, n, k, m)
-    nbytes2 = kq.kq_gemm_workspace_bytes(fmt, 200, 2560, 256)
+    nbytes = kq.kq_gemm_tiles_workspace_bytes(fmt, n, k, m)
+    nbytes2 = kq.kq_gemm_tiles_workspace_bytes(fmt, 200, 2560, 256)
     assert nbytes > 0 and nbytes2 > 0
     ws = torch.zeros(max(nbytes, nbytes2) + 65536, dtype=torch.uint8, device="cuda")
-    y0 = ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=ws)
+    y0 = ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=ws)
     check_y(c, y0, sample_rows(n) if n > 2048 else None)
     ws.random_(0, 256)
-    assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
+    assert torch.equal(ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
     for _ in range(2):
-        assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
+        assert torch.equal(ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
     # another split call in the same workspace, then this one again
     c2 = Case(fmt, 200, 2560, 256, seed=15)
-    check_y(c2, ops.gemm(fmt, c2.planes, 200, 2560, c2.q8t, workspace=ws))
-    assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
+    check_y(c2, ops.gemm_tiles(fmt, c2.planes, 200, 2560, c2.q8t, workspace=ws))
+    assert torch.equal(ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=ws), y0)
     # unsplit: the same outputs within the fold's float tolerance
-    check_y(c, ops.gemm(fmt, c.planes, n, k, c.q8t, workspace=None), sample_rows(n) if n > 2048 else None)
+    check_y(c, ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=None), sample_rows(n) if n > 2048 else None)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -274,27 +333,33 @@ def test_gemm_split_parts_meet_through_any_workspace(fmt, n, k, m):
 @pytest.mark.parametrize("m", [16, 64, 96, 128, 150])  # 64, 128, 150: token tiles paired
 def test_gemm_mid_full_size_sampled(fmt, n, k, m):
     c = Case(fmt, n, k, m, seed=6)
-    y, P, M = ops.matmul_partials("gemm", fmt, c.planes, n, k, c.q8t)
+    y, P, M = ops.matmul_partials("gemm_tiles", fmt, c.planes, n, k, c.q8t)
     check(c, y, P, M, rows=sample_rows(n))
-    check_y(c, ops.gemm(fmt, c.planes, n, k, c.q8t), rows=sample_rows(n))  # K split with a workspace
+    check_y(c, ops.gemm_tiles(fmt, c.planes, n, k, c.q8t), rows=sample_rows(n))  # K split with a workspace
 
 
 # ------------------------------------------ poison, guards, determinism --
-@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_mid", "gemm_mid_pair"])
+@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_rows", "gemm_mid", "gemm_mid_pair"])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_outputs_fully_written_and_guards_intact(kind, fmt):
-    # gemm_mid_pair: an even number of 32-token tiles, paired on 64-row panels
-    n, k, t = 70, 768, {"gemv": 3, "gemm": 170, "gemm_mid": 70, "gemm_mid_pair": 60}[kind]
+    # gemm: the 256-token tile (200 tokens, one ragged block); gemm_rows: the
+    # same through kq_gemm's row image; gemm_mid_pair: an even number of
+    # 32-token tiles, paired on 64-row panels
+    n, k, t = 70, 768, {"gemv": 3, "gemm": 200, "gemm_rows": 200, "gemm_mid": 70, "gemm_mid_pair": 60}[kind]
     c = Case(fmt, n, k, t, seed=9)
+    assert kq.kq_gemm_tile_tokens(fmt, n, k, t) == (256 if kind in ("gemm", "gemm_rows") else 32)
     g = 4096
     buf = torch.full((g + t * n + g,), float("nan"), dtype=torch.float32, device="cuda")
     canary = torch.tensor([1234.5], device="cuda")
     buf[:g] = canary
     buf[-g:] = canary
     y = buf[g:g + t * n]
-    xq, xs, xbs = c.q8 if kind == "gemv" else c.q8t
-    f = kq.kq_gemv if kind == "gemv" else kq.kq_gemm
-    f(fmt, c.planes, n, k, xq, xs, xbs, t, y)
+    if kind == "gemv":
+        kq.kq_gemv(fmt, c.planes, n, k, *c.q8, t, y)
+    elif kind == "gemm_rows":
+        kq.kq_gemm(fmt, c.planes, n, k, *c.q8, t, y, ops.gemm_workspace(fmt, n, k, t))
+    else:
+        kq.kq_gemm_tiles(fmt, c.planes, n, k, *c.q8t, t, y)
     torch.cuda.synchronize()
     assert torch.all(buf[:g] == 1234.5) and torch.all(buf[-g:] == 1234.5)
     assert not torch.isnan(y).any()
@@ -309,9 +374,9 @@ def test_repeat_runs_are_bitwise_identical(kind):
         ys = [ops.gemv("q6_k", c.planes, n, k, c.q8) for _ in range(3)]
     else:
         # one workspace reused: the split sums come out the same every call
-        ws = ops.gemm_workspace("q6_k", n, k, t)
+        ws = ops.gemm_tiles_workspace("q6_k", n, k, t)
         assert ws is not None
-        ys = [ops.gemm("q6_k", c.planes, n, k, c.q8t, workspace=ws) for _ in range(3)]
+        ys = [ops.gemm_tiles("q6_k", c.planes, n, k, c.q8t, workspace=ws) for _ in range(3)]
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
 
 
@@ -319,10 +384,20 @@ def test_repeat_runs_are_bitwise_identical(kind):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_long_k_all_kernels(fmt):
     # k = 65536 (256 superblocks per row): the large offsets of every path --
-    # GEMV (batch 1 and 5), the 32-token tile (40 tokens, k split) and the
-    # 256-token tile (130 tokens, k split in 8)
+    # GEMV (batch 1 and 5), the 32-token tile (40 and 130 tokens, k split)
+    # and the 256-token tile (200 and 300 tokens: 2 and 4 tiles, k split in
+    # 8, and unsplit), whose 32-bit code offsets GEMM_KMAX bounds
     n, k = 40, 65536
-    for t, kind in ((1, "gemv"), (5, "gemv"), (40, "gemm"), (130, "gemm")):
+    for t, kind in ((1, "gemv"), (5, "gemv"), (40, "gemm"), (130, "gemm"), (200, "gemm"), (300, "gemm")):
         c = Case(fmt, n, k, t, seed=90 + t)
-        y = ops.gemv(fmt, c.planes, n, k, c.q8) if kind == "gemv" else ops.gemm(fmt, c.planes, n, k, c.q8t)
+        if kind == "gemv":
+            check_y(c, ops.gemv(fmt, c.planes, n, k, c.q8))
+            continue
+        assert kq.kq_gemm_tile_tokens(fmt, n, k, t) == (32 if t <= 192 else 256)
+        y = ops.gemm_tiles(fmt, c.planes, n, k, c.q8t)
         check_y(c, y)
+        if t > 192:
+            ws = kq.kq_gemm_tiles_workspace_bytes(fmt, n, k, t)
+            assert ws > 0  # the split form ran above
+            check_y(c, ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=None))
+            assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8), y)
