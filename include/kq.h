@@ -169,6 +169,25 @@ size_t kq_gemm_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);
 int kq_gemm(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
             const int16_t *xbs, int64_t m, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the device array kq_gemm_noalloc uses as its workspace. */
+#define KQ_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* kq_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call without the workspace argument.  Its workspace is a file-scope
+ * device array of KQ_SCRATCH_BYTES (64 MiB) inside the library, one per
+ * GPU, held until the process ends; each device's address is looked up on
+ * the first call on that device.  The call allocates nothing, and y is
+ * bit-identical to kq_gemm's.  KQ_EINVAL if kq_gemm_workspace_bytes(fmt, n,
+ * k, m) exceeds KQ_SCRATCH_BYTES (e.g. m * k above about 5.9e7 with no
+ * k split).  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (nothing in it needs clearing: the re-laid image is
+ * rewritten by every call, and the k-split counters are tagged per call), so
+ * calls that overlap on one GPU -- on different streams, or from different
+ * threads without ordering -- race and must not be issued. */
+int kq_gemm_noalloc(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                    const int16_t *xbs, int64_t m, float *y, void *stream);
+
 /* Bytes of the optional kq_gemm_tiles workspace for this shape on the current
  * device (0: kq_gemm_tiles would not use one), or 0 on bad arguments. */
 size_t kq_gemm_tiles_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t m);

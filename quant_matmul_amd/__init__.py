@@ -29,7 +29,7 @@ SYMBOLS = ("kq_record_bytes", "kq_packed_bytes", "kq_pack", "kq_unpack", "kq_qua
            "kq_q8k_tiles_bytes", "kq_quantize_q8k_tiles", "kq_quantize_q8k_tiles_gather", "kq_gemv",
            "kq_gemv_f32", "kq_gemm_workspace_bytes", "kq_gemm", "kq_gemm_tiles_workspace_bytes",
            "kq_gemm_tile_tokens", "kq_gemm_tiles", "kq_gemm_grouped", "kq_gemv_partials", "kq_gemm_partials",
-           "kq_gemm_tiles_partials", "kq_strerror")
+           "kq_gemm_tiles_partials", "kq_gemm_noalloc", "kq_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python quant_matmul_amd/build.py`")
@@ -52,6 +52,7 @@ lib.kq_gemv.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
 lib.kq_gemm_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
 lib.kq_gemm_workspace_bytes.restype = ctypes.c_size_t
 lib.kq_gemm.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p, ctypes.c_size_t, _p]
+lib.kq_gemm_noalloc.argtypes = [_int, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
 lib.kq_gemm_tiles_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
 lib.kq_gemm_tiles_workspace_bytes.restype = ctypes.c_size_t
 lib.kq_gemm_tile_tokens.argtypes = [_int, _i64, _i64, _i64]
@@ -65,7 +66,7 @@ lib.kq_strerror.argtypes = [_int]
 lib.kq_strerror.restype = ctypes.c_char_p
 for _f in ("kq_pack", "kq_unpack", "kq_quantize_q8k", "kq_quantize_q8k_tiles", "kq_quantize_q8k_tiles_gather",
            "kq_gemv", "kq_gemv_f32", "kq_gemm", "kq_gemm_tiles", "kq_gemm_grouped",
-           "kq_gemv_partials", "kq_gemm_partials", "kq_gemm_tiles_partials"):
+           "kq_gemv_partials", "kq_gemm_partials", "kq_gemm_tiles_partials", "kq_gemm_noalloc"):
     getattr(lib, _f).restype = _int
 
 
@@ -161,6 +162,15 @@ def kq_gemm(fmt, w_planes, n: int, k: int, xq, xs, xbs, m: int, y, workspace, wo
     """GEMM on the row image of kq_quantize_q8k (workspace required)."""
     _ok(lib.kq_gemm(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), m, _ptr(y),
                     _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)), "kq_gemm")
+
+
+KQ_SCRATCH_BYTES = 64 << 20
+
+
+def kq_gemm_noalloc(fmt, w_planes, n: int, k: int, xq, xs, xbs, m: int, y, stream=None):
+    """kq_gemm with the library's own device scratch array as its workspace."""
+    _ok(lib.kq_gemm_noalloc(_fmt(fmt), _ptr(w_planes), n, k, _ptr(xq), _ptr(xs), _ptr(xbs), m, _ptr(y),
+                            _stream(stream)), "kq_gemm_noalloc")
 
 
 def kq_gemm_tiles_workspace_bytes(fmt, n: int, k: int, m: int) -> int:

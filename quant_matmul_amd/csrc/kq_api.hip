@@ -3,6 +3,8 @@
 // the launch on the caller's stream.
 #include <limits.h>
 
+#include <atomic>
+
 #include "kq_common.h"
 
 namespace kq {
@@ -286,6 +288,47 @@ int kq_gemm_partials(int fmt, const void *w_planes, int64_t n, int64_t k, const 
 {
     if (!P) return KQ_EINVAL;
     return gemm_rows(fmt, w_planes, n, k, xq, xs, xbs, m, y, P, M, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// The workspace of kq_gemm_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never names it directly (its
+// host-side name is not a device address): the entry point looks up each
+// device's address once, with that device current, and passes that.
+static __device__ __align__(256) uint8_t scratch[KQ_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_DEVICES = 64;
+std::atomic<void *> scratch_ptr[SCRATCH_DEVICES];
+
+// this device's copy of `scratch`, or nullptr if it cannot be found
+void *scratch_of_current_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_DEVICES) return nullptr;
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // racing first calls on one device look up the same address
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+}  // namespace
+
+extern "C" {
+
+int kq_gemm_noalloc(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                    const int16_t *xbs, int64_t m, float *y, void *stream)
+{
+    int rc = check_matmul(fmt, w_planes, n, k, xq, xs, xbs, m, INT_MAX, y, nullptr, nullptr, false);
+    if (rc) return rc;
+    const size_t need = kq_gemm_workspace_bytes(fmt, n, k, m);
+    if (need == 0 || need > KQ_SCRATCH_BYTES) return KQ_EINVAL;
+    void *ws = scratch_of_current_device();
+    if (!ws) return KQ_ELAUNCH;
+    return gemm_rows(fmt, w_planes, n, k, xq, xs, xbs, m, y, nullptr, nullptr, ws, KQ_SCRATCH_BYTES, stream);
 }
 
 const char *kq_strerror(int code)

@@ -135,6 +135,17 @@ def test_gemm_workspace_bytes():
     assert kq.kq_gemm_workspace_bytes(9, 300, 2560, 130) == 0
 
 
+def test_gemm_noalloc_size_limit():
+    # kq_gemm_noalloc takes no workspace: shapes whose kq_gemm workspace is
+    # larger than the library's array are refused before any device call
+    f = kq.lib.kq_gemm_noalloc
+    assert kq.kq_gemm_workspace_bytes(4, 5120, 17408, 8192) > kq.KQ_SCRATCH_BYTES
+    assert f(4, GOOD16, 5120, 17408, GOOD16, GOOD16, GOOD16, 8192, GOOD16, None) == kq.KQ_EINVAL
+    assert f(9, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EFORMAT
+    assert f(4, GOOD16, 16, 256, None, GOOD16, GOOD16, 4, GOOD16, None) == kq.KQ_EINVAL
+    assert f(4, GOOD16, 16, 256, GOOD16, GOOD16, GOOD16 + 2, 4, GOOD16, None) == kq.KQ_EALIGN
+
+
 def test_gemm_tile_choice():
     # m <= 192: the 32-token tile; from 193 tokens the 256-token tile
     for m, tok in ((1, 32), (64, 32), (192, 32), (193, 256), (200, 256), (512, 256)):
