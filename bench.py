@@ -85,6 +85,19 @@ MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
                "src_sha256_16": "5c67f30eb0f16515", "bytes_per_launch": 229721395}
 
 
+# Mean per-dispatch duration of the same kernels in the committed rocprofv3
+# kernel trace of a full bench run (profiles/kq_gemv_gemm_qwen3_4b_ffn_trace.md,
+# value-leg window), so the line carries the roofline fraction from both
+# timers; tied to the sources like the traffic records.
+GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "1604315dabe74847", "avg_us": 6.38}
+GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "11609855197ded27",
+              "avg_us": 48.51}
+
+
+def trace_us(rec):
+    return rec["avg_us"] if src_hash(rec["files"]) == rec["src_sha256_16"] else None
+
+
 def src_hash(files):
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
@@ -114,7 +127,7 @@ def parse():
     ap.add_argument("--pool-gib", type=float, default=1.0,
                     help="minimum weight bytes read per rotation cycle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--legs", default="gemv,gemm,mid,moe,probes,layers,dense,batch", help="which legs to run")
     ap.add_argument("--side-reps", type=int, default=20,
@@ -125,38 +138,152 @@ def parse():
                          "moe (the MoE layer; FMT:N:K:T ignored), copy (a plain 64 MiB device "
                          "copy, the counters' byte reference)")
     ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="only sweep the streaming-read probe over buffer size, loads in flight and grid, "
+                         "and print the curve as one JSON line")
     return ap.parse_args()
 
 
+def cpu_info():
+    """Cores this process may run on (sched_getaffinity) and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def _timed_reps(fn, reps):
+    """Steady-state timing: one discarded run, then the median of `reps`."""
+    fn()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return ts[len(ts) // 2], ts
+
+
 def cpu_baseline(seconds):
-    """The CPU oracle (oracle/kq_oracle.c, single thread) on a bounded sample:
-    Q8_K quantise + GEMV at batch 1 over row slices of the six matrices."""
+    """The CPU oracle (oracle/kq_oracle.c, unchanged) on bounded samples of the
+    benchmark's workload, timed on this host: single-thread and on all the
+    cores this process may use (threads over row slices, each calling the
+    same scalar oracle; ctypes releases the GIL during the C call).  Each
+    figure is the median of several back-to-back repetitions after one
+    discarded run.  GEMV side: Q8_K quantise + GEMV at batch 1 over a row
+    slice of each of the six FFN matrices (GB/s of the GEMV's algorithmic
+    bytes).  GEMM side: the pp512 products of a row sample of W_up and W_down
+    (GMAC/s)."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
     import synth
 
-    done_bytes, t_used, matrices = 0, 0.0, 0
-    rows = 512
-    start = time.perf_counter()
-    while t_used < seconds:
+    cores, model = cpu_info()
+    # the box's CPU share for one GPU is 16 cores, whatever the affinity says
+    workers = max(1, min(cores, 16))
+    # GEMV sample: `rows` rows of every (format, shape) pair, one token; the
+    # row count is scaled from a 64-row calibration so that one single-thread
+    # repetition takes about seconds/8
+    def gemv_sample(rows):
+        items = []
         for fmt in FMTS:
             for i, (n, k) in enumerate(SHAPES):
-                recs = synth.weights(fmt, rows, k, synth.seed_for(1, 100 + matrices))
+                recs = synth.weights(fmt, rows, k, synth.seed_for(1, 100 + len(items)))
                 x = synth.activations(1, k, synth.seed_for(1, 50 + i))
-                t0 = time.perf_counter()
-                xq, xs, xbs = oracle.quantize_q8k(x)
-                oracle.matmul(fmt, recs, xq, xs, xbs)
-                t_used += time.perf_counter() - t0
-                done_bytes += gemv_bytes(fmt, rows, k, fused=False)
-                matrices += 1
-        if time.perf_counter() - start > 4 * seconds:
-            break
-    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{matrices} GEMV calls at batch 1, each 512 rows of one of the six "
-                      f"Q4_K/Q5_K/Q6_K W_up/W_down matrices (Q8_K quantise included), "
-                      f"{t_used:.1f} s of single-thread CPU time",
-            "seconds": t_used}
+                items.append((fmt, k, recs, x))
+        return items
+
+    def gemv_once(items, lo, hi):
+        for fmt, k, recs, x in items:
+            xq, xs, xbs = oracle.quantize_q8k(x)
+            oracle.matmul(fmt, recs[lo:hi], xq, xs, xbs)
+
+    cal = gemv_sample(64)
+    t0 = time.perf_counter()
+    gemv_once(cal, 0, 64)
+    rows = int(min(2560, max(64, 64 * (seconds / 8) / max(time.perf_counter() - t0, 1e-6)))) // 64 * 64
+    gemv_items = gemv_sample(rows)
+    gemv_bytes_per_rep = sum(gemv_bytes(f, rows, k, fused=False) for f, k, _, _ in gemv_items)
+
+    def gemv_run(parts):
+        def work(item_part):
+            (fmt, k, recs, x), lo, hi = item_part
+            xq, xs, xbs = oracle.quantize_q8k(x)
+            oracle.matmul(fmt, recs[lo:hi], xq, xs, xbs)
+        jobs = []
+        for it in gemv_items:
+            step = -(-rows // parts)
+            jobs += [(it, lo, min(rows, lo + step)) for lo in range(0, rows, step)]
+        if parts == 1:
+            for j in jobs:
+                work(j)
+        else:
+            with cf.ThreadPoolExecutor(parts) as ex:
+                list(ex.map(work, jobs))
+
+    # GEMM sample: 512 tokens against `grows` rows of Q4_K W_up and Q6_K
+    # W_down, scaled so that one single-thread repetition takes about
+    # seconds/16
+    def gemm_sample(grows):
+        items = []
+        for fmt, (n, k) in (("q4_k", SHAPES[0]), ("q6_k", SHAPES[1])):
+            recs = synth.weights(fmt, grows, k, synth.seed_for(2, 100 + len(items)))
+            x = synth.activations(GEMM_M, k, synth.seed_for(2, 50 + len(items)))
+            items.append((fmt, k, recs, oracle.quantize_q8k(x)))
+        return items
+
+    cal = gemm_sample(2)
+    t0 = time.perf_counter()
+    for fmt, k, recs, q8 in cal:
+        oracle.matmul(fmt, recs, *q8)
+    grows = int(min(512, max(2 * workers, 2 * (seconds / 16) / max(time.perf_counter() - t0, 1e-6))))
+    grows = -(-grows // workers) * workers
+    gemm_items = gemm_sample(grows)
+    gemm_macs_per_rep = sum(GEMM_M * grows * k for _, k, _, _ in gemm_items)
+
+    def gemm_run(parts):
+        def work(job):
+            (fmt, k, recs, q8), lo, hi = job
+            oracle.matmul(fmt, recs[lo:hi], *q8)
+        jobs = []
+        for it in gemm_items:
+            step = -(-grows // parts)
+            jobs += [(it, lo, min(grows, lo + step)) for lo in range(0, grows, step)]
+        if parts == 1:
+            for j in jobs:
+                work(j)
+        else:
+            with cf.ThreadPoolExecutor(parts) as ex:
+                list(ex.map(work, jobs))
+
+    t_start = time.perf_counter()
+    g1, g1_all = _timed_reps(lambda: gemv_run(1), 3)
+    gN, gN_all = _timed_reps(lambda: gemv_run(workers), 5)
+    m1, _ = _timed_reps(lambda: gemm_run(1), 3)
+    mN, _ = _timed_reps(lambda: gemm_run(workers), 5)
+    spent = time.perf_counter() - t_start
+    return {"value": gemv_bytes_per_rep / gN / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "cpu_model": model, "cores_available": cores,
+            "single_thread": {"value": gemv_bytes_per_rep / g1 / 1e9, "unit": "GB/s", "cores": 1},
+            "gemm": {"single_thread_GMACs": gemm_macs_per_rep / m1 / 1e9,
+                     "all_cores_GMACs": gemm_macs_per_rep / mN / 1e9, "cores": workers,
+                     "sample": f"512 tokens x {grows} rows of Q4_K 9728x2560 and of Q6_K 2560x9728 "
+                               f"({gemm_macs_per_rep / 1e6:.0f} M MACs per repetition)"},
+            "sample": f"Q8_K quantise + GEMV at batch 1 over {rows} rows of each of the six Q4_K/Q5_K/Q6_K "
+                      f"W_up/W_down matrices ({gemv_bytes_per_rep / 1e6:.2f} MB of algorithmic bytes per "
+                      f"repetition); median of 5 all-core and 3 single-thread repetitions after one "
+                      f"discarded run; threads over row slices",
+            "seconds": spent}
 
 
 def bench_probes(mats, copies, stream, capture, ev):
@@ -172,10 +299,12 @@ def bench_probes(mats, copies, stream, capture, ev):
     for fmt, n, k, pl in mats:
         nbytes = pl[0].numel()
         best = None
-        for grid in (1024, 2048, 4096, 8192):
-            def run(grid=grid):
+        # the configurations that win somewhere in the probe's size sweep
+        # (profiles/probe_read_ceiling_vs_size.md)
+        for unroll, grid in ((1, 2048), (1, 4096), (1, 8192), (2, 4096), (4, 1024), (4, 2048)):
+            def run(grid=grid, unroll=unroll):
                 for r in range(reps):
-                    probes.kq_probe_read(pl[r % copies], nbytes, sink, grid)
+                    probes.kq_probe_read_u(pl[r % copies], nbytes, sink, grid, unroll)
             g = capture(run)
             g.replay()
             a, b = ev(), ev()
@@ -185,9 +314,9 @@ def bench_probes(mats, copies, stream, capture, ev):
             torch.cuda.synchronize()
             us = a.elapsed_time(b) * 1e3 / reps
             if best is None or us < best[0]:
-                best = (us, grid)
+                best = (us, grid, unroll)
         read.append({"matrix": f"{fmt}_{n}x{k}", "bytes": nbytes, "us": best[0], "grid": best[1],
-                     "GBps": nbytes / (best[0] * 1e-6) / 1e9})
+                     "loads_in_flight": best[2], "GBps": nbytes / (best[0] * 1e-6) / 1e9})
     read_gbps = sum(r["bytes"] for r in read) / (sum(r["us"] for r in read) * 1e-6) / 1e9
     mfma = []
     iters = 2048
@@ -638,8 +767,67 @@ class _Eager:
         self.fn(*self.a)
 
 
+def probe_sweep():
+    """Best plain streaming read on this machine per buffer size: the probe
+    (probes/kq_probe.h) over sizes from the FFN matrices to 1 GiB, 1-16 loads
+    in flight per thread and 512-16384 workgroups; small sizes rotate over
+    copies that together exceed the 256 MB Infinity Cache, each launch timed
+    back to back inside one HIP graph."""
+    import torch
+
+    import probes
+
+    torch.cuda.set_device(0)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sizes_mb = (14, 17, 20, 50, 73, 128, 256, 512, 1024)
+    out = {"probe_sweep": [], "unit": "GB/s", "peak": HBM_PEAK_GBPS}
+    for mb in sizes_mb:
+        nbytes = mb * (1 << 20)
+        copies = max(1, -(-(1 << 30) // nbytes)) if mb < 512 else 1
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        reps = max(copies, 16 if mb < 256 else 4)
+        best = None
+        rows = []
+        for unroll in (1, 2, 4, 8, 16):
+            for grid in (512, 1024, 2048, 4096, 8192, 16384):
+                g = torch.cuda.CUDAGraph()
+                s_ = torch.cuda.Stream()
+                with torch.cuda.stream(s_):
+                    probes.kq_probe_read_u(bufs[0], nbytes, sink, grid, unroll, stream=s_)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g):
+                    for r in range(reps):
+                        probes.kq_probe_read_u(bufs[r % copies], nbytes, sink, grid, unroll)
+                g.replay()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(5):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    g.replay()
+                    e1.record()
+                    e1.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+                us = sorted(ts)[2]
+                gbps = nbytes / (us * 1e-6) / 1e9
+                rows.append([unroll, grid, round(us, 3), round(gbps, 1)])
+                if best is None or gbps > best[3]:
+                    best = [unroll, grid, us, gbps]
+                del g
+        out["probe_sweep"].append({"MiB": mb, "copies": copies, "best": {"unroll": best[0], "grid": best[1],
+                                   "us": round(best[2], 3), "GBps": round(best[3], 1),
+                                   "frac_of_peak": round(best[3] / HBM_PEAK_GBPS, 4)}, "all": rows})
+        print(f"[sweep] {mb} MiB best {best}", file=sys.stderr, flush=True)
+        del bufs
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     args = parse()
+    if args.probe_sweep:
+        return probe_sweep()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
               "(the kq path is a single-GPU kernel library; see DESIGN.md for how it would shard)",
@@ -790,7 +978,11 @@ def main():
                                   "quantised on device, Qwen3-4B FFN shapes",
                       "formats": list(FMTS), "shapes_nk": [list(s) for s in SHAPES],
                       "gemv_batch": 1, "gemm_tokens": GEMM_M,
-                      "weight_copies": copies, "weight_bytes_per_rotation": cycle_bytes * copies},
+                      "weight_copies": copies, "weight_bytes_per_rotation": cycle_bytes * copies,
+                      "seeds": {"weights": [synth.seed_for(1, t) for t in range(len(mats))],
+                                "gemv_x": [synth.seed_for(1, 50 + i) for i in range(len(SHAPES))],
+                                "gemm_x": [synth.seed_for(2, 50 + i) for i in range(len(SHAPES))],
+                                "generator": "numpy PCG64 (synth/)"}},
            "device": props.name, "host_wall_s": wall}
     per = {}
     if "gemv" in graphs:
@@ -806,11 +998,16 @@ def main():
         kms = ms(krec["gemv"])
         ach = kb / (kms * 1e-3) / 1e9
         traffic = measured_traffic(GEMV_TRAFFIC)
+        alg = kb / (reps["gemv"] * len(mats))
+        tus = trace_us(GEMV_TRACE)
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
-                           "algorithmic_bytes_per_launch": kb / (reps["gemv"] * len(mats)),
+                           "algorithmic_bytes_per_launch": alg,
                            "kernel": "kq::gemv_kernel (kq_gemv)",
-                           "avg_launch_us": kms * 1e3 / (reps["gemv"] * len(mats))}
+                           "avg_launch_us": kms * 1e3 / (reps["gemv"] * len(mats)),
+                           "timer": "HIP events around graph replays of back-to-back launches",
+                           "trace_avg_us": tus,
+                           "frac_trace": None if tus is None else alg / (tus * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         for j, (f, n, k, _) in enumerate(mats):
             us = krec["gemv"][j][0].elapsed_time(krec["gemv"][j][1]) * 1e3 / reps["gemv"]
             per.setdefault(f"{f}_{n}x{k}", {})["gemv"] = {
@@ -824,11 +1021,17 @@ def main():
                        "leg_ms_per_step": leg_ms / args.steps}
         gemm_alg = sum(n * (k // 256) * BYTES[f] + GEMM_M * (k + k // 64 + k // 8) + 4 * GEMM_M * n
                        for f, n, k, _ in mats) / len(mats)
+        tus = trace_us(GEMM_TRACE)
+        ops_launch = ops_step / len(mats)
         out["roofline_gemm"] = {"bound": "mfma", "achieved": ach, "peak": MFMA_I8_PEAK_TOPS, "unit": "TOPS",
                                 "frac": ach / MFMA_I8_PEAK_TOPS, "traffic": measured_traffic(GEMM_TRAFFIC),
                                 "algorithmic_bytes_per_launch": gemm_alg,
                                 "kernel": "kq::gemm_kernel (W_down split along k, parts added in-kernel)",
-                                "avg_launch_us": kms * 1e3 / (reps["gemm"] * len(mats))}
+                                "avg_launch_us": kms * 1e3 / (reps["gemm"] * len(mats)),
+                                "timer": "HIP events around graph replays of back-to-back launches",
+                                "trace_avg_us": tus,
+                                "frac_trace": None if tus is None else
+                                ops_launch / (tus * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS}
         for j, (f, n, k, _) in enumerate(mats):
             us = krec["gemm"][j][0].elapsed_time(krec["gemm"][j][1]) * 1e3 / reps["gemm"]
             per.setdefault(f"{f}_{n}x{k}", {})["gemm"] = {
@@ -840,7 +1043,8 @@ def main():
         if "roofline" in out:
             out["roofline"]["achievable"] = {
                 "value": pr["read_GBps"], "unit": "GB/s", "frac": out["roofline"]["achieved"] / pr["read_GBps"],
-                "probe": "kq_probe_read: plain 16-byte streaming read of the same plane buffers"}
+                "probe": "kq_probe_read_u: plain 16-byte streaming read of the same plane buffers, best of six "
+                         "launch shapes"}
         if "roofline_gemm" in out:
             t = pr["mfma_i8_TOPS"]
             out["roofline_gemm"]["achievable"] = {

@@ -28,6 +28,11 @@ extern "C" {
  * buf: 16-byte aligned, bytes a positive multiple of 16; 1 <= grid <= 65536. */
 int kq_probe_read(const void *buf, size_t bytes, uint32_t *sink, int grid, void *stream);
 
+/* kq_probe_read with `unroll` (1, 2, 4, 8 or 16) loads in flight per thread
+ * instead of four; the sweep over unroll, grid and size finds the best
+ * plain read this machine sustains for a given buffer size. */
+int kq_probe_read_u(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, void *stream);
+
 /* Matrix-core rate: `grid` workgroups of 256 threads; every wave issues
  * `iters` x 4 independent v_mfma_i32_32x32x32_i8 on register operands
  * (65,536 int8 ops each) and each thread stores one int of the results to
