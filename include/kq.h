@@ -138,13 +138,15 @@ int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
  * (commit message of that name) quantises inside the consuming chain at
  * whole-superblock granules -- here inside the GEMV, which saves the
  * separate quantiser launch and the image's round trip.  For t <= 2 this
- * is one kernel: every workgroup quantises x into LDS (a workgroup covers
- * several row groups, down to about two workgroups per CU, so fewer of them
- * repeat it); xq/xs/xbs may then be NULL (all three), or receive the Q8_K
- * image.  With the image buffers given and k > 4096, where that repeated
- * quantisation costs more than a launch, the call runs kq_quantize_q8k then
- * kq_gemv instead.  y is bit-identical to kq_quantize_q8k then kq_gemv.  For
- * t > 2 the image buffers are required and the call runs the two launches.
+ * is one kernel while the image and its scales fit one workgroup's LDS
+ * stage (t*k*9/8 + t*(k/256)*4 <= 147456 bytes: k up to 129024 at t = 1,
+ * 64512 at t = 2):
+ * every workgroup quantises x into LDS (a workgroup covers as many row
+ * groups as 16 waves hold, so few of them repeat it); xq/xs/xbs may then
+ * be NULL (all three), or receive the Q8_K image.  Past that size, and for
+ * t > 2, the image buffers are required (KQ_EINVAL without them) and the
+ * call runs kq_quantize_q8k then kq_gemv.  y is bit-identical to
+ * kq_quantize_q8k then kq_gemv in every case.
  * x must be 16-byte aligned and finite. */
 int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float *x, int64_t t,
                 float *y, int8_t *xq, float *xs, int16_t *xbs, void *stream);

@@ -30,6 +30,7 @@ constexpr int64_t GEMM_MID_MAX = 192;
 inline bool gemm_uses_mid(int64_t m) { return m <= GEMM_MID_MAX; }
 int launch_pack(int fmt, const void *w_ggml, int64_t n, int64_t k, void *w_planes, hipStream_t stream);
 int launch_unpack(int fmt, const void *w_planes, int64_t n, int64_t k, void *w_ggml, hipStream_t stream);
+bool gemv_fusable(int64_t t, int64_t k);
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
                 const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
                 const float *x = nullptr, int8_t *oq = nullptr, float *os = nullptr, int16_t *obs = nullptr);
@@ -160,15 +161,15 @@ int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float
     if (t > 2 && !image) return KQ_EINVAL;              // batches past 2 need the image buffers
     if (!aligned(w_planes, 16) || !aligned(x, 16) || !aligned(y, 4)) return KQ_EALIGN;
     if (image && (!aligned(xq, 16) || !aligned(xbs, 16) || !aligned(xs, 4))) return KQ_EALIGN;
-    // The one-kernel form re-quantises x in every workgroup.  Past 16
-    // superblocks that repeated work costs more than the quantiser launch it
-    // saves (k = 9728, batch 1: 11.4 us fused against 8.5 us for quantise +
-    // GEMV), so when the caller gives the image buffers such a call runs the
-    // two launches instead; y is the same bits either way.
-    constexpr int64_t FUSE_KMAX = 16 * 256;
-    if (t <= 2 && (!image || k <= FUSE_KMAX))
+    // Batches of 1-2 run as one kernel (each workgroup quantises x into its
+    // LDS stage) while the image fits that stage; the image buffers, when
+    // given, then receive the image too.  Otherwise the quantiser and the
+    // GEMV run as two launches, which needs the buffers.  y is the same bits
+    // either way.
+    if (kq::gemv_fusable(t, k))
         return kq::launch_gemv(fmt, w_planes, n, k, nullptr, nullptr, nullptr, t, y, nullptr, nullptr,
                                (hipStream_t)stream, x, xq, xs, xbs);
+    if (!image) return KQ_EINVAL;
     int rc = kq::launch_quantize_q8k(x, t, k, xq, xs, xbs, (hipStream_t)stream);
     if (rc) return rc;
     return kq::launch_gemv(fmt, w_planes, n, k, xq, xs, xbs, t, y, nullptr, nullptr, (hipStream_t)stream);

@@ -100,26 +100,54 @@ __device__ inline int quad_sum(int v)
     return v;
 }
 
-// Q8_K quantisation of one 256-value chunk by one wave: lane l holds values
-// 4l..4l+3.  amax over the chunk, d8 = amax/127 (binary32, correctly
-// rounded), code = rint(x/d8) (correctly rounded quotient, half to even)
-// clamped to [-127, 127]; an all-zero chunk gives d8 = 0 and zero codes.
-// Returns the lane's four codes packed in a dword; `qsum` receives the sum
-// of the 16 codes of the lane's quad (bsum g = l/4) and d8 the scale.
+// Q8_K codes.  The code of x is rint(x / d8), the correctly rounded binary32
+// quotient rounded half to even, clamped to [-127, 127].  The quotient is
+// formed without a full IEEE division per value (Markstein's method, as in
+// the IA-64 division sequences): with y = 1/d8 correctly rounded,
+// q0 = x*y is within a few ulps of x/d8, and each correction
+// q += (x - q*d8)*y, whose residual one fma gives exactly, brings q closer;
+// after two corrections q is the correctly rounded quotient.  That needs
+// the residuals to stay in the normal range wherever the code can be
+// nonzero (|x| >= d8/2), which d8 >= 2^-64 guarantees; a chunk with a
+// smaller scale (amax below about 2^-57) takes the IEEE division
+// (__fdiv_rn) per value instead.  1/d8 cannot overflow for d8 >= 2^-64,
+// and d8 <= amax/127 keeps every product in range.
+__device__ inline float q8k_recip(float d8) { return d8 >= 0x1p-64f ? __fdiv_rn(1.0f, d8) : 0.0f; }
+
+__device__ inline int q8k_code(float x, float d8, float y)
+{
+    float q;
+    if (y != 0.0f) {
+        q = x * y;
+        q = fmaf(fmaf(-q, d8, x), y, q);
+        q = fmaf(fmaf(-q, d8, x), y, q);
+    } else {
+        q = __fdiv_rn(x, d8);
+    }
+    const int a = (int)rintf(q);
+    return a > 127 ? 127 : (a < -127 ? -127 : a);
+}
+
 template <int CTRL>
 __device__ inline float dpp_max(float v)
 {
     return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false)));
 }
 
-// Maximum over the 64 lanes (max is exact, so any order gives the same
-// bits): DPP within each row of 16, then the four row maxima.
-__device__ inline float wave_max(float v)
+// Maximum over each row of 16 lanes, in every lane of the row (max is exact,
+// so any order gives the same bits).
+__device__ inline float row_max(float v)
 {
     v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
     v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
     v = dpp_max<0x141>(v);  // row_half_mirror
-    v = dpp_max<0x140>(v);  // row_mirror: every lane holds its row's max
+    return dpp_max<0x140>(v);  // row_mirror
+}
+
+// Maximum over the 64 lanes: the four row maxima.
+__device__ inline float wave_max(float v)
+{
+    v = row_max(v);
     const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
     const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
@@ -127,6 +155,11 @@ __device__ inline float wave_max(float v)
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Q8_K quantisation of one 256-value chunk by one wave: lane l holds values
+// 4l..4l+3.  amax over the chunk, d8 = amax/127 (binary32, correctly
+// rounded), codes as above; an all-zero chunk gives d8 = 0 and zero codes.
+// Returns the lane's four codes packed in a dword; `qsum` receives the sum
+// of the 16 codes of the lane's quad (bsum g = l/4) and d8 the scale.
 __device__ inline uint32_t q8k_chunk(float4 v, int &qsum, float &d8)
 {
     const float amax = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
@@ -134,18 +167,43 @@ __device__ inline uint32_t q8k_chunk(float4 v, int &qsum, float &d8)
     d8 = 0.0f;
     if (amax != 0.0f) {
         d8 = __fdiv_rn(amax, 127.0f);
-        auto code = [d8](float f) {
-            const int a = (int)rintf(__fdiv_rn(f, d8));
-            return a > 127 ? 127 : (a < -127 ? -127 : a);
-        };
-        a0 = code(v.x);
-        a1 = code(v.y);
-        a2 = code(v.z);
-        a3 = code(v.w);
+        const float y = q8k_recip(d8);
+        a0 = q8k_code(v.x, d8, y);
+        a1 = q8k_code(v.y, d8, y);
+        a2 = q8k_code(v.z, d8, y);
+        a3 = q8k_code(v.w, d8, y);
     }
     qsum = quad_sum(a0 + a1 + a2 + a3);
     return (uint32_t)(a0 & 0xFF) | ((uint32_t)(a1 & 0xFF) << 8) | ((uint32_t)(a2 & 0xFF) << 16) |
            ((uint32_t)(a3 & 0xFF) << 24);
+}
+
+// Q8_K quantisation of four chunks by one wave (the wide form): the 16 lanes
+// of row r each hold 16 consecutive values v[0..15] of one chunk, lane j of
+// the row values 16j..16j+15.  All 64 lanes must be active (the amax is a
+// DPP reduction over the row).  Returns the lane's 16 codes as one 16-byte
+// piece; `qsum` receives their sum (bsum j of the chunk) and d8 the
+// chunk's scale.
+__device__ inline uint4 q8k_piece16(const float (&v)[16], int &qsum, float &d8)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = row_max(amax);
+    uint32_t pk[4] = {0, 0, 0, 0};
+    qsum = 0;
+    d8 = 0.0f;
+    if (amax != 0.0f) {
+        d8 = __fdiv_rn(amax, 127.0f);
+        const float y = q8k_recip(d8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int a = q8k_code(v[i], d8, y);
+            qsum += a;
+            pk[i >> 2] |= (uint32_t)(a & 0xFF) << (8 * (i & 3));
+        }
+    }
+    return make_uint4(pk[0], pk[1], pk[2], pk[3]);
 }
 
 // Raw bytes of one 64-weight share of a superblock, as loaded from the

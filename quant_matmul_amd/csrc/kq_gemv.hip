@@ -232,17 +232,31 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
             if (i < nst) st[j] = src_chunk(i);
         }
     }
-    // fused: wave w quantises chunks w, w + nw, ... of x (chunk = t*nsb + s);
-    // the first CMAX of them are loaded before the weights
-    constexpr int CMAX = 8;
-    const int nchunks = T * nsb;
-    float4 xr[FUSE ? CMAX : 1];
+    // fused: the activation's chunks (chunk = t*nsb + s) are quantised four
+    // per wave, in groups g = 4 consecutive chunks: wave w takes groups w,
+    // w + nw, ...; lane l holds values 16j..16j+15 (j = l % 16) of chunk
+    // 4g + l/16.  The first GMAX groups of a wave are loaded before the
+    // weights.
+    constexpr int GMAX = 2;
+    const int nchunks = T * nsb, ngroups = (nchunks + 3) >> 2;
+    const int gsub = lane >> 4, gj = lane & 15;
+    auto load_group = [&](int g, float (&v)[16]) {
+        const int ch = 4 * g + gsub;
+        const float4 *p = reinterpret_cast<const float4 *>(x + (int64_t)ch * QK + 16 * gj);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 f = ch < nchunks ? p[i] : make_float4(0, 0, 0, 0);
+            v[4 * i] = f.x;
+            v[4 * i + 1] = f.y;
+            v[4 * i + 2] = f.z;
+            v[4 * i + 3] = f.w;
+        }
+    };
+    float xv[FUSE ? GMAX : 1][16];
     if constexpr (FUSE) {
 #pragma unroll
-        for (int j = 0; j < CMAX; ++j) {
-            const int ch = wave + j * nw;
-            if (ch < nchunks) xr[j] = reinterpret_cast<const float4 *>(x + (int64_t)ch * QK)[lane];
-        }
+        for (int gi = 0; gi < GMAX; ++gi)
+            if (wave + gi * nw < ngroups) load_group(wave + gi * nw, xv[gi]);
     }
 
     // unconditional, so the count of loads in flight is static and the
@@ -258,21 +272,27 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
         int8_t *sq = reinterpret_cast<int8_t *>(stage);
         int16_t *sbs = reinterpret_cast<int16_t *>(stage + T * K);
         float *sd8 = reinterpret_cast<float *>(stage + T * K * 9 / 8);
-        auto quant = [&](int ch, float4 v) {
+        // every lane of the wave runs the quantiser (its amax is a DPP row
+        // reduction); rows past the last chunk hold zeros and store nothing
+        auto quant = [&](int g, const float (&v)[16]) {
+            const int ch = 4 * g + gsub;
             int qsum;
             float d8;
-            const uint32_t packed = q8k_chunk(v, qsum, d8);
-            reinterpret_cast<uint32_t *>(sq + (int64_t)ch * QK)[lane] = packed;
-            if ((lane & 3) == 0) sbs[ch * 16 + (lane >> 2)] = (int16_t)qsum;
-            if (lane == 0) sd8[ch] = d8;
+            const uint4 piece = q8k_piece16(v, qsum, d8);
+            if (ch < nchunks) {
+                reinterpret_cast<uint4 *>(sq + (int64_t)ch * QK)[gj] = piece;
+                sbs[ch * 16 + gj] = (int16_t)qsum;
+                if (gj == 0) sd8[ch] = d8;
+            }
         };
 #pragma unroll
-        for (int j = 0; j < CMAX; ++j) {
-            const int ch = wave + j * nw;
-            if (ch < nchunks) quant(ch, xr[j]);
+        for (int gi = 0; gi < GMAX; ++gi)
+            if (wave + gi * nw < ngroups) quant(wave + gi * nw, xv[gi]);
+        for (int g = wave + GMAX * nw; g < ngroups; g += nw) {
+            float v[16];
+            load_group(g, v);
+            quant(g, v);
         }
-        for (int ch = wave + CMAX * nw; ch < nchunks; ch += nw)
-            quant(ch, reinterpret_cast<const float4 *>(x + (int64_t)ch * QK)[lane]);
         __syncthreads();
         if (oq != nullptr && blockIdx.x == 0) {
             // the Q8_K image, for callers that keep it
@@ -384,14 +404,24 @@ struct GemvArgs {
 // Measured at batch 4 on the Qwen3-4B FFN matrices: reading from L2 took
 // 11.7-16.5 us per call against 4.9-6.9 us at batch 1 with the image staged.
 constexpr size_t STAGE_MAX = (size_t)48 << 10;
+// A batch of 1-2 stages its image (plus the f32 scales, which the fused
+// form keeps beside it) while it fits one workgroup's LDS with room to spare
+// (k up to about 128k at batch 1); longer rows read the codes from L2.
+constexpr size_t STAGE_MAX12 = (size_t)144 << 10;
+
+static bool staged_image(int64_t t, int64_t k)
+{
+    const size_t img = (size_t)t * k * 9 / 8;
+    return t <= 2 ? img + (size_t)t * (k / QK) * sizeof(float) <= STAGE_MAX12 : img <= STAGE_MAX;
+}
 
 template <int FMT, int T, int U, int SL, bool PART>
-static void launch_one(dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_one(bool staged, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
     // staged Q8_K image (codes + bsums), plus the scales when fused
     const size_t img = (size_t)T * a.nsb * QK * 9 / 8;
-    if constexpr (T <= 2) {
-        if constexpr (!PART) {
+    if (staged) {
+        if constexpr (T <= 2 && !PART) {
             if (a.x) {
                 hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, true, true>), g, b,
                                    img + (size_t)T * a.nsb * sizeof(float), st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs,
@@ -399,51 +429,48 @@ static void launch_one(dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
                 return;
             }
         }
-        hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, true>), g, b, img, st, a.w, a.n, a.nsb, a.xq,
-                           a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
-    } else {
-        // the partials (a test path) keep reading from L2
-        if constexpr (!PART) {
-            if (img <= STAGE_MAX) {
-                hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, false, true>), g, b, img, st, a.w, a.n, a.nsb,
-                                   a.xq, a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
-                return;
-            }
+        // the partials of a batch of 3-8 (a test path) keep reading from L2:
+        // the same sums in the same order
+        if constexpr (T <= 2 || !PART) {
+            hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, true>), g, b, img, st, a.w, a.n, a.nsb,
+                               a.xq, a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
+            return;
         }
-        hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, false>), g, b, 0, st, a.w, a.n, a.nsb, a.xq,
-                           a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
     }
+    hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, false>), g, b, 0, st, a.w, a.n, a.nsb, a.xq, a.xs,
+                       a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
 }
 
 template <int FMT, int T>
-static void launch_u(int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_u(bool stg, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
     if (sl == 4) {
-        if (part) return launch_one<FMT, T, 2, 4, true>(g, b, st, a);
-        if (u == 1) return launch_one<FMT, T, 1, 4, false>(g, b, st, a);
-        return launch_one<FMT, T, 2, 4, false>(g, b, st, a);
+        if (part) return launch_one<FMT, T, 2, 4, true>(stg, g, b, st, a);
+        if (u == 1) return launch_one<FMT, T, 1, 4, false>(stg, g, b, st, a);
+        return launch_one<FMT, T, 2, 4, false>(stg, g, b, st, a);
     }
-    if (part) return launch_one<FMT, T, 4, 1, true>(g, b, st, a);
+    if (part) return launch_one<FMT, T, 4, 1, true>(stg, g, b, st, a);
     switch (u) {
-    case 1: return launch_one<FMT, T, 1, 1, false>(g, b, st, a);
-    case 2: return launch_one<FMT, T, 2, 1, false>(g, b, st, a);
-    case 3: return launch_one<FMT, T, 3, 1, false>(g, b, st, a);
-    default: return launch_one<FMT, T, 4, 1, false>(g, b, st, a);
+    case 1: return launch_one<FMT, T, 1, 1, false>(stg, g, b, st, a);
+    case 2: return launch_one<FMT, T, 2, 1, false>(stg, g, b, st, a);
+    case 3: return launch_one<FMT, T, 3, 1, false>(stg, g, b, st, a);
+    default: return launch_one<FMT, T, 4, 1, false>(stg, g, b, st, a);
     }
 }
 
 template <int FMT>
-static void launch_t(int t, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_t(int t, bool stg, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st,
+                     const GemvArgs &a)
 {
     switch (t) {
-    case 1: return launch_u<FMT, 1>(sl, u, part, g, b, st, a);
-    case 2: return launch_u<FMT, 2>(sl, u, part, g, b, st, a);
-    case 3: return launch_u<FMT, 3>(sl, u, part, g, b, st, a);
-    case 4: return launch_u<FMT, 4>(sl, u, part, g, b, st, a);
-    case 5: return launch_u<FMT, 5>(sl, u, part, g, b, st, a);
-    case 6: return launch_u<FMT, 6>(sl, u, part, g, b, st, a);
-    case 7: return launch_u<FMT, 7>(sl, u, part, g, b, st, a);
-    default: return launch_u<FMT, 8>(sl, u, part, g, b, st, a);
+    case 1: return launch_u<FMT, 1>(stg, sl, u, part, g, b, st, a);
+    case 2: return launch_u<FMT, 2>(stg, sl, u, part, g, b, st, a);
+    case 3: return launch_u<FMT, 3>(stg, sl, u, part, g, b, st, a);
+    case 4: return launch_u<FMT, 4>(stg, sl, u, part, g, b, st, a);
+    case 5: return launch_u<FMT, 5>(stg, sl, u, part, g, b, st, a);
+    case 6: return launch_u<FMT, 6>(stg, sl, u, part, g, b, st, a);
+    case 7: return launch_u<FMT, 7>(stg, sl, u, part, g, b, st, a);
+    default: return launch_u<FMT, 8>(stg, sl, u, part, g, b, st, a);
     }
 }
 
@@ -452,8 +479,11 @@ static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const i
                            const float *x, int8_t *oq, float *os, int16_t *obs)
 {
     const int64_t nsb = k / QK;
-    // the fused kernel runs exactly when launch_one picks it
+    // the image is staged in LDS (always, for the fused kernel)
+    const bool staged = staged_image(t, k);
     const bool fused = x != nullptr && t <= 2 && P == nullptr;
+    if (x != nullptr && !fused) return KQ_EINVAL;
+    if (fused && !staged) return KQ_EINVAL;  // the fused kernel needs its image in LDS
     // 4 rows x 4 adjacent superblocks per wave step whenever the image is
     // staged in LDS (the fused path keeps the same shape, so its y is
     // bit-identical to quantise-then-GEMV).  A batch that reads its codes
@@ -463,12 +493,7 @@ static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const i
     // (9728 x 2560): batch 4 8.2-9.5 us against 10.7-13.6 us.  The choice
     // depends on t, k and n only, so the partials entry point (which reads
     // from L2) sums in the same order.
-    const int sl = (t <= 2 || (size_t)t * k * 9 / 8 <= STAGE_MAX) ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
-    // Row groups per workgroup (below).  Staging a read-only image costs a
-    // workgroup little, so the plain GEMV keeps one group per workgroup (the
-    // finest grain); the fused GEMV quantises the whole activation in every
-    // workgroup, so it groups rows down to about two workgroups per CU.
-    const int64_t min_wg = fused ? 512 : 0;
+    const int sl = staged ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
     const int64_t groups = (n + 16 / sl - 1) / (16 / sl);
     const int64_t nsteps = (nsb + sl - 1) / sl;
     // about 16 waves per CU in flight, at most 16 waves per workgroup, and
@@ -479,28 +504,38 @@ static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const i
     // staged batch of 3-8 gives each wave one step up to 16 steps (W_down at
     // batch 4: 59.7 against 62.3 us over the six matrices); like sl, this
     // depends on t, k and n only.
-    const bool staged3 = t > 2 && (size_t)t * k * 9 / 8 <= STAGE_MAX;
+    const bool staged3 = t > 2 && staged;
     int64_t nw = (nsteps <= 4 || (staged3 && nsteps <= 16)) ? nsteps : (4096 + groups - 1) / groups;
     nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
     nw = nw > nsteps ? nsteps : nw;
     const int64_t per_wave = (nsteps + nw - 1) / nw;
     const int64_t kw = (nsteps + per_wave - 1) / per_wave;
-    // Row groups per workgroup: doubled while the workgroup stays within 16
-    // waves and the grid keeps at least min_wg workgroups.  Each row's sum
-    // order depends only on kw and per_wave, so y does not change with the
+    // Row groups per workgroup.  Staging a read-only image costs a workgroup
+    // little, so the plain GEMV keeps one group per workgroup (the finest
+    // grain; grouping it measured slower on W_up, 5.1 -> 6.1 us).  The fused
+    // GEMV quantises the whole activation in every workgroup, so it takes
+    // as many row groups as 16 waves hold: the fewest workgroups.  Measured
+    // on the six FFN matrices at batch 1 (quantise + GEMV in one kernel, sum
+    // of the six): 58.4 us at about two workgroups per CU, 53.5-57.9 us at
+    // 6-12 waves per workgroup, 42.3 us at 15-16.  Each row's sum order
+    // depends only on kw and per_wave, so y does not change with the
     // grouping.
-    int64_t rgs = 1;
-    while (min_wg > 0 && 2 * rgs * kw <= 16 && (groups + 2 * rgs - 1) / (2 * rgs) >= min_wg) rgs *= 2;
+    int64_t rgs = fused ? 16 / kw : 1;
+    rgs = rgs > groups ? groups : rgs;
     const int umax = sl == 4 ? 2 : 4;
     const int u = per_wave >= umax ? umax : (int)per_wave;
     GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave, (int)kw, x, oq, os, obs};
     const dim3 g((unsigned)((groups + rgs - 1) / rgs)), b((unsigned)(64 * kw * rgs));
     const bool part = P != nullptr;
-    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, sl, u, part, g, b, st, a);
-    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, sl, u, part, g, b, st, a);
-    else launch_t<KQ_Q6_K>((int)t, sl, u, part, g, b, st, a);
+    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, staged, sl, u, part, g, b, st, a);
+    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, staged, sl, u, part, g, b, st, a);
+    else launch_t<KQ_Q6_K>((int)t, staged, sl, u, part, g, b, st, a);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
+
+// Whether the one-kernel quantise + GEMV (launch_gemv with x) takes t x k:
+// a batch of 1-2 whose image and scales fit the LDS stage.
+bool gemv_fusable(int64_t t, int64_t k) { return t <= 2 && staged_image(t, k); }
 
 // A batch of 3-8 whose Q8_K image is too large to stage runs as chunks of
 // the most tokens (at least 3) whose image does stage, one launch each; the

@@ -34,6 +34,15 @@
 
 namespace kq {
 
+// a / b for 0 <= a and 0 < b < 2^31; a 32-bit division whenever a < 2^32
+// (every realistic grid: the 64-bit one is a long instruction sequence ahead
+// of the first load)
+__device__ inline int64_t udiv(int64_t a, int b)
+{
+    if (a <= (int64_t)UINT32_MAX) return (int64_t)((uint32_t)a / (uint32_t)b);
+    return a / b;
+}
+
 template <bool TILES, bool GATHER>
 __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restrict__ x, int64_t t,
                                                            const int32_t *__restrict__ src, int64_t m,
@@ -43,7 +52,7 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restri
     const int lane = threadIdx.x & 63;
     const int64_t chunk = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (chunk >= rows * nsb) return;  // whole wave exits together
-    const int64_t row = chunk / nsb;
+    const int64_t row = udiv(chunk, nsb);
     const int sb = (int)(chunk - row * nsb);
     // image row `row` (< m: a real row, else tile padding) quantises source
     // row srow of x; a gather index outside [0, t) gives a zero row
@@ -80,12 +89,6 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float *__restri
     }
 }
 
-template <int CTRL>
-__device__ inline float dpp_maxf(float v)
-{
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false)));
-}
-
 // Wide form, for large batches: lane l of a wave holds values 16j .. 16j+15
 // (j = l % 16) of chunk l / 16 of the wave, so its 16 codes are one bsum
 // group and one 16-byte piece of either image (the tile form's four chunks
@@ -107,13 +110,13 @@ __global__ __launch_bounds__(256) void quantize_q8k_wide_kernel(const float *__r
     if constexpr (TILES) {
         // four consecutive tokens of one superblock: their code pieces are
         // adjacent in the tile image
-        const int64_t quad = wave / nsb;
+        const int64_t quad = udiv(wave, nsb);
         sb = (int)(wave - quad * nsb);
         row = quad * 4 + sub;
         if (quad * 4 >= rows) return;  // whole wave exits together
     } else {
         const int64_t chunk = wave * 4 + sub;
-        row = chunk / nsb;
+        row = udiv(chunk, nsb);
         sb = (int)(chunk - row * nsb);
         if (wave * 4 >= rows * nsb) return;
     }
@@ -134,28 +137,10 @@ __global__ __launch_bounds__(256) void quantize_q8k_wide_kernel(const float *__r
             v[4 * i + 3] = f.w;
         }
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = dpp_maxf<0xB1>(amax);   // quad_perm [1,0,3,2]
-    amax = dpp_maxf<0x4E>(amax);   // quad_perm [2,3,0,1]
-    amax = dpp_maxf<0x141>(amax);  // row_half_mirror
-    amax = dpp_maxf<0x140>(amax);  // row_mirror: every lane of the row holds its chunk's amax
-    float d8 = 0.0f;
-    uint32_t pk[4] = {0, 0, 0, 0};
-    int qsum = 0;
-    if (amax != 0.0f) {
-        d8 = __fdiv_rn(amax, 127.0f);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            int a = (int)rintf(__fdiv_rn(v[i], d8));
-            a = a > 127 ? 127 : (a < -127 ? -127 : a);
-            qsum += a;
-            pk[i >> 2] |= (uint32_t)(a & 0xFF) << (8 * (i & 3));
-        }
-    }
+    int qsum;
+    float d8;
+    const uint4 piece = q8k_piece16(v, qsum, d8);
     if (!inrange) return;
-    const uint4 piece = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     if constexpr (TILES) {
         // codes 16j..16j+15 of superblock sb: K chunk c = 8*sb + j/2, half q = j & 1
         const int64_t g = row >> 5;

@@ -224,6 +224,11 @@ def test_fused_gemv_argument_checks():
     assert call(t=3) == kq.KQ_EINVAL
     assert call(x=GOOD16 + 4) == kq.KQ_EALIGN
     assert call(xq=GOOD16 + 4, xs=GOOD16, xbs=GOOD16) == kq.KQ_EALIGN
+    # the one-kernel form stages the image and its scales in LDS: past
+    # 147456 bytes (k = 129024 at t = 1, 64512 at t = 2) the call needs the
+    # image buffers for its two launches
+    assert call(k=129280) == kq.KQ_EINVAL
+    assert call(t=2, k=64768) == kq.KQ_EINVAL
 
 
 def test_quantize_and_pack_argument_checks():

@@ -117,15 +117,10 @@ def test_quantize_tiles_bit_exact(t, k):
     assert not bs[t:].any()
 
 
-@pytest.mark.parametrize("t,k", [(1, 2560), (5, 1536), (40, 768), (300, 2560)])
-def test_quantize_quotient_chunks_every_form(t, k):
-    # chunks built so that rint(x/d8) and rint(x * (1/d8)) differ in many
-    # places: every device quantiser (row, tile, gather, and the one fused
-    # into the GEMV) must take the binary32 quotient, as the oracle does
-    nsb = k // 256
-    x = synth.activations(t, k, 80 + t)
-    edge = quotient_chunks(min(t * nsb, 12), seed=81 + t)
-    x.reshape(-1, 256)[: len(edge)] = edge
+def _every_quantiser_matches_oracle(x, seed):
+    """Every device quantiser (row, tile, gather, and the one fused into the
+    GEMV) gives the oracle's Q8_K bits for x[t][k]."""
+    t, k = x.shape
     rq, rs, rbs = oracle.quantize_q8k(x)
     xd = dev(x)
     xq, xs, xbs = ops.quantize_q8k(xd)
@@ -143,7 +138,7 @@ def test_quantize_quotient_chunks_every_form(t, k):
     assert np.array_equal(host(gs)[:t].view(np.uint32), rs[::-1].view(np.uint32))
     if t <= 8:
         n = 64
-        recs = synth.weights("q4_k", n, k, 82)
+        recs = synth.weights("q4_k", n, k, seed)
         planes = ops.pack("q4_k", ops.upload_records(recs), n, k)
         _, (fq, fs, fbs) = ops.gemv_f32("q4_k", planes, n, k, xd, keep_image=True)
         assert np.array_equal(host(fq), rq)
@@ -152,6 +147,33 @@ def test_quantize_quotient_chunks_every_form(t, k):
         if t <= 2:  # the one-kernel form quantises inside every workgroup
             y1 = ops.gemv_f32("q4_k", planes, n, k, xd)
             assert torch.equal(y1, ops.gemv("q4_k", planes, n, k, (xq, xs, xbs)))
+
+
+@pytest.mark.parametrize("t,k", [(1, 2560), (2, 1024), (5, 1536), (40, 768), (300, 2560)])
+def test_quantize_quotient_chunks_every_form(t, k):
+    # chunks built so that rint(x/d8) and rint(x * (1/d8)) differ in many
+    # places: every device quantiser must take the binary32 quotient, as
+    # the oracle does
+    nsb = k // 256
+    x = synth.activations(t, k, 80 + t)
+    edge = quotient_chunks(min(t * nsb, 12), seed=81 + t)
+    x.reshape(-1, 256)[: len(edge)] = edge
+    _every_quantiser_matches_oracle(x, 82)
+
+
+@pytest.mark.parametrize("t,k", [(1, 2560), (2, 1024), (6, 768), (300, 1024)])
+def test_quantize_tiny_and_huge_scales_every_form(t, k):
+    # chunks scaled by powers of two from 2^-90 to 2^99 (d8 from about
+    # 2^-95 to 2^94): below d8 = 2^-64 the device divides per value, above
+    # it it multiplies by 1/d8 and corrects twice; both must give the
+    # oracle's bits, the quotient-edge chunks included
+    x = synth.activations(t, k, 85 + t).reshape(-1, 256)
+    edge = quotient_chunks(min(len(x), 12), seed=86 + t)
+    x[: len(edge)] = edge
+    e = np.random.default_rng(87 + t).integers(-90, 100, size=len(x))
+    e[: min(len(x), 4)] = [-90, -62, -58, 99][: min(len(x), 4)]
+    x = (x.astype(np.float64) * np.ldexp(1.0, e)[:, None]).astype(np.float32).reshape(t, k)
+    _every_quantiser_matches_oracle(x, 88)
 
 
 # ------------------------------------------------------------ pack ------
@@ -401,3 +423,28 @@ def test_long_k_all_kernels(fmt):
             assert ws > 0  # the split form ran above
             check_y(c, ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=None))
             assert torch.equal(ops.gemm(fmt, c.planes, n, k, c.q8), y)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_rows_past_the_lds_stage(fmt):
+    # a batch of 1-2 stages its Q8_K image and scales in LDS up to 147456
+    # bytes (k = 129024 at t = 1, 64512 at t = 2); longer rows read their
+    # codes from L2, and kq_gemv_f32 then runs quantiser + GEMV, which needs
+    # the image buffers
+    n = 24
+    for t, k, fits in ((1, 129024, True), (1, 129280, False), (2, 64768, False)):
+        c = Case(fmt, n, k, t, seed=95 + t)
+        y, P, M = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
+        check(c, y, P, M)
+        assert torch.equal(ops.gemv(fmt, c.planes, n, k, c.q8), y)
+        xd = dev(c.x)
+        yf, (xq, xs, xbs) = ops.gemv_f32(fmt, c.planes, n, k, xd, keep_image=True)
+        assert torch.equal(yf, y)
+        rq, rs, rbs = c.q8_host
+        assert np.array_equal(host(xq), rq) and np.array_equal(host(xbs), rbs)
+        assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
+        if fits:
+            assert torch.equal(ops.gemv_f32(fmt, c.planes, n, k, xd), y)
+        else:
+            with pytest.raises(kq.KqError):
+                ops.gemv_f32(fmt, c.planes, n, k, xd)
