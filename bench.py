@@ -15,19 +15,27 @@ enough distinct copies that one step's rotation reads over 1 GiB of weights,
 so the 256 MB Infinity Cache cannot serve them from cache: every GEMV reads
 its weights from HBM.
 
-The GEMV leg runs kq_quantize_q8k then kq_gemv; the fused entry point
-kq_gemv_f32 (Q8_K quantisation inside the GEMV kernel, one launch) is timed
-beside it as gemv_fused.
+The GEMV leg runs kq_gemv_f32, the Q8_K quantisation inside the GEMV
+kernel (one launch per matrix); the same leg as two launches per matrix
+(kq_quantize_q8k, then kq_gemv on the image) is timed after the timed steps
+as gemv_two_launch.
 
-Printed: one JSON line.  Each leg is captured into a HIP graph (one per
-weight copy) and replayed, so the GPU runs its launches back to back.
-`value` is the GEMV leg's throughput in GB/s of algorithmic bytes (packed
-weights + Q8_K image + f32 output) over the leg's GPU time (HIP events
-around the replay), quantiser launches included; `gemm` holds the GEMM leg's
-int8 TOPS (2*M*N*K useful ops).  `roofline` / `roofline_gemm` divide the
-same algorithmic work by the average duration of back-to-back launches of
-the GEMV / GEMM kernel alone (a graph of repeated launches between one pair
-of HIP events on the launch stream, inside the timed region).
+Printed: one JSON line.  Each leg is captured into HIP graphs: one per
+weight copy (one step) and one per rotation over all the copies (a step per
+copy, as a model captures a whole decode token of hundreds of launches in
+one graph).  The timed region runs the GEMV leg of all steps back to back
+(whole rotations, then single steps for the rest), then the GEMM leg of all
+steps, one HIP-event pair around each phase.  `value` is the GEMV leg's
+throughput in GB/s of algorithmic bytes (packed weights + f32 activation +
+f32 output) over its phase's GPU time; `gemm` holds the GEMM leg's int8
+TOPS (2*M*N*K useful ops), quantiser launches included in both.
+`roofline` divides the same algorithmic bytes by the average duration of
+back-to-back launches of the leg's one kernel (kq_gemv_f32), and
+`roofline_gemv_image` does the same for the GEMV kernel on a resident Q8_K
+image (kq_gemv; the image's 292 bytes per 256 activations in place of the
+f32 activation); `roofline_gemm` the GEMM's int8 ops.  Each of those is a
+graph of repeated launches between one pair of HIP events on the launch
+stream, inside the timed region.
 
 Two further measurements run after the timed steps, each in its own graphs:
 `gemm_mid` (the 32-token tile: quantise 64 rows + kq_gemm on the same six
@@ -75,10 +83,12 @@ BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 # profiles/kq_gemm_hbm_traffic_qwen3_4b_ffn_pp512.md; the GEMM figure is one
 # kq_gemm call, split-sum pass included).  Each holds only for the sources
 # it was measured on; with any other sources the roofline reports null.
-GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "1604315dabe74847",
-                "bytes_per_launch": 17412658}
-GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "11609855197ded27",
-                "bytes_per_launch": 74635230}
+GEMV_F32_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f9a8f3e76bbef2ca",
+                    "bytes_per_launch": 17609692}
+GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f9a8f3e76bbef2ca",
+                "bytes_per_launch": 17415559}
+GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
+                "bytes_per_launch": 74525348}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
                "src_sha256_16": "81cae00ede1dceca", "bytes_per_launch": 35192565}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
@@ -87,11 +97,12 @@ MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
 
 # Mean per-dispatch duration of the same kernels in the committed rocprofv3
 # kernel trace of a full bench run (profiles/kq_gemv_gemm_qwen3_4b_ffn_trace.md,
-# value-leg window), so the line carries the roofline fraction from both
+# timed-region window), so the line carries the roofline fraction from both
 # timers; tied to the sources like the traffic records.
-GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "1604315dabe74847", "avg_us": 6.38}
-GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "11609855197ded27",
-              "avg_us": 48.51}
+GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f9a8f3e76bbef2ca", "avg_us": 7.51}
+GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f9a8f3e76bbef2ca", "avg_us": 6.48}
+GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
+              "avg_us": 50.95}
 
 
 def trace_us(rec):
@@ -134,7 +145,7 @@ def parse():
                     help="replays of the gemm_mid / moe graphs (after the timed steps)")
     ap.add_argument("--profile-one", metavar="KIND:FMT:N:K:T",
                     help="instead of the benchmark, run one configuration --reps times (for "
-                         "rocprofv3 counter passes): KIND gemv|gemm|mid (T activation rows), "
+                         "rocprofv3 counter passes): KIND gemv|gemv_f32|gemm|mid (T activation rows), "
                          "moe (the MoE layer; FMT:N:K:T ignored), copy (a plain 64 MiB device "
                          "copy, the counters' byte reference)")
     ap.add_argument("--reps", type=int, default=10)
@@ -641,10 +652,8 @@ def bench_layers(reps, stream, capture, ev):
 
     # The same token as a model would lay it out: q|k and gate|up, which
     # share an input and a format, packed as one matrix each (rows
-    # concatenated), and the quantisation fused into the GEMV
-    # (kq_gemv_f32) for the inputs of width 2560 and 4096; the down
-    # projection (width 9728) keeps the separate quantiser, which is faster
-    # there.  6 launches per layer instead of 11.
+    # concatenated), and the quantisation fused into every GEMV
+    # (kq_gemv_f32).  5 launches per layer instead of 11.
     names = [e[0] for e in LAYER_SET]
 
     def cat(parts_names):
@@ -669,11 +678,7 @@ def bench_layers(reps, stream, capture, ev):
     def decode_fused():
         for L in range(N_LAYERS):
             for j, ((fmt, n, k, pl), inp) in enumerate(zip(fused_layer, fused_in)):
-                if k <= 4096:
-                    kq.kq_gemv_f32(fmt, pl[L], n, k, x1[inp], 1, yf[j])
-                else:
-                    kq.kq_quantize_q8k(x1[inp], 1, k, *q1[inp])
-                    kq.kq_gemv(fmt, pl[L], n, k, *q1[inp], 1, yf[j])
+                kq.kq_gemv_f32(fmt, pl[L], n, k, x1[inp], 1, yf[j])
 
     # the prefill over the same merged matrices (q|k: 5120 rows, gate|up:
     # 19456 rows), one quantisation per distinct input
@@ -710,7 +715,7 @@ def bench_layers(reps, stream, capture, ev):
             "decode_launches_per_token": N_LAYERS * (len(layer) + len(LAYER_INPUTS)),
             "decode_fused_us_per_token": res["decode_fused"],
             "decode_fused_GBps": dec_alg / (res["decode_fused"] * 1e-6) / 1e9,
-            "decode_fused_launches_per_token": N_LAYERS * 6,
+            "decode_fused_launches_per_token": N_LAYERS * len(fused_layer),
             "prefill_us": res["prefill"],
             "prefill_TOPS": ops_prefill / (res["prefill"] * 1e-6) / 1e12,
             "prefill_frac_mfma": ops_prefill / (res["prefill"] * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS,
@@ -747,6 +752,9 @@ def profile_one(spec, reps):
             q = ops.quantize_q8k(x)
             for _ in range(reps):
                 kq.kq_gemv(fmt, planes, n, k, *q, t, y)
+        elif kind == "gemv_f32":
+            for _ in range(reps):
+                kq.kq_gemv_f32(fmt, planes, n, k, x, t, y)
         else:
             q = ops.quantize_q8k_tiles(x)
             ws = ops.gemm_tiles_workspace(fmt, n, k, t)
@@ -879,16 +887,16 @@ def main():
     # replayed, so the GPU runs the launches back to back instead of
     # waiting on Python's launch rate.
     def gemv_leg(c):
-        # decode: quantise the f32 activation to Q8_K, then the GEMV
+        # decode: the f32 activation quantised to Q8_K inside the GEMV kernel
+        for j, (fmt, n, k, pl) in enumerate(mats):
+            kq.kq_gemv_f32(fmt, pl[c], n, k, acts[k][0], 1, ys[j][0])
+
+    def gemv_leg_two(c):
+        # the same as two launches: the quantiser, then the GEMV on the image
         for j, (fmt, n, k, pl) in enumerate(mats):
             x1, (xq, xs, xbs), _, _ = acts[k]
             kq.kq_quantize_q8k(x1, 1, k, xq, xs, xbs)
             kq.kq_gemv(fmt, pl[c], n, k, xq, xs, xbs, 1, ys[j][0])
-
-    def gemv_leg_fused(c):
-        # the same with the quantiser fused into the GEMV (kq_gemv_f32)
-        for j, (fmt, n, k, pl) in enumerate(mats):
-            kq.kq_gemv_f32(fmt, pl[c], n, k, acts[k][0], 1, ys[j][0])
 
     def gemm_leg(c):
         for j, (fmt, n, k, pl) in enumerate(mats):
@@ -901,7 +909,9 @@ def main():
         x1, q1, xm, qm = acts[k]
         for r in range(reps):
             c = r % copies
-            if kind == "gemv":
+            if kind == "gemv_f32":
+                kq.kq_gemv_f32(fmt, pl[c], n, k, x1, 1, ys[j][0])
+            elif kind == "gemv":
                 kq.kq_gemv(fmt, pl[c], n, k, *q1, 1, ys[j][0])
             else:
                 kq.kq_gemm_tiles(fmt, pl[c], n, k, *qm, GEMM_M, ys[j][1], wss[j])
@@ -917,44 +927,59 @@ def main():
             fn(*a)
         return g
 
-    graphs = {}
+    # one graph per step (weight copy c), and one per whole rotation over
+    # the copies (`copies` steps in one replay, as a model captures a whole
+    # decode token of hundreds of launches); a phase of K steps replays
+    # whole rotations, then single steps for the rest
+    def rotation(leg):
+        for c in range(copies):
+            leg(c)
+
+    graphs, rgraphs = {}, {}
+    legfns = {}
     if "gemv" in legs:
-        graphs["gemv"] = [capture(gemv_leg, c) for c in range(copies)]
-        graphs["gemv2"] = [capture(gemv_leg_fused, c) for c in range(copies)]
+        legfns["gemv"], legfns["gemv2"] = gemv_leg, gemv_leg_two
     if "gemm" in legs:
-        graphs["gemm"] = [capture(gemm_leg, c) for c in range(copies)]
+        legfns["gemm"] = gemm_leg
+    for kind, fn in legfns.items():
+        graphs[kind] = [capture(fn, c) for c in range(copies)]
+        rgraphs[kind] = capture(rotation, fn)
     # activations quantised once for the kernel-only graphs
     for k in acts:
         x1, q1, xm, qm = acts[k]
         kq.kq_quantize_q8k(x1, 1, k, *q1)
         kq.kq_quantize_q8k_tiles(xm, GEMM_M, k, *qm)
-    reps = {"gemv": 8 * copies, "gemm": copies}
-    kgraphs = {kind: [capture(kernel_only, kind, j, reps[kind]) for j in range(len(mats))]
-               for kind in ("gemv", "gemm") if kind in graphs}
+    reps = {"gemv_f32": 8 * copies, "gemv": 8 * copies, "gemm": copies}
+    kinds = (("gemv_f32", "gemv") if "gemv" in graphs else ()) + (("gemm",) if "gemm" in graphs else ())
+    kgraphs = {kind: [capture(kernel_only, kind, j, reps[kind]) for j in range(len(mats))] for kind in kinds}
     torch.cuda.synchronize()
 
-    def run_steps(nsteps, rec):
-        for i in range(nsteps):
-            c = i % copies
-            for kind in ("gemv", "gemv2", "gemm"):
-                if kind in graphs:
-                    a, b = ev(), ev()
-                    a.record(stream)
-                    graphs[kind][c].replay()
-                    b.record(stream)
-                    rec[kind].append((a, b))
+    def phase(kind, nsteps):
+        # nsteps passes of one leg back to back, one event pair around them
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(nsteps // copies):
+            rgraphs[kind].replay()
+        for i in range(nsteps % copies):
+            graphs[kind][i].replay()
+        b.record(stream)
+        return a, b
 
-    run_steps(args.warmup, {"gemv": [], "gemv2": [], "gemm": []})
+    for kind in graphs:
+        phase(kind, args.warmup)
     torch.cuda.synchronize()
 
     # ------------------------------------------------------ timed region --
-    rec = {"gemv": [], "gemv2": [], "gemm": []}
-    krec = {kind: [] for kind in kgraphs}
+    # every step's GEMV leg, then every step's GEMM leg: args.steps passes
+    # of the whole path
+    rec, krec = {}, {kind: [] for kind in kgraphs}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = ev()
     start.record(stream)
-    run_steps(args.steps, rec)
+    for kind in ("gemv", "gemm"):
+        if kind in graphs:
+            rec[kind] = phase(kind, args.steps)
     end = ev()
     end.record(stream)
     for kind in kgraphs:  # kernel-only replays: the roofline's launch durations
@@ -967,9 +992,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
+    # the two-launch GEMV leg, after the timed region
+    if "gemv2" in graphs:
+        rec["gemv2"] = phase("gemv2", args.steps)
+        torch.cuda.synchronize()
 
-    def ms(ps):
-        return sum(a.elapsed_time(b) for a, b in ps)
+    def ms(pair):
+        return pair[0].elapsed_time(pair[1])
 
     out = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": total_ms / args.steps, "higher_is_better": True,
@@ -987,35 +1016,41 @@ def main():
     per = {}
     if "gemv" in graphs:
         leg_ms = ms(rec["gemv"])
-        leg_bytes = args.steps * sum(gemv_bytes(f, n, k, fused=False) for f, n, k, _ in mats)
+        leg_bytes = args.steps * sum(gemv_bytes(f, n, k, fused=True) for f, n, k, _ in mats)
         out["value"] = leg_bytes / (leg_ms * 1e-3) / 1e9
         out["gemv_leg_ms_per_step"] = leg_ms / args.steps
         leg2_ms = ms(rec["gemv2"])
-        leg2_bytes = args.steps * sum(gemv_bytes(f, n, k, fused=True) for f, n, k, _ in mats)
-        out["gemv_fused"] = {"value": leg2_bytes / (leg2_ms * 1e-3) / 1e9, "unit": "GB/s",
-                             "note": "kq_gemv_f32: Q8_K quantisation inside the GEMV, one launch per matrix"}
-        kb = sum(reps["gemv"] * gemv_bytes(f, n, k, fused=False) for f, n, k, _ in mats)
-        kms = ms(krec["gemv"])
-        ach = kb / (kms * 1e-3) / 1e9
-        traffic = measured_traffic(GEMV_TRAFFIC)
-        alg = kb / (reps["gemv"] * len(mats))
-        tus = trace_us(GEMV_TRACE)
-        out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
-                           "algorithmic_bytes_per_launch": alg,
-                           "kernel": "kq::gemv_kernel (kq_gemv)",
-                           "avg_launch_us": kms * 1e3 / (reps["gemv"] * len(mats)),
-                           "timer": "HIP events around graph replays of back-to-back launches",
-                           "trace_avg_us": tus,
-                           "frac_trace": None if tus is None else alg / (tus * 1e-6) / 1e9 / HBM_PEAK_GBPS}
-        for j, (f, n, k, _) in enumerate(mats):
-            us = krec["gemv"][j][0].elapsed_time(krec["gemv"][j][1]) * 1e3 / reps["gemv"]
-            per.setdefault(f"{f}_{n}x{k}", {})["gemv"] = {
-                "us": us, "GBps": gemv_bytes(f, n, k, fused=False) / (us * 1e-6) / 1e9}
+        leg2_bytes = args.steps * sum(gemv_bytes(f, n, k, fused=False) for f, n, k, _ in mats)
+        out["gemv_two_launch"] = {"value": leg2_bytes / (leg2_ms * 1e-3) / 1e9, "unit": "GB/s",
+                                  "leg_ms_per_step": leg2_ms / args.steps,
+                                  "note": "kq_quantize_q8k then kq_gemv, two launches per matrix; algorithmic "
+                                          "bytes count the Q8_K image in place of the f32 activation"}
+
+        def roof(kind, fused, label, traffic_rec, trace_rec):
+            kb = sum(reps[kind] * gemv_bytes(f, n, k, fused=fused) for f, n, k, _ in mats)
+            kms = sum(ms(p) for p in krec[kind])
+            ach = kb / (kms * 1e-3) / 1e9
+            alg = kb / (reps[kind] * len(mats))
+            tus = trace_us(trace_rec)
+            for j, (f, n, k, _) in enumerate(mats):
+                us = ms(krec[kind][j]) * 1e3 / reps[kind]
+                per.setdefault(f"{f}_{n}x{k}", {})[kind] = {
+                    "us": us, "GBps": gemv_bytes(f, n, k, fused=fused) / (us * 1e-6) / 1e9}
+            return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic(traffic_rec),
+                    "algorithmic_bytes_per_launch": alg, "kernel": label,
+                    "avg_launch_us": kms * 1e3 / (reps[kind] * len(mats)),
+                    "timer": "HIP events around graph replays of back-to-back launches",
+                    "trace_avg_us": tus,
+                    "frac_trace": None if tus is None else alg / (tus * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        out["roofline"] = roof("gemv_f32", True, "kq::gemv_kernel, quantiser fused (kq_gemv_f32, batch 1)",
+                               GEMV_F32_TRAFFIC, GEMV_F32_TRACE)
+        out["roofline_gemv_image"] = roof("gemv", False, "kq::gemv_kernel on a resident Q8_K image (kq_gemv, batch 1)",
+                                          GEMV_TRAFFIC, GEMV_TRACE)
     if "gemm" in graphs:
         leg_ms = ms(rec["gemm"])
         ops_step = sum(2 * GEMM_M * n * k for _, n, k, _ in mats)
-        kms = ms(krec["gemm"])
+        kms = sum(ms(p) for p in krec["gemm"])
         ach = reps["gemm"] * ops_step / (kms * 1e-3) / 1e12
         out["gemm"] = {"value": args.steps * ops_step / (leg_ms * 1e-3) / 1e12, "unit": "TOPS",
                        "leg_ms_per_step": leg_ms / args.steps}
@@ -1033,18 +1068,19 @@ def main():
                                 "frac_trace": None if tus is None else
                                 ops_launch / (tus * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS}
         for j, (f, n, k, _) in enumerate(mats):
-            us = krec["gemm"][j][0].elapsed_time(krec["gemm"][j][1]) * 1e3 / reps["gemm"]
+            us = ms(krec["gemm"][j]) * 1e3 / reps["gemm"]
             per.setdefault(f"{f}_{n}x{k}", {})["gemm"] = {
                 "us": us, "TOPS": 2 * GEMM_M * n * k / (us * 1e-6) / 1e12}
     out["per_matrix"] = per
     if "probes" in legs:
         pr = bench_probes(mats, copies, stream, capture, ev)
         out["probes"] = pr
-        if "roofline" in out:
-            out["roofline"]["achievable"] = {
-                "value": pr["read_GBps"], "unit": "GB/s", "frac": out["roofline"]["achieved"] / pr["read_GBps"],
-                "probe": "kq_probe_read_u: plain 16-byte streaming read of the same plane buffers, best of six "
-                         "launch shapes"}
+        for key in ("roofline", "roofline_gemv_image"):
+            if key in out:
+                out[key]["achievable"] = {
+                    "value": pr["read_GBps"], "unit": "GB/s", "frac": out[key]["achieved"] / pr["read_GBps"],
+                    "probe": "kq_probe_read_u: plain 16-byte streaming read of the same plane buffers, best of "
+                             "six launch shapes"}
         if "roofline_gemm" in out:
             t = pr["mfma_i8_TOPS"]
             out["roofline_gemm"]["achievable"] = {
