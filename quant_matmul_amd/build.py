@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkq.so")
-SOURCES = ["kq_api.hip", "kq_quantize.hip", "kq_pack.hip", "kq_gemv.hip", "kq_gemm.hip", "kq_gemm_mid.hip"]
+SOURCES = ["kq_api.hip", "kq_quantize.hip", "kq_pack.hip", "kq_gemv.hip", "kq_gemv_mma.hip", "kq_gemm.hip", "kq_gemm_mid.hip"]
 PROBE_DIR = os.path.join(ROOT, "probes")
 PROBE_SRC = os.path.join(PROBE_DIR, "kq_probe.hip")
 PROBE_LIB = os.path.join(PROBE_DIR, "libkq_probe.so")

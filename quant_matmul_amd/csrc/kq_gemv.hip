@@ -1,4 +1,6 @@
-// kq_gemv.hip -- decode GEMV, batch 1..8 (gfx950).
+// kq_gemv.hip -- decode GEMV, batch 1..8 (gfx950): batches 1-2 here, on
+// packed int8 dot instructions; batches 3-8 on the matrix cores
+// (kq_gemv_mma.hip), where the per-token dot work would dominate.
 //
 // y[t][n] = sum_s fold(P, M) over superblocks s (K-quant kernel arc page,
 // "The pieces", kq v2 item; k4 v2 and k5/k6 v2 commit messages): the
@@ -172,7 +174,7 @@ __device__ inline float dpp_f(float v)
 // into its LDS stage (the same per-chunk arithmetic as kq_quantize_q8k, so
 // the image is bit-identical) instead of reading a Q8_K image; workgroup 0
 // also writes that image out when oq is non-null.
-template <int FMT, int T, int U, int SL, bool PART, bool FUSE, bool STG, bool TH = false>
+template <int FMT, int T, int U, int SL, bool PART, bool FUSE, bool STG>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                     const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                     const int16_t *__restrict__ xbs, float *__restrict__ y,
@@ -181,8 +183,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
                                                     int8_t *__restrict__ oq, float *__restrict__ os,
                                                     int16_t *__restrict__ obs)
 {
-    static_assert(!FUSE || (T <= 2 && STG), "the fused quantiser stages the image in LDS");
-    static_assert(!TH || (STG && !FUSE && !PART && U == 1 && T >= 3), "token halves: one staged step per wave");
+    static_assert(T <= 2, "batches past 2 run on the matrix cores");
+    static_assert(!FUSE || STG, "the fused quantiser stages the image in LDS");
     constexpr int RPW = 16 / SL;
     __shared__ float red[16][T][RPW];
     const int lane = threadIdx.x & 63;
@@ -213,23 +215,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
 
     // STG: the whole Q8_K image (codes + bsums, T*K*9/8 bytes) is staged in
     // LDS with coalesced 16-byte loads, so no lane waits on an L2 round trip
-    // for its codes after its weights land (batches 1-2 always; larger
-    // batches while the image is small enough that several workgroups still
-    // fit on a CU).  Otherwise the codes are read straight from L2 inside
-    // the loop.  Memory counters retire in issue order, so the staging
-    // loads go out before the weight loads: writing them to LDS then waits
-    // only for themselves, and their L2 latency hides under the HBM fetch of
-    // the weights.
-    //
-    // TH (token halves, batches whose whole image is too large to stage):
-    // the image passes through LDS in two halves of tokens while each wave
-    // keeps its one step of weights in registers, so the weights are still
-    // read once.
+    // for its codes after its weights land (while it fits: k up to about
+    // 128k; longer rows read the codes straight from L2 inside the loop).
+    // Memory counters retire in issue order, so the staging loads go out
+    // before the weight loads: writing them to LDS then waits only for
+    // themselves, and their L2 latency hides under the HBM fetch of the
+    // weights.
     constexpr bool LDSA = STG;
-    constexpr int TC = TH ? (T + 1) / 2 : T;  // tokens staged at once
-    constexpr int SMAX = T <= 2 ? 2 : 8;      // staged 16-byte chunks held per thread
+    constexpr int SMAX = 2;  // staged 16-byte chunks held per thread
     extern __shared__ __align__(16) uint8_t stage[];
-    const int64_t nq = TC * K / 16, nst = nq + TC * K / 128;  // chunks: codes, then bsums
+    const int64_t nq = T * K / 16, nst = nq + T * K / 128;  // chunks: codes, then bsums
     auto src_chunk = [&](int64_t i) {
         return i < nq ? reinterpret_cast<const uint4 *>(xq)[i] : reinterpret_cast<const uint4 *>(xbs)[i - nq];
     };
@@ -324,49 +319,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
         for (int64_t i = threadIdx.x + (int64_t)SMAX * blockDim.x; i < nst; i += blockDim.x) dst[i] = src_chunk(i);
         __syncthreads();
         aq = reinterpret_cast<const int8_t *>(stage);
-        ab = reinterpret_cast<const int16_t *>(stage + TC * K);
+        ab = reinterpret_cast<const int16_t *>(stage + T * K);
     }
 
-    if constexpr (TH) {
-        constexpr int TN = T - TC;
-        const int j = j_begin;
-        const int s = sb_at(j);
-        const bool live = j * SL + sig < nsb;
-        // tokens t0 .. t0 + NT - 1, whose codes and bsums are in the stage
-        auto half = [&](auto count, int t0) {
-            constexpr int NT = decltype(count)::value;
-            Act cur[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                load_act<FMT>(cur[t], aq + t * K + (int64_t)s * QK, ab + t * KB + (int64_t)s * 16, c);
-            Lane part[NT];
-            float d, dmin = 0.0f;
-            if constexpr (FMT == KQ_Q6_K)
-                compute_q6<NT>(raw[0], c, cur, part, d);
-            else
-                compute_q45<FMT, NT>(raw[0], c, cur, part, d, dmin);
-            d = live ? d : 0.0f;
-            dmin = live ? dmin : 0.0f;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int P = quad_sum(part[t].p);
-                const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
-                const float d8 = d8src[(t0 + t) * nsb + s];
-                acc[t0 + t] = fmaf(d * d8, (float)P, acc[t0 + t]);
-                if (FMT != KQ_Q6_K) acc[t0 + t] = fmaf(-(dmin * d8), (float)M, acc[t0 + t]);
-            }
-        };
-        half(std::integral_constant<int, TC>{}, 0);
-        __syncthreads();  // every wave is done with the first half
-        const int64_t nq2 = TN * K / 16, nst2 = nq2 + TN * K / 128;
-        const uint4 *srcq = reinterpret_cast<const uint4 *>(xq + TC * K);
-        const uint4 *srcb = reinterpret_cast<const uint4 *>(xbs + TC * KB);
-        uint4 *dst = reinterpret_cast<uint4 *>(stage);
-        for (int64_t i = threadIdx.x; i < nst2; i += blockDim.x) dst[i] = i < nq2 ? srcq[i] : srcb[i - nq2];
-        __syncthreads();
-        ab = reinterpret_cast<const int16_t *>(stage + TN * K);
-        half(std::integral_constant<int, TN>{}, TC);
-    } else
     for (int j0 = j_begin; j0 < j_end; j0 += U) {
         if (j0 != j_begin) {
 #pragma unroll
@@ -378,63 +333,31 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
             if (j >= j_end) break;
             const int s = sb_at(j);
             const bool live = j * SL + sig < nsb;  // slot holds a real superblock
-            if constexpr (LDSA || T <= 2) {
-                Act cur[T];
+            Act cur[T];
 #pragma unroll
-                for (int t = 0; t < T; ++t)
-                    load_act<FMT>(cur[t], aq + t * K + (int64_t)s * QK, ab + t * KB + (int64_t)s * 16, c);
-                Lane part[T];
-                float d, dmin = 0.0f;
-                if constexpr (FMT == KQ_Q6_K)
-                    compute_q6<T>(raw[u], c, cur, part, d);
-                else
-                    compute_q45<FMT, T>(raw[u], c, cur, part, d, dmin);
-                d = live ? d : 0.0f;
-                dmin = live ? dmin : 0.0f;
+            for (int t = 0; t < T; ++t)
+                load_act<FMT>(cur[t], aq + t * K + (int64_t)s * QK, ab + t * KB + (int64_t)s * 16, c);
+            Lane part[T];
+            float d, dmin = 0.0f;
+            if constexpr (FMT == KQ_Q6_K)
+                compute_q6<T>(raw[u], c, cur, part, d);
+            else
+                compute_q45<FMT, T>(raw[u], c, cur, part, d, dmin);
+            d = live ? d : 0.0f;
+            dmin = live ? dmin : 0.0f;
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    // DPP sums run with every lane of the wave active
-                    const int P = quad_sum(part[t].p);
-                    const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
-                    const float d8 = d8src[t * nsb + s];
-                    if (PART && c == 0 && valid && live) {
-                        const int64_t o = ((int64_t)t * n + row) * nsb + s;
-                        Pout[o] = P;
-                        if (Mout) Mout[o] = M;
-                    }
-                    acc[t] = fmaf(d * d8, (float)P, acc[t]);
-                    if (FMT != KQ_Q6_K) acc[t] = fmaf(-(dmin * d8), (float)M, acc[t]);
+            for (int t = 0; t < T; ++t) {
+                // DPP sums run with every lane of the wave active
+                const int P = quad_sum(part[t].p);
+                const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
+                const float d8 = d8src[t * nsb + s];
+                if (PART && c == 0 && valid && live) {
+                    const int64_t o = ((int64_t)t * n + row) * nsb + s;
+                    Pout[o] = P;
+                    if (Mout) Mout[o] = M;
                 }
-            } else {
-                // codes read from L2 past batch 2 come one token at a time,
-                // so that a lane never holds more than one token's codes in
-                // flight (all T at once spill); the same sums in the same order
-#pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    Act cur[1];
-                    load_act<FMT>(cur[0], aq + t * K + (int64_t)s * QK, ab + t * KB + (int64_t)s * 16, c);
-                    Lane part[1];
-                    float d, dmin = 0.0f;
-                    if constexpr (FMT == KQ_Q6_K)
-                        compute_q6<1>(raw[u], c, cur, part, d);
-                    else
-                        compute_q45<FMT, 1>(raw[u], c, cur, part, d, dmin);
-                    d = live ? d : 0.0f;
-                    dmin = live ? dmin : 0.0f;
-                    const int P = quad_sum(part[0].p);
-                    const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[0].m);
-                    const float d8 = d8src[t * nsb + s];
-                    if (PART && c == 0 && valid && live) {
-                        const int64_t o = ((int64_t)t * n + row) * nsb + s;
-                        Pout[o] = P;
-                        if (Mout) Mout[o] = M;
-                    }
-                    acc[t] = fmaf(d * d8, (float)P, acc[t]);
-                    if (FMT != KQ_Q6_K) acc[t] = fmaf(-(dmin * d8), (float)M, acc[t]);
-                    // keep the scheduler from hoisting the next token's loads
-                    // above this one's compute
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                acc[t] = fmaf(d * d8, (float)P, acc[t]);
+                if (FMT != KQ_Q6_K) acc[t] = fmaf(-(dmin * d8), (float)M, acc[t]);
             }
         }
     }
@@ -480,39 +403,23 @@ struct GemvArgs {
     int16_t *obs;
 };
 
-// Largest Q8_K image a batch of 3-8 stages in LDS (three such workgroups
-// still fit on a CU); past it those batches read the codes from L2.
-// Measured at batch 4 on the Qwen3-4B FFN matrices: reading from L2 took
-// 11.7-16.5 us per call against 4.9-6.9 us at batch 1 with the image staged.
-constexpr size_t STAGE_MAX = (size_t)48 << 10;
 // A batch of 1-2 stages its image (plus the f32 scales, which the fused
 // form keeps beside it) while it fits one workgroup's LDS with room to spare
 // (k up to about 128k at batch 1); longer rows read the codes from L2.
-constexpr size_t STAGE_MAX12 = (size_t)144 << 10;
+constexpr size_t STAGE_MAX = (size_t)144 << 10;
 
-// How a batch's Q8_K image reaches the kernel: read from L2 inside the loop,
-// staged in LDS whole, or staged in two token halves (batches of 3-8 whose
-// whole image is too large to stage but half of it is not, with at most 16
-// steps per row, so one step per wave; W_down, k = 9728, at batch 8:
-// 17.1-21.9 us for two launches of batch 4 against 14.9-20.0 us in one).
-enum Stage { UNSTAGED, WHOLE, HALVES };
-
-static Stage stage_mode(int64_t t, int64_t k)
+static bool staged_image(int64_t t, int64_t k)
 {
-    const size_t img = (size_t)t * k * 9 / 8;
-    if (t <= 2) return img + (size_t)t * (k / QK) * sizeof(float) <= STAGE_MAX12 ? WHOLE : UNSTAGED;
-    if (img <= STAGE_MAX) return WHOLE;
-    if ((size_t)((t + 1) / 2) * k * 9 / 8 <= STAGE_MAX && k / QK <= 64) return HALVES;
-    return UNSTAGED;
+    return (size_t)t * k * 9 / 8 + (size_t)t * (k / QK) * sizeof(float) <= STAGE_MAX;
 }
 
 template <int FMT, int T, int U, int SL, bool PART>
-static void launch_one(Stage stg, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_one(bool staged, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
     // staged Q8_K image (codes + bsums), plus the scales when fused
     const size_t img = (size_t)T * a.nsb * QK * 9 / 8;
-    if (stg == WHOLE) {
-        if constexpr (T <= 2 && !PART) {
+    if (staged) {
+        if constexpr (!PART) {
             if (a.x) {
                 hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, true, true>), g, b,
                                    img + (size_t)T * a.nsb * sizeof(float), st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs,
@@ -520,57 +427,34 @@ static void launch_one(Stage stg, dim3 g, dim3 b, hipStream_t st, const GemvArgs
                 return;
             }
         }
-        // the partials of a batch of 3-8 (a test path) keep reading from L2:
-        // the same sums in the same order
-        if constexpr (T <= 2 || !PART) {
-            hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, true>), g, b, img, st, a.w, a.n, a.nsb,
-                               a.xq, a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
-            return;
-        }
-    }
-    if constexpr (T >= 3 && !PART && U == 1) {
-        if (stg == HALVES) {
-            const size_t half = (size_t)((T + 1) / 2) * a.nsb * QK * 9 / 8;
-            hipLaunchKernelGGL((gemv_kernel<FMT, T, 1, SL, false, false, true, true>), g, b, half, st, a.w, a.n,
-                               a.nsb, a.xq, a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
-            return;
-        }
+        hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, true>), g, b, img, st, a.w, a.n, a.nsb, a.xq,
+                           a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
+        return;
     }
     hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, false>), g, b, 0, st, a.w, a.n, a.nsb, a.xq, a.xs,
                        a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
 }
 
-// U, the steps whose loads a wave issues together: two for batches 1-2 with
-// the image staged (4 x 4 steps), else one (a staged batch of 3-8 runs one
-// step per wave anyway, and more would spill: the lane's weights of U steps
-// plus its tokens' codes); the partials (a test path) take one.  U changes
-// only when loads are issued, not the order of the sums.
+// U, the steps whose loads a wave issues together: two with the image
+// staged (4 x 4 steps), else one; the partials (a test path) take one.  U
+// changes only when loads are issued, not the order of the sums.
 template <int FMT, int T>
-static void launch_u(Stage stg, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_u(bool stg, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
     if (sl == 4) {
         if (part) return launch_one<FMT, T, 1, 4, true>(stg, g, b, st, a);
-        if (u == 1 || T > 2) return launch_one<FMT, T, 1, 4, false>(stg, g, b, st, a);
-        return launch_one<FMT, T, T <= 2 ? 2 : 1, 4, false>(stg, g, b, st, a);
+        if (u == 1) return launch_one<FMT, T, 1, 4, false>(stg, g, b, st, a);
+        return launch_one<FMT, T, 2, 4, false>(stg, g, b, st, a);
     }
     if (part) return launch_one<FMT, T, 1, 1, true>(stg, g, b, st, a);
     return launch_one<FMT, T, 1, 1, false>(stg, g, b, st, a);
 }
 
 template <int FMT>
-static void launch_t(int t, Stage stg, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st,
-                     const GemvArgs &a)
+static void launch_t(int t, bool stg, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
-    switch (t) {
-    case 1: return launch_u<FMT, 1>(stg, sl, u, part, g, b, st, a);
-    case 2: return launch_u<FMT, 2>(stg, sl, u, part, g, b, st, a);
-    case 3: return launch_u<FMT, 3>(stg, sl, u, part, g, b, st, a);
-    case 4: return launch_u<FMT, 4>(stg, sl, u, part, g, b, st, a);
-    case 5: return launch_u<FMT, 5>(stg, sl, u, part, g, b, st, a);
-    case 6: return launch_u<FMT, 6>(stg, sl, u, part, g, b, st, a);
-    case 7: return launch_u<FMT, 7>(stg, sl, u, part, g, b, st, a);
-    default: return launch_u<FMT, 8>(stg, sl, u, part, g, b, st, a);
-    }
+    if (t == 1) return launch_u<FMT, 1>(stg, sl, u, part, g, b, st, a);
+    return launch_u<FMT, 2>(stg, sl, u, part, g, b, st, a);
 }
 
 static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -579,20 +463,17 @@ static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const i
 {
     const int64_t nsb = k / QK;
     // the image is staged in LDS (always, for the fused kernel)
-    const Stage stg = stage_mode(t, k);
-    const bool staged = stg != UNSTAGED;
-    const bool fused = x != nullptr && t <= 2 && P == nullptr;
+    const bool staged = staged_image(t, k);
+    const bool fused = x != nullptr && P == nullptr;
     if (x != nullptr && !fused) return KQ_EINVAL;
     if (fused && !staged) return KQ_EINVAL;  // the fused kernel needs its image in LDS
     // 4 rows x 4 adjacent superblocks per wave step whenever the image is
     // staged in LDS (the fused path keeps the same shape, so its y is
-    // bit-identical to quantise-then-GEMV).  A batch that reads its codes
-    // from L2 takes 16 rows x one superblock when that gives two or more
-    // workgroups per CU, so that the wave's 16 rows share one superblock's
-    // codes.  Measured with the image staged, 4 x 4 against 16 x 1 on W_up
-    // (9728 x 2560): batch 4 8.2-9.5 us against 10.7-13.6 us.  The choice
-    // depends on t, k and n only, so the partials entry point (which reads
-    // from L2) sums in the same order.
+    // bit-identical to quantise-then-GEMV).  Codes read from L2 take 16 rows
+    // x one superblock when that gives two or more workgroups per CU, so
+    // that the wave's 16 rows share one superblock's codes.  The choice
+    // depends on t, k and n only, so the partials entry point sums in the
+    // same order.
     const int sl = staged ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
     const int64_t groups = (n + 16 / sl - 1) / (16 / sl);
     const int64_t nsteps = (nsb + sl - 1) / sl;
@@ -600,12 +481,8 @@ static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const i
     // every wave of a workgroup with the same share of steps; a row of at
     // most 4 steps gives each wave one step (measured: W_up 9728 x 2560 at
     // batch 1, 3 steps, runs 0.2-0.4 us faster with 3 waves of one step than
-    // with 2 of up to two, while W_down's 10 steps prefer two per wave).  A
-    // staged batch of 3-8 gives each wave one step up to 16 steps (W_down at
-    // batch 4: 59.7 against 62.3 us over the six matrices); like sl, this
-    // depends on t, k and n only.
-    const bool staged3 = t > 2 && staged;
-    int64_t nw = (nsteps <= 4 || (staged3 && nsteps <= 16)) ? nsteps : (4096 + groups - 1) / groups;
+    // with 2 of up to two, while W_down's 10 steps prefer two per wave).
+    int64_t nw = nsteps <= 4 ? nsteps : (4096 + groups - 1) / groups;
     nw = nw < 1 ? 1 : (nw > 16 ? 16 : nw);
     nw = nw > nsteps ? nsteps : nw;
     const int64_t per_wave = (nsteps + nw - 1) / nw;
@@ -622,47 +499,37 @@ static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const i
     // grouping.
     int64_t rgs = fused ? 16 / kw : 1;
     rgs = rgs > groups ? groups : rgs;
-    const int umax = staged && t <= 2 ? 2 : 1;
+    const int umax = staged ? 2 : 1;
     const int u = per_wave >= umax ? umax : (int)per_wave;
     GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave, (int)kw, x, oq, os, obs};
     const dim3 g((unsigned)((groups + rgs - 1) / rgs)), b((unsigned)(64 * kw * rgs));
     const bool part = P != nullptr;
-    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, stg, sl, u, part, g, b, st, a);
-    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, stg, sl, u, part, g, b, st, a);
-    else launch_t<KQ_Q6_K>((int)t, stg, sl, u, part, g, b, st, a);
+    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, staged, sl, u, part, g, b, st, a);
+    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, staged, sl, u, part, g, b, st, a);
+    else launch_t<KQ_Q6_K>((int)t, staged, sl, u, part, g, b, st, a);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 
 // Whether the one-kernel quantise + GEMV (launch_gemv with x) takes t x k:
 // a batch of 1-2 whose image and scales fit the LDS stage.
-bool gemv_fusable(int64_t t, int64_t k) { return t <= 2 && stage_mode(t, k) == WHOLE; }
+bool gemv_fusable(int64_t t, int64_t k) { return t <= 2 && staged_image(t, k); }
 
-// A batch of 3-8 whose Q8_K image is too large to stage whole runs in one
-// launch with the image in token halves when half of it stages and its rows
-// have at most 16 steps; otherwise as chunks of the most tokens (at least 3)
-// whose image does stage, one launch each (the weights are read once per
-// chunk, but the L2 path is slower still: W_down at batch 8 took 22-36 us
-// from L2 against two staged launches of batch 4).  The choice depends on t
-// and k only, so the partials entry point sums every token in the same
-// order.  Where no chunk of 3 stages (k above 14336), the batch reads its
-// codes from L2.
+int launch_gemv_mma(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
+                    const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st);
+
+// Batches 1-2 on the dot-product GEMV above (the fused form included);
+// batches 3-8 on the matrix cores, whose work per weight byte does not grow
+// with the batch.  The choice depends on t only, so the partials entry
+// point takes the same kernel.
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
                 const int16_t *xbs, int64_t t, float *y, int32_t *P, int32_t *M, hipStream_t st,
                 const float *x, int8_t *oq, float *os, int16_t *obs)
 {
-    int64_t tc = t;
-    while (tc > 2 && (size_t)tc * k * 9 / 8 > STAGE_MAX) --tc;
-    if (t <= 2 || tc == t || tc < 3 || stage_mode(t, k) == HALVES)
-        return launch_gemv_one(fmt, w, n, k, xq, xs, xbs, t, y, P, M, st, x, oq, os, obs);
-    const int64_t nsb = k / QK;
-    for (int64_t t0 = 0; t0 < t; t0 += tc) {
-        const int64_t tn = t - t0 < tc ? t - t0 : tc;
-        const int rc = launch_gemv_one(fmt, w, n, k, xq + t0 * k, xs + t0 * nsb, xbs + t0 * (k / 16), tn, y + t0 * n,
-                                       P ? P + t0 * n * nsb : nullptr, M ? M + t0 * n * nsb : nullptr, st, nullptr,
-                                       nullptr, nullptr, nullptr);
-        if (rc != KQ_OK) return rc;
+    if (t >= 3) {
+        if (x != nullptr) return KQ_EINVAL;  // the fused form is batches 1-2
+        return launch_gemv_mma(fmt, w, n, k, xq, xs, xbs, t, y, P, M, st);
     }
-    return KQ_OK;
+    return launch_gemv_one(fmt, w, n, k, xq, xs, xbs, t, y, P, M, st, x, oq, os, obs);
 }
 
 }  // namespace kq

@@ -287,10 +287,9 @@ def sample_rows(n):
 @pytest.mark.parametrize("n,k", [(9728, 2560), (2560, 9728)])
 @pytest.mark.parametrize("t", [1, 4, 6, 7, 8])
 def test_gemv_full_size_sampled(fmt, n, k, t):
-    # batch 4 stages the Q8_K image in LDS at both shapes; batches 6-8 stage
-    # it on W_up and run W_down (a 66-88 KB image) as staged launches of 4
-    # and 2-4 tokens, the partials entry point included, in the same sum
-    # order
+    # batch 1 on the dot-product kernel with its image staged in LDS;
+    # batches 4-8 on the matrix-core kernel at both shapes (one launch, the
+    # partials entry point in the same sum order)
     c = Case(fmt, n, k, t, seed=3)
     y, P, M = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
     check(c, y, P, M, rows=sample_rows(n))
@@ -430,8 +429,13 @@ def test_gemv_rows_past_the_lds_stage(fmt):
     # a batch of 1-2 stages its Q8_K image and scales in LDS up to 147456
     # bytes (k = 129024 at t = 1, 64512 at t = 2); longer rows read their
     # codes from L2, and kq_gemv_f32 then runs quantiser + GEMV, which needs
-    # the image buffers
+    # the image buffers.  Batches 3-8 (the matrix-core kernel) stage one
+    # superblock per wave, so no row length moves them off their path.
     n = 24
+    c = Case(fmt, n, 129280, 7, seed=94)
+    y, P, M = ops.matmul_partials("gemv", fmt, c.planes, n, 129280, c.q8)
+    check(c, y, P, M)
+    assert torch.equal(ops.gemv(fmt, c.planes, n, 129280, c.q8), y)
     for t, k, fits in ((1, 129024, True), (1, 129280, False), (2, 64768, False)):
         c = Case(fmt, n, k, t, seed=95 + t)
         y, P, M = ops.matmul_partials("gemv", fmt, c.planes, n, k, c.q8)
