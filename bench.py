@@ -444,7 +444,8 @@ def bench_batch(mats, copies, reps, stream, capture, ev, batches=(4, 8)):
         ach = tb / (tus * 1e-6) / 1e9
         res[f"t{t}"] = {"per_matrix": per,
                         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                     "frac": ach / HBM_PEAK_GBPS, "kernel": f"kq::gemv_kernel (kq_gemv, batch {t})",
+                                     "frac": ach / HBM_PEAK_GBPS,
+                                     "kernel": f"kq::gemv_mma_kernel (kq_gemv, batch {t}, matrix cores)",
                                      "avg_launch_us": tus / len(mats)}}
     return res
 
