@@ -83,26 +83,29 @@ BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 # profiles/kq_gemm_hbm_traffic_qwen3_4b_ffn_pp512.md; the GEMM figure is one
 # kq_gemm call, split-sum pass included).  Each holds only for the sources
 # it was measured on; with any other sources the roofline reports null.
-GEMV_F32_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f9a8f3e76bbef2ca",
-                    "bytes_per_launch": 17609692}
-GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f9a8f3e76bbef2ca",
-                "bytes_per_launch": 17415559}
+GEMV_F32_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "77fafbcadaf67c36",
+                    "bytes_per_launch": 17612251}
+GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "77fafbcadaf67c36",
+                "bytes_per_launch": 17416582}
+# the matrix-core GEMV at batch 8 (the gemv_batch leg's t8)
+GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "fb616db77ee1a461",
+                 "bytes_per_launch": 17898619}
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
                 "bytes_per_launch": 74525348}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "81cae00ede1dceca", "bytes_per_launch": 35192565}
+               "src_sha256_16": "60c317f68877164f", "bytes_per_launch": 35192587}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "5c67f30eb0f16515", "bytes_per_launch": 229721395}
+               "src_sha256_16": "9dd5cb976df19a66", "bytes_per_launch": 229725521}
 
 
 # Mean per-dispatch duration of the same kernels in the committed rocprofv3
 # kernel trace of a full bench run (profiles/kq_gemv_gemm_qwen3_4b_ffn_trace.md,
 # timed-region window), so the line carries the roofline fraction from both
 # timers; tied to the sources like the traffic records.
-GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f9a8f3e76bbef2ca", "avg_us": 7.51}
-GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f9a8f3e76bbef2ca", "avg_us": 6.48}
+GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "77fafbcadaf67c36", "avg_us": 7.40}
+GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "77fafbcadaf67c36", "avg_us": 6.35}
 GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
-              "avg_us": 50.95}
+              "avg_us": 49.96}
 
 
 def trace_us(rec):
@@ -445,6 +448,8 @@ def bench_batch(mats, copies, reps, stream, capture, ev, batches=(4, 8)):
         res[f"t{t}"] = {"per_matrix": per,
                         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                      "frac": ach / HBM_PEAK_GBPS,
+                                     "traffic": measured_traffic(GEMV8_TRAFFIC) if t == 8 else None,
+                                     "algorithmic_bytes_per_launch": tb / len(mats),
                                      "kernel": f"kq::gemv_mma_kernel (kq_gemv, batch {t}, matrix cores)",
                                      "avg_launch_us": tus / len(mats)}}
     return res
