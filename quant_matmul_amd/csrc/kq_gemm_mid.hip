@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
 constexpr int MID_STRIDE = 272;
 
 template <int FMT, bool GROUPED, bool PART, int TT>
-__global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
+__global__ __launch_bounds__(256, GROUPED && FMT == KQ_Q4_K ? 3 : 2) void gemm_mid_lds_kernel(
     const uint8_t *__restrict__ w, int64_t w_stride, const int32_t *__restrict__ tile_expert, int experts, int64_t n,
     int nsb, const int8_t *__restrict__ xq, const float *__restrict__ xs, const _Float16 *__restrict__ xbs,
     int64_t mtok, float *__restrict__ y, int32_t *__restrict__ Pout, int32_t *__restrict__ Mout, int mtiles, int S)
@@ -273,11 +273,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
     // TT token tiles x RW row blocks of 32 per workgroup: the panel of PR
     // rows serves 32*TT tokens
     constexpr int RW = 4 / TT, PR = 32 * RW;
-    __shared__ __align__(16) int8_t qp[2][PR * MID_STRIDE];
-    __shared__ __align__(16) uint32_t scw[2][PR][2];  // 8 sub-scales per row, as bytes
-    __shared__ __align__(16) uint32_t mnw[2][PR][2];  // 8 mins per row, as bytes
-    __shared__ float dd[2][PR], dmm[2][PR];
-    __shared__ __align__(16) float d8s[2][32 * TT];
+    // The panel and its scales, double-buffered (one barrier per superblock)
+    // -- except in the grouped Q4_K form, which keeps one buffer and takes a
+    // second barrier so that three workgroups fit a CU instead of two (the
+    // two staging buffers are the workgroup's whole 76 KB footprint; the
+    // KHR tile page's opening change list makes the same trade).  Q5_K would
+    // need more than the 168 VGPRs that three workgroups leave.
+    constexpr int NB = GROUPED && FMT == KQ_Q4_K ? 1 : 2;
+    __shared__ __align__(16) int8_t qp[NB][PR * MID_STRIDE];
+    __shared__ __align__(16) uint32_t scw[NB][PR][2];  // 8 sub-scales per row, as bytes
+    __shared__ __align__(16) uint32_t mnw[NB][PR][2];  // 8 mins per row, as bytes
+    __shared__ float dd[NB][PR], dmm[NB][PR];
+    __shared__ __align__(16) float d8s[NB][32 * TT];
 
     const int item = item_of_mid(blockIdx.x, gridDim.x);
     const int tile = item / S, split = item - tile * S;
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
     const int64_t row = n0 + rl;
     f32x16 accf = f32x16{};
     for (int s = s0; s < s1; ++s) {
-        const int b = (s - s0) & 1;
+        const int b = NB == 1 ? 0 : (s - s0) & 1;
         const int sn = s + 1 < s1 ? s + 1 : s1 - 1, sn2 = s + 2 < s1 ? s + 2 : s1 - 1;
         const uint2 scv = *reinterpret_cast<const uint2 *>(scw[b][rl]);
         i32x16 P = i32x16{};
@@ -456,8 +463,10 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_lds_kernel(
             }
         }
         // superblock s+1 into the other buffer (its last readers passed the
-        // previous barrier), then fetch s+2
-        stage(b ^ 1);
+        // previous barrier; with one buffer, once every wave is done with
+        // it), then fetch s+2
+        if constexpr (NB == 1) __syncthreads();
+        stage(NB == 1 ? 0 : b ^ 1);
         fetch(sn2);
         d8v = xs_row[sn2];
         __syncthreads();
@@ -504,23 +513,22 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
     // token tiles pair up, on 64-row panels (Q4_K/Q5_K) or within each wave
     // (Q6_K), when their count is even or five (129-160 tokens: three pairs,
     // the last one's second tile empty, beat five single tiles)
-    const bool pair = !GROUPED && (mtiles % 2 == 0 || mtiles == 5);
+    // The Q6_K partials (a test path) run unpaired: the paired register
+    // form with the partials stores spills.  Each output's fold runs over
+    // the same superblocks in the same order either way, so y is the same.
+    const bool pair = !GROUPED && (mtiles % 2 == 0 || mtiles == 5) && !(FMT == KQ_Q6_K && part);
     const int64_t ntiles = pair && FMT != KQ_Q6_K ? (n + 63) / 64 : (n + 127) / 128;
     const dim3 g((unsigned)(ntiles * (pair ? (mtiles + 1) / 2 : mtiles) * S)), b(256);
     if constexpr (FMT == KQ_Q6_K) {
         if constexpr (!GROUPED) {
             if (pair) {
-                if (part)
-                    hipLaunchKernelGGL((gemm_mid_kernel<FMT, false, true, 2>), g, b, 0, st, w, w_stride, tile_expert,
-                                       experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
-                else
-                    hipLaunchKernelGGL((gemm_mid_kernel<FMT, false, false, 2>), g, b, 0, st, w, w_stride,
-                                       tile_expert, experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
+                hipLaunchKernelGGL((gemm_mid_kernel<FMT, false, false, 2>), g, b, 0, st, w, w_stride, tile_expert,
+                                   experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
                 return;
             }
         }
         if (part)
-            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, true, 1>), g, b, 0, st, w, w_stride, tile_expert, experts,
+            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, !GROUPED, 1>), g, b, 0, st, w, w_stride, tile_expert, experts,
                                n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
         else
             hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, false, 1>), g, b, 0, st, w, w_stride, tile_expert,
@@ -538,7 +546,7 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
             }
         }
         if (part)
-            hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, true, 1>), g, b, 0, st, w, w_stride, tile_expert,
+            hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, !GROUPED, 1>), g, b, 0, st, w, w_stride, tile_expert,
                                experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
         else
             hipLaunchKernelGGL((gemm_mid_lds_kernel<FMT, GROUPED, false, 1>), g, b, 0, st, w, w_stride, tile_expert,
