@@ -19,8 +19,11 @@
 //                 M = sum_g m_{g/2} * bsum_g  on v_mfma_f32_16x16x16_f16
 //                     (exact: |bsum| <= 2032 and m <= 63 are f16 integers,
 //                     |M| < 2^24);
-//   Q6_K:         16-wide sub-blocks, so each 32-weight chunk runs twice with
-//                 half of its quants masked; P = sum_b sc_b * D_b - 32 * B,
+//   Q6_K:         16-wide sub-blocks.  At most 8 tokens fill half the 16
+//                 token slots, so slot i < 8 carries token i over a chunk's
+//                 first 16 weights and slot 8 + i the same token over the
+//                 last 16 (the rest of each A row zero): one MFMA per chunk
+//                 gives both sub-blocks' dots.  P = sum_b sc_b * D_b - 32 * B,
 //                 B = sum_b sc_b * bsum_b on the f16 matrix core (|B| < 2^23).
 //
 // Operand layouts (checked on the device): 16x16x32 i8 -- A[i][k]: lane l
