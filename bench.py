@@ -88,8 +88,8 @@ GEMV_F32_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "7
 GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "77fafbcadaf67c36",
                 "bytes_per_launch": 17416582}
 # the matrix-core GEMV at batch 8 (the gemv_batch leg's t8)
-GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "fb616db77ee1a461",
-                 "bytes_per_launch": 17898619}
+GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "f324a75e3f91e773",
+                 "bytes_per_launch": 17898683}
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
                 "bytes_per_launch": 74525348}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
