@@ -302,7 +302,11 @@ __global__ __launch_bounds__(256, GROUPED && FMT == KQ_Q4_K ? 3 : 2) void gemm_m
         mg = tile - nt * mgroups;
     }
     const int s0 = (int)((int64_t)nsb * split / S), s1 = (int)((int64_t)nsb * (split + 1) / S);
-    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+    // the wave index read as uniform: the token tile, and so the tile
+    // image's buffer ranges below, depend on it, and a range the compiler
+    // takes for per-lane values becomes a loop over lanes at every load
+    const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 31,
+              lh = lane >> 5;
     // wave wv: row block wv % RW, token tile wv / RW of the group (a token
     // tile past the last one still stages and meets the barriers, its codes
     // read as zero and its outputs unstored)
@@ -338,6 +342,24 @@ __global__ __launch_bounds__(256, GROUPED && FMT == KQ_Q4_K ? 3 : 2) void gemm_m
                 rqh[j] = *reinterpret_cast<const uint4 *>(wb + pl.off[1] + (qrow[j] + s) * 32 + 16 * (chunk & 1));
         }
         rh = *reinterpret_cast<const uint4 *>(wb + pl.off[0] + (hrow + s) * 16);
+    };
+    // an empty asm that reads and rewrites the fetched registers: code that
+    // uses them cannot be scheduled above it
+    auto hold = [](uint4(&q)[RW], uint4(&qh)[RW], uint4 &h) {
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            i32x4 t = __builtin_bit_cast(i32x4, q[j]);
+            asm volatile("" : "+v"(t));
+            q[j] = __builtin_bit_cast(uint4, t);
+            if constexpr (FMT == KQ_Q5_K) {
+                i32x4 u = __builtin_bit_cast(i32x4, qh[j]);
+                asm volatile("" : "+v"(u));
+                qh[j] = __builtin_bit_cast(uint4, u);
+            }
+        }
+        i32x4 t = __builtin_bit_cast(i32x4, h);
+        asm volatile("" : "+v"(t));
+        h = __builtin_bit_cast(uint4, t);
     };
     const int64_t td = mg0 + (tid & (32 * TT - 1));  // token whose d8 this thread stages
     const float *xs_row = xs + (td < mtok ? td : mtok - 1) * nsb;
@@ -466,6 +488,11 @@ __global__ __launch_bounds__(256, GROUPED && FMT == KQ_Q4_K ? 3 : 2) void gemm_m
         // previous barrier; with one buffer, once every wave is done with
         // it), then fetch s+2
         if constexpr (NB == 1) __syncthreads();
+        // the fetched bytes become usable only here: left to itself the
+        // scheduler starts their expand among the K steps above, and the
+        // wait for that fetch (issued just before the last barrier, an HBM
+        // round trip) then stalls the loop's first K step
+        hold(rq, rqh, rh);
         stage(NB == 1 ? 0 : b ^ 1);
         fetch(sn2);
         d8v = xs_row[sn2];
@@ -512,11 +539,13 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
     const int64_t mtiles = (m + 31) / 32;
     // token tiles pair up, on 64-row panels (Q4_K/Q5_K) or within each wave
     // (Q6_K), when their count is even or five (129-160 tokens: three pairs,
-    // the last one's second tile empty, beat five single tiles)
+    // the last one's second tile empty, beat five single tiles -- except for
+    // Q6_K split along k, whose half-empty last pair costs more than it saves)
     // The Q6_K partials (a test path) run unpaired: the paired register
     // form with the partials stores spills.  Each output's fold runs over
     // the same superblocks in the same order either way, so y is the same.
-    const bool pair = !GROUPED && (mtiles % 2 == 0 || mtiles == 5) && !(FMT == KQ_Q6_K && part);
+    const bool pair = !GROUPED && (mtiles % 2 == 0 || (mtiles == 5 && (FMT != KQ_Q6_K || S == 1))) &&
+                      !(FMT == KQ_Q6_K && part);
     const int64_t ntiles = pair && FMT != KQ_Q6_K ? (n + 63) / 64 : (n + 127) / 128;
     const dim3 g((unsigned)(ntiles * (pair ? (mtiles + 1) / 2 : mtiles) * S)), b(256);
     if constexpr (FMT == KQ_Q6_K) {
