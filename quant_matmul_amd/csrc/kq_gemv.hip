@@ -164,8 +164,9 @@ __device__ inline float dpp_f(float v)
 // step covers SL adjacent superblocks of each of its group's 16/SL rows
 // (quad q = sig + SL*rho of the wave: superblock slot sig, row rho), so
 // small-n matrices still spread over many waves; the kw waves of a row
-// group take contiguous runs of `per_wave` steps, U steps at a time with
-// every weight load of the U issued before the first is consumed.  The SL
+// group take contiguous runs of `per_wave` steps, one step's weight loads
+// in flight at a time (two steps' loads per wave measured 2-4% slower on
+// the 14-73 MB matrices, three or five slower still).  The SL
 // slot sums of a row meet by DPP mirrors, the kw waves' sums in LDS.  The
 // activation image is staged (or, fused, quantised) once per workgroup, so
 // a workgroup of several row groups pays for it once.
@@ -174,7 +175,7 @@ __device__ inline float dpp_f(float v)
 // into its LDS stage (the same per-chunk arithmetic as kq_quantize_q8k, so
 // the image is bit-identical) instead of reading a Q8_K image; workgroup 0
 // also writes that image out when oq is non-null.
-template <int FMT, int T, int U, int SL, bool PART, bool FUSE, bool STG>
+template <int FMT, int T, int SL, bool PART, bool FUSE, bool STG>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                     const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                     const int16_t *__restrict__ xbs, float *__restrict__ y,
@@ -265,9 +266,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
 
     // unconditional, so the count of loads in flight is static and the
     // staging write below waits only for the staging loads
-    Raw<FMT> raw[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_raw(raw[u], w, pl, rbase + sb_at(j_begin + u), c);
+    Raw<FMT> raw;
+    load_raw(raw, w, pl, rbase + sb_at(j_begin), c);
 
     const int8_t *aq = xq;
     const int16_t *ab = xbs;
@@ -322,43 +322,35 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
         ab = reinterpret_cast<const int16_t *>(stage + T * K);
     }
 
-    for (int j0 = j_begin; j0 < j_end; j0 += U) {
-        if (j0 != j_begin) {
+    for (int j = j_begin; j < j_end; ++j) {
+        if (j != j_begin) load_raw(raw, w, pl, rbase + sb_at(j), c);
+        const int s = sb_at(j);
+        const bool live = j * SL + sig < nsb;  // slot holds a real superblock
+        Act cur[T];
 #pragma unroll
-            for (int u = 0; u < U; ++u) load_raw(raw[u], w, pl, rbase + sb_at(j0 + u), c);
-        }
+        for (int t = 0; t < T; ++t)
+            load_act<FMT>(cur[t], aq + t * K + (int64_t)s * QK, ab + t * KB + (int64_t)s * 16, c);
+        Lane part[T];
+        float d, dmin = 0.0f;
+        if constexpr (FMT == KQ_Q6_K)
+            compute_q6<T>(raw, c, cur, part, d);
+        else
+            compute_q45<FMT, T>(raw, c, cur, part, d, dmin);
+        d = live ? d : 0.0f;
+        dmin = live ? dmin : 0.0f;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = j0 + u;
-            if (j >= j_end) break;
-            const int s = sb_at(j);
-            const bool live = j * SL + sig < nsb;  // slot holds a real superblock
-            Act cur[T];
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-                load_act<FMT>(cur[t], aq + t * K + (int64_t)s * QK, ab + t * KB + (int64_t)s * 16, c);
-            Lane part[T];
-            float d, dmin = 0.0f;
-            if constexpr (FMT == KQ_Q6_K)
-                compute_q6<T>(raw[u], c, cur, part, d);
-            else
-                compute_q45<FMT, T>(raw[u], c, cur, part, d, dmin);
-            d = live ? d : 0.0f;
-            dmin = live ? dmin : 0.0f;
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                // DPP sums run with every lane of the wave active
-                const int P = quad_sum(part[t].p);
-                const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
-                const float d8 = d8src[t * nsb + s];
-                if (PART && c == 0 && valid && live) {
-                    const int64_t o = ((int64_t)t * n + row) * nsb + s;
-                    Pout[o] = P;
-                    if (Mout) Mout[o] = M;
-                }
-                acc[t] = fmaf(d * d8, (float)P, acc[t]);
-                if (FMT != KQ_Q6_K) acc[t] = fmaf(-(dmin * d8), (float)M, acc[t]);
+        for (int t = 0; t < T; ++t) {
+            // DPP sums run with every lane of the wave active
+            const int P = quad_sum(part[t].p);
+            const int M = FMT == KQ_Q6_K ? 0 : quad_sum(part[t].m);
+            const float d8 = d8src[t * nsb + s];
+            if (PART && c == 0 && valid && live) {
+                const int64_t o = ((int64_t)t * n + row) * nsb + s;
+                Pout[o] = P;
+                if (Mout) Mout[o] = M;
             }
+            acc[t] = fmaf(d * d8, (float)P, acc[t]);
+            if (FMT != KQ_Q6_K) acc[t] = fmaf(-(dmin * d8), (float)M, acc[t]);
         }
     }
 
@@ -413,7 +405,7 @@ static bool staged_image(int64_t t, int64_t k)
     return (size_t)t * k * 9 / 8 + (size_t)t * (k / QK) * sizeof(float) <= STAGE_MAX;
 }
 
-template <int FMT, int T, int U, int SL, bool PART>
+template <int FMT, int T, int SL, bool PART>
 static void launch_one(bool staged, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
     // staged Q8_K image (codes + bsums), plus the scales when fused
@@ -421,40 +413,36 @@ static void launch_one(bool staged, dim3 g, dim3 b, hipStream_t st, const GemvAr
     if (staged) {
         if constexpr (!PART) {
             if (a.x) {
-                hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, false, true, true>), g, b,
+                hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, false, true, true>), g, b,
                                    img + (size_t)T * a.nsb * sizeof(float), st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs,
                                    a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
                 return;
             }
         }
-        hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, true>), g, b, img, st, a.w, a.n, a.nsb, a.xq,
+        hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, PART, false, true>), g, b, img, st, a.w, a.n, a.nsb, a.xq,
                            a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
         return;
     }
-    hipLaunchKernelGGL((gemv_kernel<FMT, T, U, SL, PART, false, false>), g, b, 0, st, a.w, a.n, a.nsb, a.xq, a.xs,
+    hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, PART, false, false>), g, b, 0, st, a.w, a.n, a.nsb, a.xq, a.xs,
                        a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
 }
 
-// U, the steps whose loads a wave issues together: two with the image
-// staged (4 x 4 steps), else one; the partials (a test path) take one.  U
-// changes only when loads are issued, not the order of the sums.
 template <int FMT, int T>
-static void launch_u(bool stg, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_sl(bool stg, int sl, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
     if (sl == 4) {
-        if (part) return launch_one<FMT, T, 1, 4, true>(stg, g, b, st, a);
-        if (u == 1) return launch_one<FMT, T, 1, 4, false>(stg, g, b, st, a);
-        return launch_one<FMT, T, 2, 4, false>(stg, g, b, st, a);
+        if (part) return launch_one<FMT, T, 4, true>(stg, g, b, st, a);
+        return launch_one<FMT, T, 4, false>(stg, g, b, st, a);
     }
-    if (part) return launch_one<FMT, T, 1, 1, true>(stg, g, b, st, a);
-    return launch_one<FMT, T, 1, 1, false>(stg, g, b, st, a);
+    if (part) return launch_one<FMT, T, 1, true>(stg, g, b, st, a);
+    return launch_one<FMT, T, 1, false>(stg, g, b, st, a);
 }
 
 template <int FMT>
-static void launch_t(int t, bool stg, int sl, int u, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
+static void launch_t(int t, bool stg, int sl, bool part, dim3 g, dim3 b, hipStream_t st, const GemvArgs &a)
 {
-    if (t == 1) return launch_u<FMT, 1>(stg, sl, u, part, g, b, st, a);
-    return launch_u<FMT, 2>(stg, sl, u, part, g, b, st, a);
+    if (t == 1) return launch_sl<FMT, 1>(stg, sl, part, g, b, st, a);
+    return launch_sl<FMT, 2>(stg, sl, part, g, b, st, a);
 }
 
 static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const int8_t *xq, const float *xs,
@@ -499,14 +487,12 @@ static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const i
     // grouping.
     int64_t rgs = fused ? 16 / kw : 1;
     rgs = rgs > groups ? groups : rgs;
-    const int umax = staged ? 2 : 1;
-    const int u = per_wave >= umax ? umax : (int)per_wave;
     GemvArgs a{(const uint8_t *)w, n, (int)nsb, xq, xs, xbs, y, P, M, (int)per_wave, (int)kw, x, oq, os, obs};
     const dim3 g((unsigned)((groups + rgs - 1) / rgs)), b((unsigned)(64 * kw * rgs));
     const bool part = P != nullptr;
-    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, staged, sl, u, part, g, b, st, a);
-    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, staged, sl, u, part, g, b, st, a);
-    else launch_t<KQ_Q6_K>((int)t, staged, sl, u, part, g, b, st, a);
+    if (fmt == KQ_Q4_K) launch_t<KQ_Q4_K>((int)t, staged, sl, part, g, b, st, a);
+    else if (fmt == KQ_Q5_K) launch_t<KQ_Q5_K>((int)t, staged, sl, part, g, b, st, a);
+    else launch_t<KQ_Q6_K>((int)t, staged, sl, part, g, b, st, a);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
 }
 
