@@ -175,7 +175,7 @@ __device__ inline float dpp_f(float v)
 // into its LDS stage (the same per-chunk arithmetic as kq_quantize_q8k, so
 // the image is bit-identical) instead of reading a Q8_K image; workgroup 0
 // also writes that image out when oq is non-null.
-template <int FMT, int T, int SL, bool PART, bool FUSE, bool STG>
+template <int FMT, int T, int SL, bool PART, bool FUSE, bool STG, int SMAX>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                     const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                     const int16_t *__restrict__ xbs, float *__restrict__ y,
@@ -221,9 +221,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint8_t *__restrict__ 
     // Memory counters retire in issue order, so the staging loads go out
     // before the weight loads: writing them to LDS then waits only for
     // themselves, and their L2 latency hides under the HBM fetch of the
-    // weights.
+    // weights.  SMAX chunks per thread go out ahead of the weights (2, or 6
+    // when the image holds more than two per thread: the long rows of the
+    // large dense matrices); the rest follow them.
     constexpr bool LDSA = STG;
-    constexpr int SMAX = 2;  // staged 16-byte chunks held per thread
     extern __shared__ __align__(16) uint8_t stage[];
     const int64_t nq = T * K / 16, nst = nq + T * K / 128;  // chunks: codes, then bsums
     auto src_chunk = [&](int64_t i) {
@@ -413,17 +414,27 @@ static void launch_one(bool staged, dim3 g, dim3 b, hipStream_t st, const GemvAr
     if (staged) {
         if constexpr (!PART) {
             if (a.x) {
-                hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, false, true, true>), g, b,
+                hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, false, true, true, 2>), g, b,
                                    img + (size_t)T * a.nsb * sizeof(float), st, a.w, a.n, a.nsb, a.xq, a.xs, a.xbs,
                                    a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
                 return;
             }
         }
-        hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, PART, false, true>), g, b, img, st, a.w, a.n, a.nsb, a.xq,
+        // image chunks (codes, then bsums) per thread of the workgroup; held
+        // six at a time before the weight loads where two would not cover
+        // them (measured on the dense 17408 x 5120 set: 0.52 -> 0.56 of
+        // 8 TB/s; on the FFN matrices six would only cost occupancy)
+        const int64_t nst = (int64_t)T * a.nsb * QK / 16 + (int64_t)T * a.nsb * QK / 128;
+        if (!PART && nst > 2 * (int64_t)b.x) {
+            hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, false, false, true, 6>), g, b, img, st, a.w, a.n, a.nsb, a.xq,
+                               a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
+            return;
+        }
+        hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, PART, false, true, 2>), g, b, img, st, a.w, a.n, a.nsb, a.xq,
                            a.xs, a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
         return;
     }
-    hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, PART, false, false>), g, b, 0, st, a.w, a.n, a.nsb, a.xq, a.xs,
+    hipLaunchKernelGGL((gemv_kernel<FMT, T, SL, PART, false, false, 2>), g, b, 0, st, a.w, a.n, a.nsb, a.xq, a.xs,
                        a.xbs, a.y, a.P, a.M, a.per_wave, a.kw, a.x, a.oq, a.os, a.obs);
 }
 
