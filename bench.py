@@ -83,10 +83,10 @@ BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
 # profiles/kq_gemm_hbm_traffic_qwen3_4b_ffn_pp512.md; the GEMM figure is one
 # kq_gemm call, split-sum pass included).  Each holds only for the sources
 # it was measured on; with any other sources the roofline reports null.
-GEMV_F32_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "9f4ef8bba96d411d",
-                    "bytes_per_launch": 17601332}
-GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "9f4ef8bba96d411d",
-                "bytes_per_launch": 17414194}
+GEMV_F32_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d",
+                    "bytes_per_launch": 17591366}
+GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d",
+                "bytes_per_launch": 17414023}
 # the matrix-core GEMV at batch 8 (the gemv_batch leg's t8)
 GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "f324a75e3f91e773",
                  "bytes_per_launch": 17898683}
@@ -102,10 +102,10 @@ MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
 # kernel trace of a full bench run (profiles/kq_gemv_gemm_qwen3_4b_ffn_trace.md,
 # timed-region window), so the line carries the roofline fraction from both
 # timers; tied to the sources like the traffic records.
-GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "9f4ef8bba96d411d", "avg_us": 7.30}
-GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "9f4ef8bba96d411d", "avg_us": 6.16}
+GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.88}
+GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.13}
 GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
-              "avg_us": 49.20}
+              "avg_us": 50.75}
 
 
 def trace_us(rec):

@@ -145,8 +145,12 @@ int kq_gemv(int fmt, const void *w_planes, int64_t n, int64_t k, const int8_t *x
  * groups as 16 waves hold, so few of them repeat it); xq/xs/xbs may then
  * be NULL (all three), or receive the Q8_K image.  Past that size, and for
  * t > 2, the image buffers are required (KQ_EINVAL without them) and the
- * call runs kq_quantize_q8k then kq_gemv.  y is bit-identical to
- * kq_quantize_q8k then kq_gemv in every case.
+ * call runs kq_quantize_q8k then kq_gemv.  The image and every
+ * superblock's fold are those of kq_quantize_q8k then kq_gemv, and so is y,
+ * bit for bit, except in the one-kernel form on rows of at most 16
+ * superblocks (k <= 4096), whose steps cover 16 rows x one superblock: there
+ * each row sums its superblock folds in another order, and y matches
+ * quantise-then-GEMV within float rounding.
  * x must be 16-byte aligned and finite. */
 int kq_gemv_f32(int fmt, const void *w_planes, int64_t n, int64_t k, const float *x, int64_t t,
                 float *y, int8_t *xq, float *xs, int16_t *xbs, void *stream);

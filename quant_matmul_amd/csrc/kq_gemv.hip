@@ -401,6 +401,9 @@ struct GemvArgs {
 // (k up to about 128k at batch 1); longer rows read the codes from L2.
 constexpr size_t STAGE_MAX = (size_t)144 << 10;
 
+// rows of at most this many superblocks take 16-row steps in the fused GEMV
+constexpr int64_t FUSED_SL1_NSB = 16;
+
 static bool staged_image(int64_t t, int64_t k)
 {
     return (size_t)t * k * 9 / 8 + (size_t)t * (k / QK) * sizeof(float) <= STAGE_MAX;
@@ -467,13 +470,18 @@ static int launch_gemv_one(int fmt, const void *w, int64_t n, int64_t k, const i
     if (x != nullptr && !fused) return KQ_EINVAL;
     if (fused && !staged) return KQ_EINVAL;  // the fused kernel needs its image in LDS
     // 4 rows x 4 adjacent superblocks per wave step whenever the image is
-    // staged in LDS (the fused path keeps the same shape, so its y is
-    // bit-identical to quantise-then-GEMV).  Codes read from L2 take 16 rows
-    // x one superblock when that gives two or more workgroups per CU, so
-    // that the wave's 16 rows share one superblock's codes.  The choice
-    // depends on t, k and n only, so the partials entry point sums in the
-    // same order.
-    const int sl = staged ? 4 : ((n + 15) / 16 >= 512 ? 1 : 4);
+    // staged in LDS, except in the fused kernel on rows of at most
+    // FUSED_SL1_NSB superblocks, which takes 16 rows x one superblock (fewer
+    // workgroups, so fewer repeats of the quantisation; measured on the
+    // Qwen3-4B W_up matrices at batch 1: 6.18 / 6.95 / 7.04 -> 4.79 / 6.23 /
+    // 6.44 us, while the plain GEMV and the longer W_down rows keep 4 x 4).
+    // There the fused y sums each row's superblock folds in another order
+    // than quantise-then-GEMV, so it matches that within rounding, not bit
+    // for bit.  Codes read from L2 take 16 rows x one superblock when that
+    // gives two or more workgroups per CU, so that the wave's 16 rows share
+    // one superblock's codes.  The choice depends on t, k and n only, so the
+    // partials entry point sums in the same order as kq_gemv.
+    const int sl = staged ? (fused && nsb <= FUSED_SL1_NSB ? 1 : 4) : ((n + 15) / 16 >= 512 ? 1 : 4);
     const int64_t groups = (n + 16 / sl - 1) / (16 / sl);
     const int64_t nsteps = (nsb + sl - 1) / sl;
     // about 16 waves per CU in flight, at most 16 waves per workgroup, and

@@ -31,6 +31,13 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
+def fused_same_bits(t, k):
+    """Whether kq_gemv_f32's y equals quantise-then-kq_gemv's bit for bit: the
+    one-kernel form (t <= 2) takes 16-row steps on rows of at most 16
+    superblocks and then sums each row's superblock folds in another order."""
+    return t > 2 or k // 256 > 16
+
+
 class Case:
     """Seeded weights and activations, the oracle's view and the device's."""
 
@@ -146,7 +153,12 @@ def _every_quantiser_matches_oracle(x, seed):
         assert np.array_equal(host(fbs), rbs)
         if t <= 2:  # the one-kernel form quantises inside every workgroup
             y1 = ops.gemv_f32("q4_k", planes, n, k, xd)
-            assert torch.equal(y1, ops.gemv("q4_k", planes, n, k, (xq, xs, xbs)))
+            y2 = ops.gemv("q4_k", planes, n, k, (xq, xs, xbs))
+            if fused_same_bits(t, k):
+                assert torch.equal(y1, y2)
+            else:
+                d = np.abs(host(y1).astype(np.float64) - host(y2).astype(np.float64))
+                assert np.all(d <= TOL * np.abs(host(y2)).max() + 1e-30)
 
 
 @pytest.mark.parametrize("t,k", [(1, 2560), (2, 1024), (5, 1536), (40, 768), (300, 2560)])
@@ -223,14 +235,20 @@ def test_gemv_f32_fused_matches_two_step(fmt, t, n, k):
     assert np.array_equal(host(xq), rq)
     assert np.array_equal(host(xs).view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(host(xbs), rbs)
-    # and the same y as quantise-then-GEMV, bit for bit
+    # and the same y as quantise-then-GEMV: bit for bit, except that the
+    # one-kernel form on rows of at most 16 superblocks sums a row's
+    # superblock folds in another order (within rounding of each other)
     y2 = ops.gemv(fmt, c.planes, n, k, c.q8)
-    assert torch.equal(y, y2)
+    rows = sample_rows(n) if n > 512 else None
+    y_o, _, _, R = c.oracle_rows(rows)
+    if fused_same_bits(t, k):
+        assert torch.equal(y, y2)
+    else:
+        d = np.abs(host(y).astype(np.float64) - host(y2).astype(np.float64))
+        assert np.all(d <= TOL * np.abs(host(y2)).max() + 1e-30)
     if t <= 2:  # the image is optional for the one-kernel path
         y3 = ops.gemv_f32(fmt, c.planes, n, k, xd)
         assert torch.equal(y, y3)
-    rows = sample_rows(n) if n > 512 else None
-    y_o, _, _, R = c.oracle_rows(rows)
     yh = host(y) if rows is None else host(y)[:, rows]
     assert np.all(np.abs(yh.astype(np.float64) - y_o) <= TOL * R)
 
