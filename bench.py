@@ -93,9 +93,9 @@ GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
                 "bytes_per_launch": 74525348}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "13bcd9635b495ae5", "bytes_per_launch": 35175793}
+               "src_sha256_16": "c011b03e57b5c874", "bytes_per_launch": 24177035}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "c3eaf62318337b7b", "bytes_per_launch": 232352439}
+               "src_sha256_16": "52baee8f02bad16a", "bytes_per_launch": 232277266}
 
 
 # Mean per-dispatch duration of the same kernels in the committed rocprofv3

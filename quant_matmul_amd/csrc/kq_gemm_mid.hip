@@ -33,6 +33,7 @@
 // w_planes + expert * w_stride.  The page's MoE path fills one Q8_K image
 // for the gate and up projections ("The pieces", kq v2 item).
 #include <atomic>
+#include <type_traits>
 
 #include "kq_common.h"
 #include "kq_digits.h"
@@ -100,7 +101,12 @@ __device__ inline int item_of_mid(int b, int G)
 // two digit passes (kq_digits.h), high and low digit in two accumulators.
 // With TT = 2 a wave covers two consecutive 32-token tiles, so each digit
 // it unpacks feeds four MFMAs (two tiles x two digits) instead of two.
-template <int FMT, bool GROUPED, bool PART, int TT>
+// With KP = 2 or 4 the workgroup's four waves take 4/KP row blocks of 32
+// and split their K range KP ways (part p of KP*S: superblocks
+// [nsb*p/(KP*S), nsb*(p+1)/(KP*S)), as the K split with KP*S parts), and
+// meet in LDS, added in part order, so the workgroup writes finished sums
+// (or one of S slices) instead of KP slices for the summing pass.
+template <int FMT, bool GROUPED, bool PART, int TT, int KP>
 __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
     const uint8_t *__restrict__ w, int64_t w_stride, const int32_t *__restrict__ tile_expert, int experts, int64_t n,
     int nsb, const int8_t *__restrict__ xq, const float *__restrict__ xs, const _Float16 *__restrict__ xbs,
@@ -108,7 +114,10 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
 {
     static_assert(FMT == KQ_Q6_K, "Q4_K/Q5_K use the LDS-panel form");
     static_assert(TT == 1 || (TT == 2 && !GROUPED), "two token tiles per wave only in the plain form");
+    static_assert(KP == 1 || ((KP == 2 || KP == 4) && !GROUPED && !PART), "k-parts in the plain production form only");
+    constexpr int RB = 4 / KP;  // row blocks of 32 per workgroup
     __shared__ __align__(16) float d8w[4][32 * TT];
+    __shared__ float red[KP > 1 ? (KP - 1) * RB : 1][TT][16][KP > 1 ? 64 : 1];  // the parts' sums
 
     // item = (128-row panel, 32-token tile -- or pair of tiles when TT = 2 --,
     // K split): the token tiles of a panel run on one XCD and share its L2
@@ -131,10 +140,16 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
         nt = tile / mgroups;
         mt = 2 * (tile - nt * mgroups);  // the first of the wave's two token tiles
     }
-    const int s0 = (int)((int64_t)nsb * split / S), s1 = (int)((int64_t)nsb * (split + 1) / S);
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-    const int64_t row0 = (int64_t)nt * 128 + wv * 32;
-    if (row0 >= n) return;  // whole wave: no rows of its own
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, lr = lane & 31,
+              lh = lane >> 5;
+    // wave wv: row block wv % RB, k-part wv / RB of this split
+    const int rbk = wv % RB, kq = wv / RB;
+    const int part = split * KP + kq;
+    const int s0 = (int)((int64_t)nsb * part / (KP * S)), s1 = (int)((int64_t)nsb * (part + 1) / (KP * S));
+    const int64_t row0 = (int64_t)nt * (32 * RB) + rbk * 32;
+    // whole wave with no rows of its own (with k-parts the wave still runs,
+    // clamped, to meet the workgroup's barrier)
+    if (KP == 1 && row0 >= n) return;
     const int64_t row = row0 + lr;
     const bool rvalid = row < n;
     const int64_t m0 = (int64_t)mt * 32;
@@ -239,6 +254,24 @@ __global__ __launch_bounds__(256, 2) void gemm_mid_kernel(
         raw = nxt;
     }
 
+    if constexpr (KP > 1) {
+        // the parts meet: waves 1..KP-1 leave their sums in LDS, wave 0
+        // adds them in part order
+        if (kq > 0) {
+#pragma unroll
+            for (int j = 0; j < TT; ++j)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) red[(kq - 1) * RB + rbk][j][i][lane] = accf[j][i];
+        }
+        __syncthreads();
+        if (kq > 0) return;
+#pragma unroll
+        for (int q = 1; q < KP; ++q)
+#pragma unroll
+            for (int j = 0; j < TT; ++j)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) accf[j][i] += red[(q - 1) * RB + rbk][j][i][lane];
+    }
     // K split j of S writes slice j of y (y then points at the workspace)
     if (!rvalid) return;
     float *yo = y + (int64_t)split * mtok * n;
@@ -508,13 +541,234 @@ __global__ __launch_bounds__(256, GROUPED && FMT == KQ_Q4_K ? 3 : 2) void gemm_m
     }
 }
 
+// The paired 32-token tile (Q4_K/Q5_K, two token tiles) with its K range
+// split KP ways (2 or 3) inside the workgroup: 2*KP waves, k-part q =
+// wave / 2 and token tile wave % 2, each k-part with its own 32-row panel of
+// its own superblock, staged together and double-buffered with one barrier
+// per step.  The parts meet in LDS at the end, added in part order, so the
+// workgroup writes the finished sums (or, split again across workgroups, one
+// slice of them) instead of KP slices that a second pass adds.  Part p of
+// KP*S covers superblocks [nsb*p/(KP*S), nsb*(p+1)/(KP*S)) as the K split of
+// the 32-token tile does, so its sums are those of that split with S*KP
+// parts, added in the same order.
+template <int FMT, int KP>
+__global__ __launch_bounds__(64 * 2 * KP, 2) void gemm_mid_kp_kernel(
+    const uint8_t *__restrict__ w, int64_t n, int nsb, const int8_t *__restrict__ xq, const float *__restrict__ xs,
+    const _Float16 *__restrict__ xbs, int64_t mtok, float *__restrict__ y, int mtiles, int S)
+{
+    static_assert(FMT != KQ_Q6_K, "Q6_K uses the register form");
+    static_assert(KP == 2 || KP == 3, "two or three k-parts");
+    constexpr int PR = 32;
+    __shared__ __align__(16) int8_t qp[2][KP][PR * MID_STRIDE];
+    __shared__ __align__(16) uint32_t scw[2][KP][PR][2];
+    __shared__ __align__(16) uint32_t mnw[2][KP][PR][2];
+    __shared__ float dd[2][KP][PR], dmm[2][KP][PR];
+    __shared__ __align__(16) float d8s[2][KP][64];
+
+    const int item = item_of_mid(blockIdx.x, gridDim.x);
+    const int tile = item / S, split = item - tile * S;
+    const int mgroups = (mtiles + 1) / 2;
+    const int nt = tile / mgroups, mg = tile - nt * mgroups;
+    const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 31,
+              lh = lane >> 5;
+    const int kp = wv >> 1, tt = wv & 1;  // the wave's k-part and token tile
+    const int mt = mg * 2 + tt;
+    const int64_t n0 = (int64_t)nt * PR, m0 = (int64_t)mt * 32, mg0 = (int64_t)mg * 64;
+    auto sbeg = [&](int q) { return (int)((int64_t)nsb * (split * KP + q) / (KP * S)); };
+    int its = 0;  // steps: the longest part
+#pragma unroll
+    for (int q = 0; q < KP; ++q) its = max(its, sbeg(q + 1) - sbeg(q));
+    const int s0 = sbeg(kp), s1 = sbeg(kp + 1);  // this wave's part
+    const int64_t K = (int64_t)nsb * QK;
+    const Planes pl = planes_of(FMT, n, nsb);
+
+    // staging task: part sp = tid / 128 of the panels; 16 bytes (chunk u%8)
+    // of rows u/8 and u/8 + 16 of that part's panel; u < 32 also takes row
+    // u's header, u < 64 the d8 of the group's token u
+    const int sp = tid >> 7, u = tid & 127, chunk = u & 7, rsub = u >> 3;
+    const int ps0 = sbeg(sp), ps1 = sbeg(sp + 1);
+    auto sb_of = [&](int it) { return min(ps0 + it, ps1 - 1); };  // staged superblock of step it, clamped
+    int64_t qrow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t r = n0 + 16 * j + rsub;
+        qrow[j] = (r < n ? r : n - 1) * nsb;
+    }
+    const int64_t hr = n0 + (u & (PR - 1));
+    const bool hvalid = hr < n;
+    const int64_t hrow = (hvalid ? hr : n - 1) * nsb;
+    const int64_t td = mg0 + (u & 63);  // token whose d8 this thread stages
+    const float *xs_row = xs + (td < mtok ? td : mtok - 1) * nsb;
+    uint4 rq[2], rqh[2], rh;
+    float d8v;
+    auto fetch = [&](int it) {
+        const int s = sb_of(it);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            rq[j] = *reinterpret_cast<const uint4 *>(w + pl.off[FMT == KQ_Q5_K ? 2 : 1] + (qrow[j] + s) * 128 + 16 * chunk);
+            if constexpr (FMT == KQ_Q5_K)
+                rqh[j] = *reinterpret_cast<const uint4 *>(w + pl.off[1] + (qrow[j] + s) * 32 + 16 * (chunk & 1));
+        }
+        rh = *reinterpret_cast<const uint4 *>(w + pl.off[0] + (hrow + s) * 16);
+        d8v = xs_row[s];
+    };
+    // the fetched registers pass an empty asm before the expand, so it is
+    // not scheduled among the K steps (where the wait for the fetch would
+    // stall them)
+    auto hold = [&]() {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            i32x4 t = __builtin_bit_cast(i32x4, rq[j]);
+            asm volatile("" : "+v"(t));
+            rq[j] = __builtin_bit_cast(uint4, t);
+            if constexpr (FMT == KQ_Q5_K) {
+                i32x4 v = __builtin_bit_cast(i32x4, rqh[j]);
+                asm volatile("" : "+v"(v));
+                rqh[j] = __builtin_bit_cast(uint4, v);
+            }
+        }
+        i32x4 t = __builtin_bit_cast(i32x4, rh);
+        asm volatile("" : "+v"(t), "+v"(d8v));
+        rh = __builtin_bit_cast(uint4, t);
+    };
+    // expand into buffer b of part sp's panel: quant byte 32c + b of a row
+    // holds weight 64c + b (low nibble) and 64c + 32 + b (high nibble)
+    auto stage = [&](int b) {
+        const int c = chunk >> 1, b0 = 16 * (chunk & 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t q[4] = {rq[j].x, rq[j].y, rq[j].z, rq[j].w};
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo[i] = q[i] & 0x0F0F0F0Fu;
+                hi[i] = (q[i] >> 4) & 0x0F0F0F0Fu;
+                if constexpr (FMT == KQ_Q5_K) {
+                    const uint32_t hb = i == 0 ? rqh[j].x : i == 1 ? rqh[j].y : i == 2 ? rqh[j].z : rqh[j].w;
+                    lo[i] |= ((hb >> (2 * c)) & 0x01010101u) << 4;
+                    hi[i] |= ((hb >> (2 * c + 1)) & 0x01010101u) << 4;
+                }
+            }
+            int8_t *row = qp[b][sp] + (16 * j + rsub) * MID_STRIDE + 64 * c + b0;
+            *reinterpret_cast<uint4 *>(row) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint4 *>(row + 32) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        }
+        if (u < PR) {
+            // rows past n: scales, mins and d masked to zero
+            const uint32_t vm = hvalid ? 0xFFFFFFFFu : 0u;
+            const uint32_t s0w = rh.y & vm, s1w = rh.z & vm, s2w = rh.w & vm;
+            scw[b][sp][u][0] = s0w & 0x3F3F3F3Fu;
+            scw[b][sp][u][1] = (s2w & 0x0F0F0F0Fu) | ((s0w >> 2) & 0x30303030u);
+            mnw[b][sp][u][0] = s1w & 0x3F3F3F3Fu;
+            mnw[b][sp][u][1] = ((s2w >> 4) & 0x0F0F0F0Fu) | ((s1w >> 2) & 0x30303030u);
+            dd[b][sp][u] = f16_bits_to_float(rh.x & vm & 0xFFFFu);
+            dmm[b][sp][u] = f16_bits_to_float((rh.x & vm) >> 16);
+        }
+        if (u < 64) d8s[b][sp][u] = td < mtok ? d8v : 0.0f;
+    };
+
+    // the wave's token tile of codes and f16 bsums (a tile past the image
+    // gets empty ranges: every load reads zero)
+    const int64_t mpad = (mtok + 31) & ~(int64_t)31;
+    const bool mvalid = m0 < mpad;
+    const int64_t mb = mvalid ? m0 : 0;
+    const uint64_t a_bytes = mvalid ? (uint64_t)(mpad - m0) * (uint64_t)K : 0;
+    const uint64_t b_bytes = mvalid ? (uint64_t)(mpad - m0) * (uint64_t)nsb * 32 : 0;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xq + mb * K), 0, (int)(uint32_t)(a_bytes < 0xFFFFFFFFu ? a_bytes : 0xFFFFFFFFu), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(xbs + mb * nsb * 16), 0, (int)(uint32_t)(b_bytes < 0xFFFFFFFFu ? b_bytes : 0xFFFFFFFFu),
+        0x00020000);
+    i32x4 A[8];
+    f16x8 Ab;
+    auto load_a = [&](int s, int ks) {
+        A[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, 16 * lane, (s * 8 + ks) * 1024, 0));
+    };
+    auto load_bs = [&](int s) {
+        Ab = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, 16 * lane, s * 1024, 0));
+    };
+
+    fetch(0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) load_a(s0, ks);
+    load_bs(s0);
+    stage(0);
+    fetch(1);
+    __syncthreads();
+
+    const int rl = lr;  // this lane's panel row
+    const int64_t row = n0 + rl;
+    f32x16 accf = f32x16{};
+    for (int it = 0; it < its; ++it) {
+        const int b = it & 1;
+        const bool live = s0 + it < s1;  // a shorter part idles on the longest part's last step
+        const int sw = min(s0 + it + 1, s1 - 1);  // the next step's codes (clamped)
+        const uint2 scv = *reinterpret_cast<const uint2 *>(scw[b][kp][rl]);
+        i32x16 P = i32x16{};
+        const int8_t *brow = qp[b][kp] + rl * MID_STRIDE + 16 * lh;
+        i32x4 Bc = *reinterpret_cast<const i32x4 *>(brow);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            i32x4 Bn = Bc;
+            if (ks + 1 < 8) Bn = *reinterpret_cast<const i32x4 *>(brow + 32 * (ks + 1));
+            const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks], Bc, i32x16{}, 0, 0, 0);
+            const int sc = (int)byte_of(ks < 4 ? scv.x : scv.y, ks & 3);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) P[i] = __mul24(d[i], sc) + P[i];
+            load_a(sw, ks);
+            asm volatile("" : "+v"(P), "+v"(Bn)::"memory");
+            Bc = Bn;
+        }
+        const uint32_t mw = *reinterpret_cast<const uint32_t *>(&mnw[b][kp][rl][lh]);
+        f16x8 bm;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bm[2 * j] = bm[2 * j + 1] = (_Float16)(int)byte_of(mw, j);
+        const f32x16 mf = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ab, bm, f32x16{}, 0, 0, 0);
+        load_bs(sw);
+        const float dv = dd[b][kp][rl], dm = dmm[b][kp][rl];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int tl = 8 * (i >> 2) + 4 * lh + (i & 3);
+            const float uu = fmaf(dv, (float)P[i], -(dm * mf[i]));
+            const float a = fmaf(d8s[b][kp][32 * tt + tl], uu, accf[i]);
+            accf[i] = live ? a : accf[i];
+        }
+        // step it+1 into the other buffers (their last readers passed the
+        // previous barrier), then fetch step it+2
+        hold();
+        stage(b ^ 1);
+        fetch(it + 2);
+        __syncthreads();
+    }
+
+    // the parts meet: parts 1..KP-1 leave their sums in LDS (the panel
+    // buffers, free after the last barrier), part 0 adds them in order
+    float *red = reinterpret_cast<float *>(&qp[0][0][0]);
+    if (kp > 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[(((kp - 1) * 2 + tt) * 16 + i) * 64 + lane] = accf[i];
+    }
+    __syncthreads();
+    if (kp > 0 || row >= n) return;
+#pragma unroll
+    for (int q = 1; q < KP; ++q)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) accf[i] += red[(((q - 1) * 2 + tt) * 16 + i) * 64 + lane];
+    float *yo = y + (int64_t)split * mtok * n;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t t = m0 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (t < mtok) yo[t * n + row] = accf[i];
+    }
+}
+
 void launch_sum_splits(const float *p, int S, int64_t count, float *y, hipStream_t st);
 
 namespace {
 
-int pick_splits_mid(int64_t waves, int nsb)
+int cu_count()
 {
-    // the CU count, read once (an atomic, so concurrent first calls are safe)
+    // read once (an atomic, so concurrent first calls are safe)
     static std::atomic<int> cus_once{0};
     int cus = cus_once.load(std::memory_order_relaxed);
     if (!cus) {
@@ -524,6 +778,12 @@ int pick_splits_mid(int64_t waves, int nsb)
             cus = 256;
         cus_once.store(cus, std::memory_order_relaxed);
     }
+    return cus;
+}
+
+int pick_splits_mid(int64_t waves, int nsb)
+{
+    const int cus = cu_count();
     // about 8 resident waves per CU
     int S = (int)((8 * (int64_t)cus) / waves);
     S = S < nsb / 2 ? S : nsb / 2;
@@ -551,16 +811,16 @@ void launch_mid_fmt(bool part, const uint8_t *w, int64_t w_stride, const int32_t
     if constexpr (FMT == KQ_Q6_K) {
         if constexpr (!GROUPED) {
             if (pair) {
-                hipLaunchKernelGGL((gemm_mid_kernel<FMT, false, false, 2>), g, b, 0, st, w, w_stride, tile_expert,
+                hipLaunchKernelGGL((gemm_mid_kernel<FMT, false, false, 2, 1>), g, b, 0, st, w, w_stride, tile_expert,
                                    experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
                 return;
             }
         }
         if (part)
-            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, !GROUPED, 1>), g, b, 0, st, w, w_stride, tile_expert, experts,
+            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, !GROUPED, 1, 1>), g, b, 0, st, w, w_stride, tile_expert, experts,
                                n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
         else
-            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, false, 1>), g, b, 0, st, w, w_stride, tile_expert,
+            hipLaunchKernelGGL((gemm_mid_kernel<FMT, GROUPED, false, 1, 1>), g, b, 0, st, w, w_stride, tile_expert,
                                experts, n, nsb, xq, xs, xbs, m, y, P, M, (int)mtiles, S);
     } else {
         if constexpr (!GROUPED) {
@@ -601,6 +861,9 @@ void launch_mid_any(int fmt, bool part, const uint8_t *w, int64_t w_stride, cons
 
 int64_t mid_waves(int64_t n, int64_t m) { return ((n + 31) / 32) * ((m + 31) / 32); }
 
+// four-wave k-part workgroups (KP = 2) held per CU in one round
+constexpr int KP_PER_CU = 2;
+
 }  // namespace
 
 size_t gemm_mid_workspace_bytes(int64_t n, int64_t k, int64_t m)
@@ -617,6 +880,67 @@ int launch_gemm_mid(int fmt, const void *w, int64_t n, int64_t k, const int8_t *
     const bool part = P != nullptr;
     int S = 1;
     if (!part && ws && ws_bytes >= gemm_mid_workspace_bytes(n, k, m)) S = pick_splits_mid(mid_waves(n, m), nsb);
+    // A Q4_K/Q5_K paired tile split along k runs KP of its parts inside each
+    // workgroup (gemm_mid_kp_kernel) and S/KP (rounded) across workgroups, so
+    // the summing pass adds fewer slices, or none -- while its grid runs in
+    // one round: one six-wave workgroup per CU for KP = 3 (two do not fit a
+    // CU's VGPRs: measured at 320 workgroups, W_down at 100-160 tokens,
+    // 22.4 -> 32.4 us), KP_PER_CU four-wave ones for KP = 2.
+    const int64_t mtiles = (m + 31) / 32;
+    const bool pairq = mtiles % 2 == 0 || mtiles == 5;
+    if (!part && fmt != KQ_Q6_K && pairq && S >= 2) {
+        for (int kp = 3; kp >= 2; --kp) {
+            if (S < kp) continue;
+            int Sw = (S + (kp == 3 ? 1 : 0)) / kp;  // three parts: rounded; two: floor, so S = 3 stays in one slice
+            Sw = Sw > 1 ? Sw : 1;
+            while (Sw > 1 && kp * Sw > nsb) --Sw;
+            const int64_t grid = ((n + 31) / 32) * ((mtiles + 1) / 2) * Sw;
+            if (kp * Sw > nsb || grid > (kp == 3 ? 1 : KP_PER_CU) * (int64_t)cu_count()) continue;
+            float *dst = Sw > 1 ? (float *)ws : y;
+            const dim3 g((unsigned)grid), b(64 * 2 * kp);
+            auto go = [&](auto f, auto k) {
+                hipLaunchKernelGGL((gemm_mid_kp_kernel<decltype(f)::value, decltype(k)::value>), g, b, 0, st,
+                                   (const uint8_t *)w, n, nsb, xq, xs, (const _Float16 *)xbs, m, dst, (int)mtiles, Sw);
+            };
+            using I4 = std::integral_constant<int, KQ_Q4_K>;
+            using I5 = std::integral_constant<int, KQ_Q5_K>;
+            using K2 = std::integral_constant<int, 2>;
+            using K3 = std::integral_constant<int, 3>;
+            if (fmt == KQ_Q4_K) kp == 3 ? go(I4{}, K3{}) : go(I4{}, K2{});
+            else kp == 3 ? go(I5{}, K3{}) : go(I5{}, K2{});
+            if (Sw > 1) launch_sum_splits((const float *)ws, Sw, m * n, y, st);
+            return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
+        }
+    }
+    // Q6_K split along k: the register tile's four waves take 4/KP row
+    // blocks and KP of the parts (gemm_mid_kernel, KP = 4, else 2), S/KP
+    // across workgroups, while the grid holds at most one workgroup per CU
+    // (its 241 VGPRs leave one wave per SIMD)
+    if (!part && fmt == KQ_Q6_K && S >= 2) {
+        const bool pair6 = mtiles % 2 == 0;  // as launch_mid_fmt pairs a split Q6_K tile
+        for (int kp = 4; kp >= 2; kp -= 2) {
+            if (S < kp) continue;
+            int S6 = (S + (kp == 4 ? 2 : 0)) / kp;  // four parts: rounded; two: floor
+            S6 = S6 > 1 ? S6 : 1;
+            while (S6 > 1 && kp * S6 > nsb) --S6;
+            const int64_t grid = ((n + 32 * (4 / kp) - 1) / (32 * (4 / kp))) * (pair6 ? (mtiles + 1) / 2 : mtiles) * S6;
+            if (kp * S6 > nsb || grid > cu_count()) continue;
+            float *dst = S6 > 1 ? (float *)ws : y;
+            const dim3 g((unsigned)grid), b(256);
+            auto go = [&](auto tt, auto k) {
+                hipLaunchKernelGGL((gemm_mid_kernel<KQ_Q6_K, false, false, decltype(tt)::value, decltype(k)::value>), g,
+                                   b, 0, st, (const uint8_t *)w, 0, nullptr, 0, n, nsb, xq, xs, (const _Float16 *)xbs, m,
+                                   dst, nullptr, nullptr, (int)mtiles, S6);
+            };
+            using T1 = std::integral_constant<int, 1>;
+            using T2 = std::integral_constant<int, 2>;
+            using K4 = std::integral_constant<int, 4>;
+            if (pair6) kp == 4 ? go(T2{}, K4{}) : go(T2{}, T2{});
+            else kp == 4 ? go(T1{}, K4{}) : go(T1{}, T2{});
+            if (S6 > 1) launch_sum_splits((const float *)ws, S6, m * n, y, st);
+            return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
+        }
+    }
     float *dst = S > 1 ? (float *)ws : y;
     launch_mid_any<false>(fmt, part, (const uint8_t *)w, 0, nullptr, 0, n, nsb, xq, xs, (const _Float16 *)xbs, m, dst,
                           P, M, S, st);
