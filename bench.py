@@ -93,19 +93,19 @@ GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
                 "bytes_per_launch": 74525348}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "c011b03e57b5c874", "bytes_per_launch": 24177035}
+               "src_sha256_16": "7db0e6a7ade65b98", "bytes_per_launch": 24398521}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "52baee8f02bad16a", "bytes_per_launch": 232277266}
+               "src_sha256_16": "56bf534cac7060bc", "bytes_per_launch": 232380302}
 
 
 # Mean per-dispatch duration of the same kernels in the committed rocprofv3
 # kernel trace of a full bench run (profiles/kq_gemv_gemm_qwen3_4b_ffn_trace.md,
 # timed-region window), so the line carries the roofline fraction from both
 # timers; tied to the sources like the traffic records.
-GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.88}
-GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.13}
+GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.91}
+GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.15}
 GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
-              "avg_us": 50.75}
+              "avg_us": 50.74}
 
 
 def trace_us(rec):
@@ -405,7 +405,7 @@ def bench_mid(mats, copies, reps, stream, capture, ev, tokens=MID_M):
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBPS, "traffic": measured_traffic(MID_TRAFFIC) if tokens == MID_M else None,
                          "algorithmic_bytes_per_launch": kb_total / len(mats),
-                         "kernel": "kq::gemm_mid_lds_kernel (Q4_K, Q5_K) / kq::gemm_mid_kernel (Q6_K) (kq_gemm, 32-token tile)",
+                         "kernel": "kq::gemm_mid_kp_kernel / gemm_mid_lds_kernel (Q4_K, Q5_K), kq::gemm_mid_kernel (Q6_K) (kq_gemm, 32-token tile)",
                          "avg_launch_us": kus_total / len(mats)}}
 
 

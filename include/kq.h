@@ -211,13 +211,16 @@ int kq_gemm_tile_tokens(int fmt, int64_t n, int64_t k, int64_t m);
  * through an LDS panel for Q4_K/Q5_K); m >= 193 a 256-token tile that
  * unpacks it once per 256 tokens into LDS.
  * workspace: NULL, or a 256-byte aligned device buffer of workspace_bytes >=
- * kq_gemm_tiles_workspace_bytes bytes (no initial contents needed).  With
- * it, a grid too small to fill the GPU is split along k: for the 256-token
- * tile each tile's parts write partial sums to the workspace and the last
- * part of the tile to finish adds them into y (one launch); for the 32-token
- * tile whole-output slices that a second kernel adds.  Both add in split
- * order, so results are the same from call to call (they may differ from the
- * unsplit sum in the last bits, within the fold's float tolerance).  The
+ * kq_gemm_tiles_workspace_bytes bytes (no initial contents needed; a
+ * non-NULL pointer where that size is 0).  With it, a grid too small to fill
+ * the GPU is split along k: for the 256-token tile each tile's parts write
+ * partial sums to the workspace and the last part of the tile to finish adds
+ * them into y (one launch); for the 32-token tile the waves of a workgroup
+ * take two to four parts of k and add them in LDS where the grid still runs
+ * in one round, and whole-output slices that a second kernel adds take the
+ * rest.  All add in split order, so results are the same from call to call
+ * (they may differ from the unsplit sum in the last bits, within the fold's
+ * float tolerance).  The
  * 256-token tile's parts count in through counter words at the start of the
  * workspace that every call tags as its own, so stale contents are ignored
  * and graph replays may reuse the workspace.  Calls sharing one workspace

@@ -32,6 +32,7 @@
 // names the expert of every 32-row tile; its weights are the planes at
 // w_planes + expert * w_stride.  The page's MoE path fills one Q8_K image
 // for the gate and up projections ("The pieces", kq v2 item).
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(256, GROUPED && FMT == KQ_Q4_K ? 3 : 2) void gemm_m
 }
 
 // The paired 32-token tile (Q4_K/Q5_K, two token tiles) with its K range
-// split KP ways (2 or 3) inside the workgroup: 2*KP waves, k-part q =
+// split KP ways (2 to 4) inside the workgroup: 2*KP waves, k-part q =
 // wave / 2 and token tile wave % 2, each k-part with its own 32-row panel of
 // its own superblock, staged together and double-buffered with one barrier
 // per step.  The parts meet in LDS at the end, added in part order, so the
@@ -552,12 +553,12 @@ __global__ __launch_bounds__(256, GROUPED && FMT == KQ_Q4_K ? 3 : 2) void gemm_m
 // the 32-token tile does, so its sums are those of that split with S*KP
 // parts, added in the same order.
 template <int FMT, int KP>
-__global__ __launch_bounds__(64 * 2 * KP, 2) void gemm_mid_kp_kernel(
+__global__ __launch_bounds__(64 * 2 * KP, KP >= 4 ? 1 : 2) void gemm_mid_kp_kernel(
     const uint8_t *__restrict__ w, int64_t n, int nsb, const int8_t *__restrict__ xq, const float *__restrict__ xs,
     const _Float16 *__restrict__ xbs, int64_t mtok, float *__restrict__ y, int mtiles, int S)
 {
     static_assert(FMT != KQ_Q6_K, "Q6_K uses the register form");
-    static_assert(KP == 2 || KP == 3, "two or three k-parts");
+    static_assert(KP >= 2 && KP <= 4, "two to four k-parts");
     constexpr int PR = 32;
     __shared__ __align__(16) int8_t qp[2][KP][PR * MID_STRIDE];
     __shared__ __align__(16) uint32_t scw[2][KP][PR][2];
@@ -861,8 +862,9 @@ void launch_mid_any(int fmt, bool part, const uint8_t *w, int64_t w_stride, cons
 
 int64_t mid_waves(int64_t n, int64_t m) { return ((n + 31) / 32) * ((m + 31) / 32); }
 
-// four-wave k-part workgroups (KP = 2) held per CU in one round
-constexpr int KP_PER_CU = 2;
+// four-wave k-part workgroups (KP = 2) held per CU in one round: their
+// 149-161 VGPRs leave room for three waves per SIMD
+constexpr int KP_PER_CU = 3;
 
 }  // namespace
 
@@ -878,24 +880,39 @@ int launch_gemm_mid(int fmt, const void *w, int64_t n, int64_t k, const int8_t *
 {
     const int nsb = (int)(k / QK);
     const bool part = P != nullptr;
-    int S = 1;
-    if (!part && ws && ws_bytes >= gemm_mid_workspace_bytes(n, k, m)) S = pick_splits_mid(mid_waves(n, m), nsb);
+    // a NULL or too small workspace runs the tile unsplit (bitwise the
+    // partials kernel's outputs)
+    const bool split_ok = !part && ws && ws_bytes >= gemm_mid_workspace_bytes(n, k, m);
+    const int S = split_ok ? pick_splits_mid(mid_waves(n, m), nsb) : 1;
     // A Q4_K/Q5_K paired tile split along k runs KP of its parts inside each
-    // workgroup (gemm_mid_kp_kernel) and S/KP (rounded) across workgroups, so
-    // the summing pass adds fewer slices, or none -- while its grid runs in
-    // one round: one six-wave workgroup per CU for KP = 3 (two do not fit a
-    // CU's VGPRs: measured at 320 workgroups, W_down at 100-160 tokens,
-    // 22.4 -> 32.4 us), KP_PER_CU four-wave ones for KP = 2.
+    // workgroup (gemm_mid_kp_kernel) and Sw slices across workgroups, so the
+    // summing pass adds fewer slices, or none -- while its grid runs in one
+    // round.  KP = 4 (eight waves, one workgroup per CU) takes as many
+    // slices as fill the CUs once, where that is at least two (W_down at up
+    // to 64 tokens: 240 workgroups of three slices).  KP = 3 takes S/3
+    // (rounded) slices, at most one six-wave workgroup per CU (at 320
+    // workgroups, W_down at 100-160 tokens, the CUs given two set the end:
+    // 22.4 -> 32.4 us).  KP = 2 takes S/2 slices, KP_PER_CU four-wave
+    // workgroups per CU; an unsplit tile (S = 1) runs as two parts where
+    // that grid fits (W_up at 100-128 tokens: 20.8 -> 18.8 us on Q4_K).
     const int64_t mtiles = (m + 31) / 32;
     const bool pairq = mtiles % 2 == 0 || mtiles == 5;
-    if (!part && fmt != KQ_Q6_K && pairq && S >= 2) {
-        for (int kp = 3; kp >= 2; --kp) {
-            if (S < kp) continue;
-            int Sw = (S + (kp == 3 ? 1 : 0)) / kp;  // three parts: rounded; two: floor, so S = 3 stays in one slice
-            Sw = Sw > 1 ? Sw : 1;
+    if (split_ok && fmt != KQ_Q6_K && pairq) {
+        const int64_t cells = ((n + 31) / 32) * ((mtiles + 1) / 2);
+        for (int kp = 4; kp >= 2; --kp) {
+            int Sw;
+            if (kp == 4) {
+                if (S < 4) continue;
+                Sw = (int)std::min<int64_t>(cu_count() / cells, S);
+            } else {
+                if (S < kp && !(S == 1 && kp == 2)) continue;
+                Sw = (S + (kp == 3 ? 1 : 0)) / kp;  // three parts: rounded; two: floor, so S = 3 stays in one slice
+                Sw = Sw > 1 ? Sw : 1;
+            }
             while (Sw > 1 && kp * Sw > nsb) --Sw;
-            const int64_t grid = ((n + 31) / 32) * ((mtiles + 1) / 2) * Sw;
-            if (kp * Sw > nsb || grid > (kp == 3 ? 1 : KP_PER_CU) * (int64_t)cu_count()) continue;
+            if (kp == 4 && Sw < 2) continue;
+            const int64_t grid = cells * Sw;
+            if (kp * Sw > nsb || grid > (kp == 2 ? KP_PER_CU : 1) * (int64_t)cu_count()) continue;
             float *dst = Sw > 1 ? (float *)ws : y;
             const dim3 g((unsigned)grid), b(64 * 2 * kp);
             auto go = [&](auto f, auto k) {
@@ -906,22 +923,30 @@ int launch_gemm_mid(int fmt, const void *w, int64_t n, int64_t k, const int8_t *
             using I5 = std::integral_constant<int, KQ_Q5_K>;
             using K2 = std::integral_constant<int, 2>;
             using K3 = std::integral_constant<int, 3>;
-            if (fmt == KQ_Q4_K) kp == 3 ? go(I4{}, K3{}) : go(I4{}, K2{});
-            else kp == 3 ? go(I5{}, K3{}) : go(I5{}, K2{});
+            using K4 = std::integral_constant<int, 4>;
+            if (fmt == KQ_Q4_K) kp == 4 ? go(I4{}, K4{}) : kp == 3 ? go(I4{}, K3{}) : go(I4{}, K2{});
+            else kp == 4 ? go(I5{}, K4{}) : kp == 3 ? go(I5{}, K3{}) : go(I5{}, K2{});
             if (Sw > 1) launch_sum_splits((const float *)ws, Sw, m * n, y, st);
             return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ELAUNCH;
         }
     }
     // Q6_K split along k: the register tile's four waves take 4/KP row
     // blocks and KP of the parts (gemm_mid_kernel, KP = 4, else 2), S/KP
-    // across workgroups, while the grid holds at most one workgroup per CU
-    // (its 241 VGPRs leave one wave per SIMD)
-    if (!part && fmt == KQ_Q6_K && S >= 2) {
+    // (or, for KP = 4, enough to fill the CUs) across workgroups, while the grid holds at most one workgroup per CU
+    // (its 241 VGPRs leave room for two waves per SIMD, but with more
+    // workgroups than CUs the CUs given two set the end: W_down at 100-128
+    // tokens, 25.4 -> 29.9 us)
+    if (split_ok && fmt == KQ_Q6_K && S >= 2) {
         const bool pair6 = mtiles % 2 == 0;  // as launch_mid_fmt pairs a split Q6_K tile
         for (int kp = 4; kp >= 2; kp -= 2) {
             if (S < kp) continue;
             int S6 = (S + (kp == 4 ? 2 : 0)) / kp;  // four parts: rounded; two: floor
             S6 = S6 > 1 ? S6 : 1;
+            if (kp == 4) {  // or as many slices as fill the CUs once, if more (W_down at up to 64 tokens: three)
+                const int64_t cells = ((n + 31) / 32) * (pair6 ? (mtiles + 1) / 2 : mtiles);
+                const int sf = (int)(cu_count() / cells);
+                if (sf > S6 && sf <= S) S6 = sf;
+            }
             while (S6 > 1 && kp * S6 > nsb) --S6;
             const int64_t grid = ((n + 32 * (4 / kp) - 1) / (32 * (4 / kp))) * (pair6 ? (mtiles + 1) / 2 : mtiles) * S6;
             if (kp * S6 > nsb || grid > cu_count()) continue;

@@ -127,9 +127,11 @@ def gemm(fmt, planes, n: int, k: int, q8, workspace=None, stream=None) -> torch.
 
 
 def gemm_tiles_workspace(fmt, n: int, k: int, m: int, device="cuda"):
-    """A kq_gemm_tiles workspace for this shape (None if it takes none)."""
+    """A kq_gemm_tiles workspace for this shape: at least 256 bytes, since a
+    non-NULL workspace also lets the 32-token tile split k inside its
+    workgroups where no slices are needed."""
     nb = kq_gemm_tiles_workspace_bytes(fmt, n, k, m)
-    return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+    return torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
 
 
 def gemm_tiles(fmt, planes, n: int, k: int, q8t, workspace="auto", stream=None) -> torch.Tensor:
