@@ -93,9 +93,9 @@ GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
                 "bytes_per_launch": 74525348}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "7db0e6a7ade65b98", "bytes_per_launch": 24398521}
+               "src_sha256_16": "e4829b075324a6b6", "bytes_per_launch": 24398521}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "56bf534cac7060bc", "bytes_per_launch": 232380302}
+               "src_sha256_16": "5ac5cad59ae4e73a", "bytes_per_launch": 232444087}
 
 
 # Mean per-dispatch duration of the same kernels in the committed rocprofv3

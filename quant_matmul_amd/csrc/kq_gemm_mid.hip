@@ -744,6 +744,7 @@ __global__ __launch_bounds__(64 * 2 * KP, KP >= 4 ? 1 : 2) void gemm_mid_kp_kern
 
     // the parts meet: parts 1..KP-1 leave their sums in LDS (the panel
     // buffers, free after the last barrier), part 0 adds them in order
+    static_assert(sizeof(qp) >= sizeof(float) * (KP - 1) * 2 * 16 * 64, "the parts' sums fit the panel buffers");
     float *red = reinterpret_cast<float *>(&qp[0][0][0]);
     if (kp > 0) {
 #pragma unroll
