@@ -381,13 +381,18 @@ def test_gemm_mid_full_size_sampled(fmt, n, k, m):
 
 
 # ------------------------------------------ poison, guards, determinism --
-@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_rows", "gemm_mid", "gemm_mid_pair"])
+@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_rows", "gemm_mid", "gemm_mid_pair", "gemm_mid_parts",
+                                  "gemm_mid_parts_slices"])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_outputs_fully_written_and_guards_intact(kind, fmt):
     # gemm: the 256-token tile (200 tokens, one ragged block); gemm_rows: the
     # same through kq_gemm's row image; gemm_mid_pair: an even number of
-    # 32-token tiles, paired on 64-row panels
-    n, k, t = 70, 768, {"gemv": 3, "gemm": 200, "gemm_rows": 200, "gemm_mid": 70, "gemm_mid_pair": 60}[kind]
+    # 32-token tiles, paired on 64-row panels; gemm_mid_parts: the same with a
+    # workspace, so k is split inside the workgroup; _slices: k = 2048, split
+    # inside the workgroup and into whole-output slices too
+    n, t = 70, {"gemv": 3, "gemm": 200, "gemm_rows": 200, "gemm_mid": 70, "gemm_mid_pair": 60, "gemm_mid_parts": 60,
+                "gemm_mid_parts_slices": 60}[kind]
+    k = 2048 if kind == "gemm_mid_parts_slices" else 768
     c = Case(fmt, n, k, t, seed=9)
     assert kq.kq_gemm_tile_tokens(fmt, n, k, t) == (256 if kind in ("gemm", "gemm_rows") else 32)
     g = 4096
@@ -400,25 +405,32 @@ def test_outputs_fully_written_and_guards_intact(kind, fmt):
         kq.kq_gemv(fmt, c.planes, n, k, *c.q8, t, y)
     elif kind == "gemm_rows":
         kq.kq_gemm(fmt, c.planes, n, k, *c.q8, t, y, ops.gemm_workspace(fmt, n, k, t))
+    elif kind.startswith("gemm_mid_parts"):
+        kq.kq_gemm_tiles(fmt, c.planes, n, k, *c.q8t, t, y, ops.gemm_tiles_workspace(fmt, n, k, t))
     else:
         kq.kq_gemm_tiles(fmt, c.planes, n, k, *c.q8t, t, y)
     torch.cuda.synchronize()
     assert torch.all(buf[:g] == 1234.5) and torch.all(buf[-g:] == 1234.5)
     assert not torch.isnan(y).any()
+    if kind.startswith("gemm_mid_parts"):
+        check_y(c, y.view(t, n))
 
 
-@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("kind", ["gemv", "gemm", "gemm_mid"])
 def test_repeat_runs_are_bitwise_identical(kind):
+    # gemm_mid: 64 tokens of W_down, k split inside the workgroup and into
+    # whole-output slices
     n, k = 2560, 9728
-    t = 4 if kind == "gemv" else 256
-    c = Case("q6_k", n, k, t, seed=12)
+    t = {"gemv": 4, "gemm": 256, "gemm_mid": 64}[kind]
+    c = Case("q6_k" if kind != "gemm_mid" else "q4_k", n, k, t, seed=12)
     if kind == "gemv":
         ys = [ops.gemv("q6_k", c.planes, n, k, c.q8) for _ in range(3)]
     else:
         # one workspace reused: the split sums come out the same every call
-        ws = ops.gemm_tiles_workspace("q6_k", n, k, t)
+        fmt = "q6_k" if kind == "gemm" else "q4_k"
+        ws = ops.gemm_tiles_workspace(fmt, n, k, t)
         assert ws is not None
-        ys = [ops.gemm_tiles("q6_k", c.planes, n, k, c.q8t, workspace=ws) for _ in range(3)]
+        ys = [ops.gemm_tiles(fmt, c.planes, n, k, c.q8t, workspace=ws) for _ in range(3)]
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
 
 
