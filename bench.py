@@ -90,10 +90,10 @@ GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f0
 # the matrix-core GEMV at batch 8 (the gemv_batch leg's t8)
 GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "f324a75e3f91e773",
                  "bytes_per_launch": 17898683}
-GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
-                "bytes_per_launch": 74525348}
+GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "b2745a3913703daf",
+                "bytes_per_launch": 74649054}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "e4829b075324a6b6", "bytes_per_launch": 24398521}
+               "src_sha256_16": "b68259fb4c11142b", "bytes_per_launch": 24398521}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
                "src_sha256_16": "5ac5cad59ae4e73a", "bytes_per_launch": 232444087}
 
@@ -102,10 +102,10 @@ MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
 # kernel trace of a full bench run (profiles/kq_gemv_gemm_qwen3_4b_ffn_trace.md,
 # timed-region window), so the line carries the roofline fraction from both
 # timers; tied to the sources like the traffic records.
-GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.9}
-GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.06}
-GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "30d15b99f225897a",
-              "avg_us": 50.83}
+GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.72}
+GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.04}
+GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "b2745a3913703daf",
+              "avg_us": 49.82}
 
 
 def trace_us(rec):

@@ -190,8 +190,11 @@ __device__ inline int item_of(int b, int G)
 
 }  // namespace
 
+// Two workgroups per CU.  The partials form (PART: every superblock's P and M
+// stored too) holds one, so its extra live values sit in the accumulation
+// registers instead of spilling to scratch; the arithmetic is the same.
 template <int FMT, bool PART>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
+__global__ __launch_bounds__(256, PART ? 1 : 2) void gemm_kernel(const uint8_t *__restrict__ w, int64_t n, int nsb,
                                                       const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                       const _Float16 *__restrict__ xbs, int64_t mtok,
                                                       float *__restrict__ y, int32_t *__restrict__ Pout,
