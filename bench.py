@@ -93,9 +93,9 @@ GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "b2745a3913703daf",
                 "bytes_per_launch": 74649054}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "b68259fb4c11142b", "bytes_per_launch": 24398521}
+               "src_sha256_16": "50ee42d6a0615c3c", "bytes_per_launch": 24398521}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "5ac5cad59ae4e73a", "bytes_per_launch": 232444087}
+               "src_sha256_16": "917ad03f6a3c2d61", "bytes_per_launch": 232242270}
 
 
 # Mean per-dispatch duration of the same kernels in the committed rocprofv3

@@ -207,9 +207,11 @@ int kq_gemm_tile_tokens(int fmt, int64_t n, int64_t k, int64_t m);
  * (codes and f16 bsums in MFMA operand order, xs row-major): y[m][n], the
  * folds of kq_gemv.  k <= 2^23 - 256 (KQ_EINVAL above).  m <= 192 runs a
  * 32-token tile that unpacks each weight once per 32 tokens, or per 64 when
- * the tiles pair up (33..64 and 97..192 tokens; in registers for Q6_K,
- * through an LDS panel for Q4_K/Q5_K); m >= 193 a 256-token tile that
- * unpacks it once per 256 tokens into LDS.
+ * the tiles pair up (33..64 and 97..192 tokens; with a workspace, Q4_K/Q5_K
+ * also pair 65..96 tokens and split tiles of up to 32, the last pair's
+ * second tile empty; in registers for Q6_K, through an LDS panel for
+ * Q4_K/Q5_K); m >= 193 a 256-token tile that unpacks it once per 256 tokens
+ * into LDS.
  * workspace: NULL, or a 256-byte aligned device buffer of workspace_bytes >=
  * kq_gemm_tiles_workspace_bytes bytes (no initial contents needed; a
  * non-NULL pointer where that size is 0).  With it, a grid too small to fill

@@ -895,12 +895,17 @@ int launch_gemm_mid(int fmt, const void *w, int64_t n, int64_t k, const int8_t *
     // workgroups, W_down at 100-160 tokens, the CUs given two set the end:
     // 22.4 -> 32.4 us).  KP = 2 takes S/2 slices, KP_PER_CU four-wave
     // workgroups per CU; an unsplit tile (S = 1) runs as two parts where
-    // that grid fits (W_up at 100-128 tokens: 20.8 -> 18.8 us on Q4_K).
+    // that grid fits (W_up at 100-128 tokens: 20.8 -> 18.8 us on Q4_K).  An
+    // odd tile count pairs its last tile with an empty one (codes read as
+    // zero, outputs unstored): three tiles (65-96 tokens) take the pairs
+    // (W_up 21.5 -> 17.6 us on Q4_K), one tile (up to 32 tokens) only with
+    // four parts (W_down 15.4 -> 14.6 us; two parts and two slices were
+    // slower on W_up).
     const int64_t mtiles = (m + 31) / 32;
-    const bool pairq = mtiles % 2 == 0 || mtiles == 5;
-    if (split_ok && fmt != KQ_Q6_K && pairq) {
+    if (split_ok && fmt != KQ_Q6_K) {
         const int64_t cells = ((n + 31) / 32) * ((mtiles + 1) / 2);
         for (int kp = 4; kp >= 2; --kp) {
+            if (mtiles == 1 && kp != 4) continue;
             int Sw;
             if (kp == 4) {
                 if (S < 4) continue;
