@@ -266,7 +266,9 @@ def test_gemv_f32_fused_matches_two_step(fmt, t, n, k):
                                    (176, 130, 1024), (160, 64, 512), (200, 96, 768),
                                    # 64 tokens, k = 4096: four k-parts per workgroup and
                                    # slices across workgroups (Q6_K: as many as fill the CUs)
-                                   (64, 300, 4096), (64, 1100, 4096)])
+                                   (64, 300, 4096), (64, 1100, 4096),
+                                   # three tiles: the last pair's second tile empty
+                                   (80, 200, 2560)])
 def test_gemm_parity(fmt, m, n, k):
     c = Case(fmt, n, k, m, seed=m + n)
     y, P, M = ops.matmul_partials("gemm_tiles", fmt, c.planes, n, k, c.q8t)
