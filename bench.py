@@ -102,10 +102,10 @@ MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
 # kernel trace of a full bench run (profiles/kq_gemv_gemm_qwen3_4b_ffn_trace.md,
 # timed-region window), so the line carries the roofline fraction from both
 # timers; tied to the sources like the traffic records.
-GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.72}
-GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.04}
+GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.85}
+GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.13}
 GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "b2745a3913703daf",
-              "avg_us": 49.82}
+              "avg_us": 50.44}
 
 
 def trace_us(rec):
