@@ -90,22 +90,22 @@ GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f0
 # the matrix-core GEMV at batch 8 (the gemv_batch leg's t8)
 GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "f324a75e3f91e773",
                  "bytes_per_launch": 17898683}
-GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "b2745a3913703daf",
-                "bytes_per_launch": 74649054}
+GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "9c27a56fa3c1d0a0",
+                "bytes_per_launch": 74551099}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "50ee42d6a0615c3c", "bytes_per_launch": 24398521}
+               "src_sha256_16": "71fbfcce4fe0047b", "bytes_per_launch": 24398521}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "917ad03f6a3c2d61", "bytes_per_launch": 232242270}
+               "src_sha256_16": "9c41cc94204d77bf", "bytes_per_launch": 232479627}
 
 
 # Mean per-dispatch duration of the same kernels in the committed rocprofv3
 # kernel trace of a full bench run (profiles/kq_gemv_gemm_qwen3_4b_ffn_trace.md,
 # timed-region window), so the line carries the roofline fraction from both
 # timers; tied to the sources like the traffic records.
-GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.85}
-GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.13}
-GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "b2745a3913703daf",
-              "avg_us": 50.44}
+GEMV_F32_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.95}
+GEMV_TRACE = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f035fc554a12d", "avg_us": 6.2}
+GEMM_TRACE = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "9c27a56fa3c1d0a0",
+              "avg_us": 50.15}
 
 
 def trace_us(rec):

@@ -54,6 +54,12 @@
 extern "C" {
 #endif
 
+/* the library is built with hidden visibility: only these entry points are
+ * exported */
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility push(default)
+#endif
+
 /* Weight formats (the ggml K-quant records). */
 typedef enum { KQ_Q4_K = 4, KQ_Q5_K = 5, KQ_Q6_K = 6 } kq_format;
 
@@ -266,6 +272,10 @@ int kq_gemm_tiles_partials(int fmt, const void *w_planes, int64_t n, int64_t k, 
 
 /* Static text for a status code. */
 const char *kq_strerror(int code);
+
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

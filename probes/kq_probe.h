@@ -19,6 +19,10 @@
 extern "C" {
 #endif
 
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility push(default)
+#endif
+
 /* Streaming read: `grid` workgroups of 256 threads read the `bytes` bytes at
  * `buf` once with 16-byte loads (grid-strided, four loads in flight per
  * thread) and fold them into an xor that is stored to `sink` (4 bytes) only
@@ -39,6 +43,10 @@ int kq_probe_read_u(const void *buf, size_t bytes, uint32_t *sink, int grid, int
  * sink[grid * 256] so none is dead.  Ops per launch =
  * grid * 4 * iters * 4 * 65536.  1 <= grid <= 65536, 1 <= iters <= 2^24. */
 int kq_probe_mfma_i8(int64_t iters, int grid, int32_t *sink, void *stream);
+
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

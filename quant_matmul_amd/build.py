@@ -30,6 +30,8 @@ FLAGS = [
     # keep hipcc from forming packed-FP32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # export only the entry points include/kq.h declares
+    "-fvisibility=hidden",
 ]
 
 

@@ -468,9 +468,10 @@ struct Plan {
     int full, tail, TS;
 };
 
-static Plan plan_of(int64_t n, int64_t m, int nsb)
+// the device's CU count, read once (an atomic, so concurrent first calls are
+// safe); both GEMM tiles size their grids by it
+int cu_count()
 {
-    // the CU count, read once (an atomic, so concurrent first calls are safe)
     static std::atomic<int> cus_once{0};
     int cus = cus_once.load(std::memory_order_relaxed);
     if (!cus) {
@@ -480,7 +481,12 @@ static Plan plan_of(int64_t n, int64_t m, int nsb)
             cus = 256;
         cus_once.store(cus, std::memory_order_relaxed);
     }
-    const int64_t slots = 2 * (int64_t)cus;
+    return cus;
+}
+
+static Plan plan_of(int64_t n, int64_t m, int nsb)
+{
+    const int64_t slots = 2 * (int64_t)cu_count();
     const int64_t tiles = ((n + 31) / 32) * ((m + 255) / 256);
     const int64_t tail = tiles < slots ? tiles : 0;
     Plan p{(int)tiles, 0, 1};

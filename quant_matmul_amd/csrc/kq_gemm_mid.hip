@@ -33,7 +33,6 @@
 // w_planes + expert * w_stride.  The page's MoE path fills one Q8_K image
 // for the gate and up projections ("The pieces", kq v2 item).
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "kq_common.h"
@@ -765,23 +764,9 @@ __global__ __launch_bounds__(64 * 2 * KP, KP >= 4 ? 1 : 2) void gemm_mid_kp_kern
 }
 
 void launch_sum_splits(const float *p, int S, int64_t count, float *y, hipStream_t st);
+int cu_count();
 
 namespace {
-
-int cu_count()
-{
-    // read once (an atomic, so concurrent first calls are safe)
-    static std::atomic<int> cus_once{0};
-    int cus = cus_once.load(std::memory_order_relaxed);
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-            cus = 256;
-        cus_once.store(cus, std::memory_order_relaxed);
-    }
-    return cus;
-}
 
 int pick_splits_mid(int64_t waves, int nsb)
 {
