@@ -875,7 +875,8 @@ int launch_gemm_mid(int fmt, const void *w, int64_t n, int64_t k, const int8_t *
     // summing pass adds fewer slices, or none -- while its grid runs in one
     // round.  KP = 4 (eight waves, one workgroup per CU) takes as many
     // slices as fill the CUs once, where that is at least two (W_down at up
-    // to 64 tokens: 240 workgroups of three slices).  KP = 3 takes S/3
+    // to 64 tokens: 240 workgroups of three slices), or one where the tiles
+    // alone take three quarters of the CUs.  KP = 3 takes S/3
     // (rounded) slices, at most one six-wave workgroup per CU (at 320
     // workgroups, W_down at 100-160 tokens, the CUs given two set the end:
     // 22.4 -> 32.4 us).  KP = 2 takes S/2 slices, KP_PER_CU four-wave
@@ -901,7 +902,10 @@ int launch_gemm_mid(int fmt, const void *w, int64_t n, int64_t k, const int8_t *
                 Sw = Sw > 1 ? Sw : 1;
             }
             while (Sw > 1 && kp * Sw > nsb) --Sw;
-            if (kp == 4 && Sw < 2) continue;
+            // one slice only where the cells alone nearly fill the CUs (W_down at
+            // 129-192 tokens, 240 cells: 27.3 -> 22.8 us on Q4_K at 160 tokens;
+            // at 160 cells, 100-128 tokens, two parts and three slices stay faster)
+            if (kp == 4 && Sw < 2 && !(Sw == 1 && 4 * cells >= 3 * (int64_t)cu_count())) continue;
             const int64_t grid = cells * Sw;
             if (kp * Sw > nsb || grid > (kp == 2 ? KP_PER_CU : 1) * (int64_t)cu_count()) continue;
             float *dst = Sw > 1 ? (float *)ws : y;
