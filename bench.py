@@ -91,11 +91,11 @@ GEMV_TRAFFIC = {"files": ("kq_gemv.hip", "kq_common.h"), "src_sha256_16": "f08f0
 GEMV8_TRAFFIC = {"files": ("kq_gemv_mma.hip", "kq_common.h"), "src_sha256_16": "f324a75e3f91e773",
                  "bytes_per_launch": 17898683}
 GEMM_TRAFFIC = {"files": ("kq_gemm.hip", "kq_digits.h", "kq_common.h"), "src_sha256_16": "9c27a56fa3c1d0a0",
-                "bytes_per_launch": 74546407}
+                "bytes_per_launch": 74575427}
 MID_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_gemm.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "8ef7be5560fa4b56", "bytes_per_launch": 24398521}
+               "src_sha256_16": "19986ef945635242", "bytes_per_launch": 24398521}
 MOE_TRAFFIC = {"files": ("kq_gemm_mid.hip", "kq_digits.h", "kq_common.h"),
-               "src_sha256_16": "db9b4b4ceedb4737", "bytes_per_launch": 232319779}
+               "src_sha256_16": "2a677adcde19b108", "bytes_per_launch": 232180308}
 
 
 # Mean per-dispatch duration of the same kernels in the committed rocprofv3
